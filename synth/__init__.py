@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for the MXFP4 MoE expert FFN.
+
+This module only draws random numbers: it holds none of the method's
+arithmetic (no quantisation, routing, decode or FFN).  Both the CPU oracle
+and the HIP path take their inputs from here, so it imports neither.
+
+Recipe (one workload = one ``Workload`` below):
+
+* x: T x d, N(0, 1) drawn in float32, then rounded to bfloat16 (round to
+  nearest even on the float32 bits).  Returned as uint16 bf16 bit patterns.
+* logits: T x E, N(0, 1) float32, plus a per-expert bias added in float32:
+  "none" (0), "normal" (N(0, 0.5) per expert) or "zipf" (a log-Zipf tilt,
+  ``-s * alpha * ln(rank)`` with s = 1.1, alpha = 0.34 and a random rank
+  permutation, which gives the hottest expert about ten times the pairs of
+  the median one at top-8 of 128).
+* expert weights: for expert e, W_gate (f x d), W_up (f x d), W_down (d x f),
+  N(0, 0.02) float32, drawn from a stream of their own per expert so that any
+  subset of experts can be regenerated alone and in parallel.
+
+Streams: ``numpy.random.default_rng([seed, 0])`` for x then logits then bias;
+``numpy.random.default_rng([seed, 1, e])`` for expert e's three matrices in
+the order gate, up, down.  The default seed of a named workload is
+1000 + its index.
+"""
+from __future__ import annotations
+
+import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "workload", "make_activations",
+           "expert_weights_f32", "all_expert_weights_f32", "bf16_bits_from_f32",
+           "bf16_bits_to_f32"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int            # tokens (sequences x draft block of 8)
+    d: int            # d_model
+    f: int            # d_ff
+    E: int            # experts
+    k: int            # top-k
+    act: str = "bf16"     # "bf16" or "mxfp8" (activations micro-scaled to E4M3)
+    bias: str = "none"    # "none" | "normal" | "zipf"
+    seed: int = 0
+
+    @property
+    def P(self) -> int:
+        return self.T * self.k
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads: a tiny case, one verify step (1 sequence x block 8),
+# a batched verify step (32 sequences x 8), one GPU's expert share under a
+# skewed load (64 sequences x 8) and a dense 8192-token chunk.
+WORKLOADS = (
+    Workload("tiny",            8,  256,  512,   4, 2, "bf16",  "none",   1000),
+    Workload("verify_1seq",     8, 4096, 1536,  64, 8, "bf16",  "none",   1001),
+    Workload("verify_32seq",  256, 4096, 1536,  64, 8, "bf16",  "normal", 1002),
+    Workload("share_64seq",   512, 6144, 2048, 128, 8, "bf16",  "zipf",   1003),
+    Workload("chunk_8192",   8192, 6144, 2048, 128, 8, "mxfp8", "none",   1004),
+)
+
+
+def workload(key) -> Workload:
+    """Look a workload up by index or name."""
+    if isinstance(key, int):
+        return WORKLOADS[key]
+    for w in WORKLOADS:
+        if w.name == key:
+            return w
+    raise KeyError(key)
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite input)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounding = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32)
+            << np.uint32(16)).view(np.float32)
+
+
+def _bias(w: Workload, rng: np.random.Generator) -> np.ndarray:
+    if w.bias == "none":
+        return np.zeros(w.E, np.float32)
+    if w.bias == "normal":
+        return rng.normal(0.0, 0.5, size=w.E).astype(np.float32)
+    if w.bias == "zipf":
+        rank = rng.permutation(w.E).astype(np.float64) + 1.0
+        return (-1.1 * 0.34 * np.log(rank)).astype(np.float32)
+    raise ValueError(f"unknown bias kind {w.bias!r}")
+
+
+def make_activations(w: Workload, seed: int | None = None) -> dict:
+    """Hidden states and router logits of one verify batch.
+
+    Returns ``{"x_bf16": uint16 [T, d], "x": float32 [T, d] (the same values),
+    "logits": float32 [T, E], "bias": float32 [E]}``.
+    """
+    rng = np.random.default_rng([w.seed if seed is None else seed, 0])
+    x32 = rng.standard_normal((w.T, w.d), dtype=np.float32)
+    logits = rng.standard_normal((w.T, w.E), dtype=np.float32)
+    bias = _bias(w, rng)
+    logits = (logits + bias[None, :]).astype(np.float32)
+    xb = bf16_bits_from_f32(x32)
+    return {"x_bf16": xb, "x": bf16_bits_to_f32(xb), "logits": logits, "bias": bias}
+
+
+def expert_weights_f32(w: Workload, e: int, seed: int | None = None):
+    """(W_gate [f, d], W_up [f, d], W_down [d, f]) of expert e, float32 N(0, 0.02)."""
+    rng = np.random.default_rng([w.seed if seed is None else seed, 1, e])
+    gate = rng.standard_normal((w.f, w.d), dtype=np.float32)
+    up = rng.standard_normal((w.f, w.d), dtype=np.float32)
+    down = rng.standard_normal((w.d, w.f), dtype=np.float32)
+    for m in (gate, up, down):
+        m *= np.float32(0.02)
+    return gate, up, down
+
+
+def all_expert_weights_f32(w: Workload, experts=None, seed: int | None = None,
+                           threads: int | None = None):
+    """Yield ``(e, gate, up, down)`` for the given experts (default: all), in order.
+
+    Generation runs on a thread pool (numpy releases the GIL while filling),
+    a few experts ahead of the consumer so that memory stays bounded.
+    """
+    experts = list(range(w.E)) if experts is None else list(experts)
+    threads = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(threads) as ex:
+        pending = []
+        it = iter(experts)
+        for e in it:
+            pending.append((e, ex.submit(expert_weights_f32, w, e, seed)))
+            if len(pending) >= threads:
+                break
+        while pending:
+            e, fut = pending.pop(0)
+            nxt = next(it, None)
+            if nxt is not None:
+                pending.append((nxt, ex.submit(expert_weights_f32, w, nxt, seed)))
+            yield (e, *fut.result())

@@ -1,0 +1,345 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test checks one oracle function against a closed form, a library
+routine (torch's float8 codecs), brute force, or an independent second
+implementation (tests/pins.py), chosen so that a dropped term, a wrong sign,
+index or nibble order, or a transposed operand fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ codecs
+
+def test_e2m1_decode_matches_bitfield_closed_form():
+    for c in range(16):
+        got = oracle.e2m1_value(c)
+        want = pins.e2m1_value_bitfield(c)
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), c
+
+
+def test_e8m0_decode_matches_torch_all_bytes():
+    ref = pins.e8m0_values_torch()
+    for b in range(255):
+        assert oracle.e8m0_value(b) == ref[b], b
+    assert math.isnan(oracle.e8m0_value(255)) and math.isnan(ref[255])
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    ref = pins.e4m3_values_torch()
+    for c in range(256):
+        got = oracle.e4m3_value(c)
+        if math.isnan(ref[c]):
+            assert math.isnan(got), c
+        else:
+            assert got == ref[c] and math.copysign(1, got) == math.copysign(1, ref[c]), c
+
+
+def _e2m1_probe_values():
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 6.5, 7.999, 8.0, 100.0]
+    for t in ties:
+        vals += [t, np.nextafter(t, 0.0), np.nextafter(t, 10.0)]
+    rng = np.random.default_rng(5)
+    vals += list(rng.uniform(0.0, 8.0, 4000))
+    vals += list(np.float32(rng.uniform(0.0, 8.0, 4000)).astype(np.float64))
+    v = np.array(vals, np.float64)
+    return np.concatenate([v, -v])
+
+
+def test_e2m1_round_matches_threshold_table():
+    q = _e2m1_probe_values()
+    want = pins.e2m1_round_np(q)
+    got = np.array([oracle.e2m1_round(float(v)) for v in q], np.uint8)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(q[i], got[i], want[i]) for i in bad[:10]]
+
+
+def test_e2m1_round_tie_table():
+    # nearest-even: ties go to the code whose mantissa bit is 0
+    expect = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for q, v in expect.items():
+        assert oracle.e2m1_value(oracle.e2m1_round(q)) == v
+        assert oracle.e2m1_value(oracle.e2m1_round(-q)) == -v
+    assert oracle.e2m1_round(-0.1) == 8          # negative underflow keeps its sign
+    assert oracle.e2m1_round(7.5) == 7           # saturates to 6
+
+
+def test_e4m3_round_matches_torch():
+    rng = np.random.default_rng(6)
+    q = np.concatenate([
+        rng.uniform(-448, 448, 20000),
+        rng.uniform(-0.02, 0.02, 5000),                       # subnormal range
+        np.float32(rng.standard_normal(5000) * 50).astype(np.float64),
+        np.arange(-448, 449, 0.125),                           # many exact ties
+    ])
+    got = np.array([oracle.e4m3_round(float(v)) for v in q], np.uint8)
+    want = pins.e4m3_round_torch(q)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(q[i], got[i], want[i]) for i in bad[:10]]
+    # saturation, never the NaN code
+    for v in (448.5, 463.9, 464.0, 500.0, 511.99):
+        assert oracle.e4m3_round(v) == 0x7E and oracle.e4m3_round(-v) == 0xFE
+
+
+def test_e4m3_round_all_bf16_inputs():
+    b = np.arange(65536, dtype=np.uint32)
+    v32 = (b << 16).astype(np.uint32).view(np.float32)
+    v32 = v32[np.isfinite(v32)]
+    vals = v32[np.abs(v32) <= 1024.0].astype(np.float64)
+    got = np.array([oracle.e4m3_round(float(v)) for v in vals], np.uint8)
+    want = pins.e4m3_round_torch(vals)
+    assert np.array_equal(got, want)
+
+
+# -------------------------------------------------------------- MX tensors
+
+def test_mx_block_size_is_the_pages_32():
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    blk = facts["mx_block_size"]
+    w = np.full((1, 4 * blk), 0.01, np.float32)
+    _, s0 = oracle.quant_mxfp4(w)
+    w2 = w.copy()
+    w2[0, blk - 1] = 1.0          # last element of block 0
+    _, s1 = oracle.quant_mxfp4(w2)
+    w3 = w.copy()
+    w3[0, blk] = 1.0              # first element of block 1
+    _, s2 = oracle.quant_mxfp4(w3)
+    assert s0.shape == (1, 4)
+    assert s1[0, 0] != s0[0, 0] and np.array_equal(s1[0, 1:], s0[0, 1:])
+    assert s2[0, 1] != s0[0, 1] and s2[0, 0] == s0[0, 0]
+
+
+@pytest.mark.parametrize("e", [-127, -100, -20, -7, -1, 0, 1, 9, 60, 125])
+def test_mxfp4_codebook_times_pow2_round_trips_exactly(e):
+    rng = np.random.default_rng(1000 + e)
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    rows = []
+    for top in (4.0, 6.0):
+        for _ in range(8):
+            v = rng.choice(mags, 32) * rng.choice([-1.0, 1.0], 32)
+            v[rng.integers(32)] = top * rng.choice([-1.0, 1.0])
+            rows.append(v)
+    blk = np.ldexp(np.array(rows), e).astype(np.float32)
+    assert np.array_equal(blk.astype(np.float64), np.ldexp(np.array(rows), e))
+    packed, scales = oracle.quant_mxfp4(blk)
+    assert np.all(scales == e + 127)
+    back = oracle.dequant_mxfp4(packed, scales)
+    assert np.array_equal(back, blk.astype(np.float64))
+
+
+def test_mxfp4_nibble_order_low_nibble_is_even_element():
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = 4.0          # amax 4 -> scale 2^0, code 6 (value 4)
+    w[0, 1] = -1.0         # code 0b1010
+    packed, scales = oracle.quant_mxfp4(w)
+    assert scales[0, 0] == 127
+    assert packed[0, 0] == (6 | (10 << 4))
+
+
+def test_mxfp4_quantizer_matches_second_quantizer():
+    rng = np.random.default_rng(7)
+    mats = [rng.standard_normal((64, 256)).astype(np.float32) * 0.02,
+            rng.standard_normal((16, 512)).astype(np.float32) * 3e4,
+            (rng.standard_normal((8, 128)) * 1e-30).astype(np.float32),
+            np.zeros((2, 64), np.float32)]
+    t = np.array(_e2m1_probe_values()[:4096], np.float32).reshape(32, 128)
+    mats.append(t)
+    for m in mats:
+        p1, s1 = oracle.quant_mxfp4(m)
+        p2, s2 = pins.quant_mxfp4_np(m)
+        assert np.array_equal(s1, s2)
+        assert np.array_equal(p1, p2)
+
+
+def test_mxfp4_dequant_matches_bitfield_decoder():
+    rng = np.random.default_rng(8)
+    packed = rng.integers(0, 256, (16, 64), dtype=np.uint8)
+    scales = rng.integers(0, 255, (16, 4), dtype=np.uint8)
+    assert np.array_equal(oracle.dequant_mxfp4(packed, scales),
+                          pins.dequant_mxfp4_np(packed, scales))
+
+
+def test_mxfp8_quantizer_matches_torch_based_quantizer():
+    rng = np.random.default_rng(9)
+    for v in (rng.standard_normal((32, 256)),
+              np.float32(rng.standard_normal((8, 512)) * 1e-3).astype(np.float64),
+              rng.standard_normal((4, 64)) * 1e6):
+        c1, s1 = oracle.quant_mxfp8(v)
+        c2, s2 = pins.quant_mxfp8_np(v)
+        assert np.array_equal(s1, s2)
+        assert np.array_equal(c1, c2)
+        assert np.array_equal(oracle.dequant_mxfp8(c1, s1), pins.dequant_mxfp8_np(c2, s2))
+
+
+def test_mxfp8_e4m3_grid_times_pow2_round_trips():
+    grid = pins.e4m3_values_torch()[:127]
+    rng = np.random.default_rng(10)
+    for e in (-120, -3, 0, 5, 100):
+        v = rng.choice(grid, (4, 64)) * rng.choice([-1.0, 1.0], (4, 64))
+        v[:, 0] = 448.0
+        v[:, 32] = -256.0
+        v = np.ldexp(v, e)
+        c, s = oracle.quant_mxfp8(v)
+        assert np.all(s == e + 127)
+        assert np.array_equal(oracle.dequant_mxfp8(c, s), v)
+
+
+# ----------------------------------------------------------------- routing
+
+def _route_cases():
+    rng = np.random.default_rng(11)
+    yield rng.standard_normal((64, 16)).astype(np.float32), 4
+    yield rng.integers(-2, 3, (64, 16)).astype(np.float32), 5          # many exact ties
+    yield np.zeros((4, 8), np.float32), 8                                # all equal, k = E
+    base = rng.standard_normal((32, 12)).astype(np.float32)
+    # k-th and (k+1)-th logits one ulp apart
+    srt = np.sort(base, axis=1)[:, ::-1]
+    for t in range(32):
+        j = int(np.argwhere(base[t] == srt[t, 3])[0, 0])
+        i = int(np.argwhere(base[t] == srt[t, 2])[0, 0])
+        base[t, j] = np.nextafter(base[t, i], np.float32(-np.inf))
+    yield base, 3
+    yield rng.standard_normal((16, 128)).astype(np.float32), 8
+
+
+def test_route_matches_bruteforce():
+    for logits, k in _route_cases():
+        ids, w = oracle.route(logits, k)
+        ids2, w2 = pins.route_bruteforce(logits, k)
+        assert np.array_equal(ids, ids2)
+        np.testing.assert_allclose(w, w2, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-14)
+
+
+def test_route_equal_logits_give_uniform_weights():
+    for k in (1, 2, 3, 8):
+        ids, w = oracle.route(np.full((3, 9), 0.7, np.float32), k)
+        assert np.array_equal(ids, np.tile(np.arange(k), (3, 1)))
+        np.testing.assert_allclose(w, 1.0 / k, rtol=1e-15)
+
+
+def test_permute_is_stable_sort_by_expert():
+    rng = np.random.default_rng(12)
+    for T, k, E in ((8, 2, 4), (256, 8, 64), (100, 3, 7), (1, 1, 1), (0, 4, 8)):
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        ids, _ = oracle.route(logits, k) if T else (np.zeros((0, k), np.int32), None)
+        r = oracle.permute(ids, E)
+        flat = ids.reshape(-1)
+        assert np.array_equal(r["counts"], np.bincount(flat, minlength=E))
+        assert r["offsets"][0] == 0 and r["offsets"][-1] == T * k
+        assert np.all(np.diff(r["offsets"]) >= 0)
+        assert np.array_equal(r["sorted_pairs"], np.argsort(flat, kind="stable"))
+        assert np.array_equal(r["sorted_pairs"][r["inverse"]], np.arange(T * k))
+
+
+# --------------------------------------------------------------- forward
+
+def _problem(T, d, f, E, k, seed, act="bf16", bias="none"):
+    w = synth.Workload("t", T, d, f, E, k, act, bias, seed)
+    acts = synth.make_activations(w)
+    g, u, dn = zip(*[synth.expert_weights_f32(w, e) for e in range(E)])
+    return w, acts, oracle.quantize_experts(g, u, dn)
+
+
+@pytest.mark.parametrize("shape", [(8, 256, 512, 4, 2), (8, 128, 64, 8, 2), (5, 64, 96, 3, 3)])
+def test_forward_equals_dense_evaluation(shape):
+    T, d, f, E, k = shape
+    w, acts, wts = _problem(T, d, f, E, k, seed=21)
+    r = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)
+    ref = pins.dense_moe_np(acts["x"], acts["logits"], wts, k)
+    np.testing.assert_allclose(r["y"], ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+
+
+def test_forward_mxfp8_equals_dense_evaluation():
+    T, d, f, E, k = 8, 128, 96, 4, 2
+    w, acts, wts = _problem(T, d, f, E, k, seed=22, act="mxfp8")
+    r = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k, act_mode=oracle.ACT_MXFP8)
+    ref = pins.dense_moe_np(acts["x"], acts["logits"], wts, k, act_mxfp8=True)
+    # h is re-quantised on both sides; the dense path's different summation
+    # order can flip an E4M3 rounding only on an exact-tie knife edge
+    np.testing.assert_allclose(r["y"], ref, rtol=1e-9, atol=1e-12 * np.abs(ref).max())
+
+
+def test_forward_single_expert_reduces_to_matmuls():
+    w, acts, wts = _problem(6, 64, 64, 1, 1, seed=23)
+    r = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, 1)
+    Wg = pins.dequant_mxfp4_np(wts["w_gate"][0], wts["w_gate_scale"][0])
+    Wu = pins.dequant_mxfp4_np(wts["w_up"][0], wts["w_up_scale"][0])
+    Wd = pins.dequant_mxfp4_np(wts["w_down"][0], wts["w_down_scale"][0])
+    g = acts["x"].astype(np.float64) @ Wg.T
+    u = acts["x"].astype(np.float64) @ Wu.T
+    y = (g / (1 + np.exp(-g)) * u) @ Wd.T
+    assert np.all(r["w"] == 1.0)
+    np.testing.assert_allclose(r["y"], y, rtol=1e-12, atol=1e-14)
+
+
+def test_forward_one_hot_activation_picks_weight_columns():
+    T, d, f, E, k = 4, 64, 32, 2, 1
+    w, acts, wts = _problem(T, d, f, E, k, seed=24)
+    x = np.zeros((T, d), np.uint16)
+    cols = [0, 31, 32, 63]
+    for t, c in enumerate(cols):
+        x[t, c] = 0x3F80                                  # bf16 1.0
+    r = oracle.moe_forward(x, acts["logits"], wts, k, want_h=True)
+    for t, c in enumerate(cols):
+        e = r["ids"][t, 0]
+        Wg = pins.dequant_mxfp4_np(wts["w_gate"][e], wts["w_gate_scale"][e])
+        Wu = pins.dequant_mxfp4_np(wts["w_up"][e], wts["w_up_scale"][e])
+        g, u = Wg[:, c], Wu[:, c]
+        np.testing.assert_allclose(r["h"][t, 0], g / (1 + np.exp(-g)) * u, rtol=1e-15, atol=0)
+
+
+def test_forward_zero_weights_give_exact_zero():
+    T, d, f, E, k = 8, 64, 64, 4, 2
+    w, acts, wts = _problem(T, d, f, E, k, seed=25)
+    for n in ("w_gate", "w_up", "w_down"):
+        wts[n][:] = 0
+    r = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)
+    assert np.all(r["y"] == 0.0)
+
+
+def test_forward_dominant_logit_selects_one_expert():
+    T, d, f, E, k = 4, 64, 64, 4, 2
+    w, acts, wts = _problem(T, d, f, E, k, seed=26)
+    logits = acts["logits"].copy()
+    logits[:, 2] = 80.0
+    r = oracle.moe_forward(acts["x_bf16"], logits, wts, k)
+    r1 = oracle.moe_forward(acts["x_bf16"], np.zeros((T, 1), np.float32),
+                            {n: v[2:3] for n, v in wts.items()}, 1)
+    assert np.all(r["ids"][:, 0] == 2)
+    np.testing.assert_allclose(r["y"], r1["y"], rtol=1e-25 + 1e-12, atol=1e-30)
+
+
+def test_forward_token_subset_equals_rows_of_full_batch():
+    T, d, f, E, k = 16, 128, 64, 8, 3
+    w, acts, wts = _problem(T, d, f, E, k, seed=27, bias="normal")
+    full = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)
+    rows = [0, 5, 15]
+    sub = oracle.moe_forward(acts["x_bf16"][rows], acts["logits"][rows], wts, k)
+    assert np.array_equal(sub["y"], full["y"][rows])
+    assert np.array_equal(sub["ids"], full["ids"][rows])
+
+
+def test_forward_threads_do_not_change_result():
+    T, d, f, E, k = 12, 64, 64, 4, 2
+    w, acts, wts = _problem(T, d, f, E, k, seed=28)
+    a = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k, nthreads=1)
+    b = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k, nthreads=4)
+    assert np.array_equal(a["y"], b["y"])
+
+
+def test_forward_rejects_bad_shapes():
+    w, acts, wts = _problem(2, 64, 64, 2, 1, seed=29)
+    with pytest.raises(ValueError):
+        oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, 3)      # k > E

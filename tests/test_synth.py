@@ -1,0 +1,49 @@
+"""The seeded input generator (CPU only)."""
+import json
+import os
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_verify_batches_are_whole_dflash_blocks():
+    blk = json.load(open(os.path.join(GOLDEN, "page_facts.json")))["dflash_block_max"]
+    for w in synth.WORKLOADS[:4]:
+        assert w.T % blk == 0, w.name
+
+
+def test_generator_is_deterministic_and_per_expert():
+    w = synth.workload("tiny")
+    a, b = synth.make_activations(w), synth.make_activations(w)
+    assert np.array_equal(a["x_bf16"], b["x_bf16"]) and np.array_equal(a["logits"], b["logits"])
+    g1 = synth.expert_weights_f32(w, 2)
+    g2 = [m for e, *m in synth.all_expert_weights_f32(w) if e == 2][0]
+    for x, y in zip(g1, g2):
+        assert np.array_equal(x, y)
+
+
+def test_bf16_rounding_is_nearest_even():
+    f = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 1.0 + 2**-8 + 2**-20], np.float32)
+    back = synth.bf16_bits_to_f32(synth.bf16_bits_from_f32(f))
+    assert list(back) == [1.0, 1.0, 1.0 + 2**-6, -2.5, 1.0 + 2**-7]
+
+
+def test_weight_and_activation_statistics():
+    w = synth.workload("tiny")
+    acts = synth.make_activations(w)
+    assert abs(acts["x"].std() - 1.0) < 0.05
+    g, u, d = synth.expert_weights_f32(w, 0)
+    assert g.shape == (w.f, w.d) and d.shape == (w.d, w.f)
+    assert abs(g.std() - 0.02) < 0.001
+
+
+def test_zipf_bias_makes_top_expert_about_ten_times_median():
+    w = synth.workload("share_64seq")
+    logits = synth.make_activations(w)["logits"]
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :w.k]
+    n = np.bincount(top.ravel(), minlength=w.E)
+    ratio = n.max() / np.median(n)
+    assert 5.0 < ratio < 20.0, ratio
