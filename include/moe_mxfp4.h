@@ -1,0 +1,212 @@
+/*
+ * moe_mxfp4.h -- C ABI of the MXFP4 Mixture-of-Experts expert FFN for
+ * speculative-decoding verify steps, on AMD Instinct MI355X (gfx950).
+ *
+ * What one forward call computes (the expert layer of a verify step):
+ *   1. top-k routing of every token from its router logits;
+ *   2. a stable token-to-expert permutation of the (token, slot) pairs;
+ *   3. decode of the MXFP4 expert weights -- 4-bit E2M1 elements with one
+ *      E8M0 power-of-two scale per block of 32 along the reduction dimension;
+ *   4. gate/up projection with SwiGLU;
+ *   5. down projection and the routing-weighted combine of the k experts.
+ *
+ * Passages this follows (sources are web pages about Xiaomi's
+ * MiMo-V2.5-Pro-UltraSpeed):
+ *   - ai.appwright.xyz, tag page "投機的デコード", section
+ *     "第1層：FP4量子化（モデル側）": only the MoE experts are MXFP4, block size
+ *     32; decoding is bound by weight footprint and bandwidth.
+ *   - techllm.github.io, "Xiaomi MiMo x TileRT ... 1000 tokens per second",
+ *     section "1. MXFP4 — MoE에만 걸린 양자화" (experts hold most weights, FP4
+ *     cuts footprint and bandwidth), section "2. DFlash" (draft blocks of up
+ *     to 8 tokens, verified by the target model), section "3. TileRT" (the
+ *     expert-routing pattern; microsecond operators where launch gaps matter).
+ *   - dothoosh.com, "Xiaomi: 1000 tokens per second for a 1T model"
+ *     (Persian), section "جزئیات پیاده‌سازی DFlash": block size capped at 8.
+ * The pages give no routing rule, activation, layout or API.  Readings taken
+ * here: softmax over the k selected logits; SwiGLU h = silu(W_gate a) *
+ * (W_up a); the packed layout below; the element/scale bit meanings and the
+ * scale rule of the OCP Microscaling Formats (MX) v1.0 specification.
+ *
+ * Conventions for every entry point:
+ *   - Pointers documented as "device" are HIP device pointers (from
+ *     hipMalloc or a torch CUDA tensor); all others are host pointers.
+ *   - Device buffers must be 16-byte aligned.  The library never allocates,
+ *     frees or copies caller memory; it only reads inputs and writes outputs
+ *     and the caller-provided workspace.
+ *   - `hip_stream` is a hipStream_t passed as void* (NULL = default stream).
+ *     Work is queued on it asynchronously; no call synchronises the device or
+ *     copies device data to the host, so forward calls can be captured into
+ *     a HIP graph.
+ *   - Every call returns a moe_status.  Argument errors are detected on the
+ *     host before anything is queued and leave all state unchanged.  A
+ *     failed kernel launch returns MOE_ERR_HIP; faults inside kernels surface
+ *     asynchronously at the caller's next synchronisation.
+ *   - Preconditions that are NOT checked (undefined results if broken):
+ *     finite logits and activations; no E8M0 scale byte 0xFF; products of
+ *     decoded weights and activations that stay finite in float32.
+ *   - Thread safety: a context is immutable after create; concurrent forward
+ *     calls on one context are safe when they use distinct workspaces and
+ *     outputs.
+ */
+#ifndef MOE_MXFP4_H
+#define MOE_MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_MXFP4_ABI_VERSION 1
+#define MOE_MXFP4_BLOCK 32          /* elements per E8M0 scale (MX block) */
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,       /* null pointer, bad enum, negative size     */
+    MOE_ERR_UNSUPPORTED_SHAPE = 2, /* dims outside what the kernels handle      */
+    MOE_ERR_CAPACITY = 3,          /* num_tokens > max_tokens                   */
+    MOE_ERR_ALIGNMENT = 4,         /* a device pointer not 16-byte aligned      */
+    MOE_ERR_WORKSPACE = 5,         /* workspace missing or too small            */
+    MOE_ERR_HIP = 6,               /* a HIP runtime call or launch failed       */
+    MOE_ERR_INTERNAL = 7
+} moe_status;
+
+/* How the activations enter the projections. */
+typedef enum {
+    MOE_ACT_BF16 = 0,        /* bf16 hidden states used as they are              */
+    MOE_ACT_MXFP8_E4M3 = 1   /* hidden states and h micro-scaled to E4M3 + E8M0  */
+} moe_act_mode;
+
+typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
+
+typedef struct {
+    uint32_t struct_size;    /* sizeof(moe_mxfp4_config)                        */
+    int32_t num_experts;     /* E, 1..512                                       */
+    int32_t d_model;         /* d, multiple of 256                              */
+    int32_t d_ff;            /* f, multiple of 256                              */
+    int32_t top_k;           /* k, 1..min(E, 32)                                */
+    int32_t max_tokens;      /* upper bound of num_tokens per forward call, >= 1 */
+    int32_t act_mode;        /* moe_act_mode                                    */
+    int32_t out_dtype;       /* moe_out_dtype                                   */
+    uint32_t flags;          /* reserved, must be 0                             */
+} moe_mxfp4_config;
+
+/*
+ * Packed MXFP4 expert weights (device, borrowed: the caller keeps them alive
+ * and unchanged until moe_mxfp4_destroy).  Each matrix is row-major with one
+ * output unit per row and the reduction dimension K along the row:
+ *   w_gate, w_up : uint8 [E][d_ff][d_model/2],  scales uint8 [E][d_ff][d_model/32]
+ *   w_down       : uint8 [E][d_model][d_ff/2],  scales uint8 [E][d_model][d_ff/32]
+ * Element kk of a row is in byte kk/2: the LOW nibble holds even kk, the high
+ * nibble odd kk.  A nibble is an E2M1 code (sign bit 3; magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6).  Scale byte kk/32 of the same row is the E8M0 exponent of
+ * that block: the element's value is E2M1(code) * 2^(byte - 127).
+ */
+typedef struct {
+    const uint8_t* w_gate;
+    const uint8_t* w_gate_scale;
+    const uint8_t* w_up;
+    const uint8_t* w_up_scale;
+    const uint8_t* w_down;
+    const uint8_t* w_down_scale;
+} moe_mxfp4_weights;
+
+/*
+ * Optional routing outputs of a forward call (device pointers; any may be
+ * NULL).  Sizes for T tokens, P = T * k pairs, pair id p = t * k + j:
+ *   topk_ids       int32 [T][k]  expert of slot j, descending logit, ties to
+ *                                the lower expert index
+ *   topk_w         float [T][k]  softmax over the k selected logits
+ *   expert_offsets int32 [E+1]   pairs of expert e are sorted_pairs[off[e] ..
+ *                                off[e+1]); off[0] = 0, off[E] = P
+ *   sorted_pairs   int32 [P]     pair ids grouped by expert, ascending within
+ *                                each expert (a stable counting sort)
+ */
+typedef struct {
+    int32_t* topk_ids;
+    float* topk_w;
+    int32_t* expert_offsets;
+    int32_t* sorted_pairs;
+} moe_mxfp4_routing;
+
+typedef struct moe_mxfp4_ctx moe_mxfp4_ctx;   /* opaque, host memory only */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_mxfp4_status_string(moe_status s);
+
+/* ABI version the library was built with (MOE_MXFP4_ABI_VERSION). */
+int32_t moe_mxfp4_abi_version(void);
+
+/*
+ * Validate `cfg` and the weight pointers and create a context.  Host only:
+ * queues no device work and touches no device memory.  `*out` receives the
+ * context (left untouched on error).  Errors: INVALID_ARG (null pointer,
+ * struct_size mismatch, bad enum, nonzero flags), UNSUPPORTED_SHAPE (limits
+ * in moe_mxfp4_config), ALIGNMENT (a weight pointer not 16-byte aligned).
+ */
+moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg,
+                            const moe_mxfp4_weights* weights,
+                            moe_mxfp4_ctx** out);
+
+/* Release a context (host memory only).  destroy(NULL) returns MOE_OK. */
+moe_status moe_mxfp4_destroy(moe_mxfp4_ctx* ctx);
+
+/*
+ * Bytes of device workspace a forward call with `num_tokens` tokens needs
+ * (0 for num_tokens <= 0 or a NULL context).  The workspace holds routing,
+ * permutation and the per-pair intermediate activations; it is scratch with
+ * no state carried between calls.
+ */
+size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_ctx* ctx, int32_t num_tokens);
+
+/*
+ * Run the expert layer for `num_tokens` tokens (0 is a no-op returning
+ * MOE_OK).  All buffers are device memory:
+ *   hidden         bf16  [T][d_model] (uint16 bit patterns)
+ *   router_logits  float [T][E]
+ *   out            [T][d_model], bf16 (round to nearest even) or float per
+ *                  cfg.out_dtype; fully overwritten
+ *   workspace      at least moe_mxfp4_workspace_bytes(ctx, T) bytes
+ *   debug_out      optional routing outputs (host struct, may be NULL)
+ * out = sum over the k selected experts e of w_e * W_down,e ( silu(W_gate,e a)
+ * * (W_up,e a) ), where a is the token's hidden state (after an MXFP8 round
+ * trip per 32-block in MOE_ACT_MXFP8_E4M3 mode, which also rounds h the same
+ * way).  Accumulation is float32; routing ids and the permutation are exact
+ * and deterministic; the output is deterministic for a given input.
+ * Errors: INVALID_ARG, CAPACITY (T > max_tokens), ALIGNMENT, WORKSPACE, HIP.
+ */
+moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden,
+                             const float* router_logits, int32_t num_tokens,
+                             void* out, void* workspace, size_t workspace_bytes,
+                             void* hip_stream, const moe_mxfp4_routing* debug_out);
+
+/*
+ * Decode rows [row0, row0 + nrows) of one expert matrix (0 gate, 1 up,
+ * 2 down) with the forward path's own in-register FP4 decode, widened to
+ * float: out (device) float [nrows][K], K = d_model for gate/up, d_ff for
+ * down.  For checking the decode bit for bit.  Errors: INVALID_ARG (bad
+ * expert, matrix or row range, null out), ALIGNMENT, HIP.
+ */
+moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
+                                   int32_t matrix, int32_t row0, int32_t nrows,
+                                   float* out, void* hip_stream);
+
+/*
+ * Weight preparation (off the forward path): quantise a row-major float
+ * matrix w (device) [rows][K] into the packed layout above -- per block of
+ * 32 along K, scale 2^(floor(log2(amax)) - 2) clamped to the E8M0 range
+ * (an all-zero block gets byte 0), elements rounded to the nearest E2M1
+ * value with ties to the even code, saturating at +-6, the sign of a value
+ * that rounds to zero kept.  packed (device) uint8 [rows][K/2], scales
+ * (device) uint8 [rows][K/32].  K must be a positive multiple of 32.
+ * Errors: INVALID_ARG, ALIGNMENT, HIP.
+ */
+moe_status moe_mxfp4_quantize_weights(const float* w, int64_t rows, int64_t K,
+                                      uint8_t* packed, uint8_t* scales,
+                                      void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MXFP4_H */

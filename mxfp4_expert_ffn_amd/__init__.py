@@ -1,0 +1,199 @@
+"""Python binding of libmoe_mxfp4 (the MXFP4 MoE expert FFN on MI355X).
+
+Argument marshalling only: every step of the forward path runs in the HIP
+kernels behind the C ABI in ``include/moe_mxfp4.h``.  PyTorch supplies device
+memory and the current stream; nothing here computes any part of the method,
+and there is no CPU fallback -- if the library is missing, loading fails.
+
+Names follow the C ABI: ``MoeMxfp4`` wraps ``moe_mxfp4_create / _forward /
+_destroy / _workspace_bytes / _debug_dequant``; ``quantize_weights`` wraps
+``moe_mxfp4_quantize_weights``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mxfp4.so")
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED_SHAPE",
+                3: "MOE_ERR_CAPACITY", 4: "MOE_ERR_ALIGNMENT", 5: "MOE_ERR_WORKSPACE",
+                6: "MOE_ERR_HIP", 7: "MOE_ERR_INTERNAL"}
+ACT_BF16, ACT_MXFP8_E4M3 = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+
+# Every symbol include/moe_mxfp4.h declares.
+EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create",
+           "moe_mxfp4_destroy", "moe_mxfp4_workspace_bytes", "moe_mxfp4_forward",
+           "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("num_experts", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("act_mode", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate", "w_gate_scale", "w_up", "w_up_scale",
+                                               "w_down", "w_down_scale")]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("topk_ids", "topk_w", "expert_offsets",
+                                               "sorted_pairs")]
+
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              f"`python -m mxfp4_expert_ffn_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.moe_mxfp4_status_string.argtypes = [ctypes.c_int]
+        L.moe_mxfp4_status_string.restype = ctypes.c_char_p
+        L.moe_mxfp4_abi_version.argtypes = []
+        L.moe_mxfp4_abi_version.restype = i32
+        L.moe_mxfp4_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
+                                       ctypes.POINTER(P)]
+        L.moe_mxfp4_create.restype = ctypes.c_int
+        L.moe_mxfp4_destroy.argtypes = [P]
+        L.moe_mxfp4_destroy.restype = ctypes.c_int
+        L.moe_mxfp4_workspace_bytes.argtypes = [P, i32]
+        L.moe_mxfp4_workspace_bytes.restype = sz
+        L.moe_mxfp4_forward.argtypes = [P, P, P, i32, P, P, sz, P, ctypes.POINTER(Routing)]
+        L.moe_mxfp4_forward.restype = ctypes.c_int
+        L.moe_mxfp4_debug_dequant.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.moe_mxfp4_debug_dequant.restype = ctypes.c_int
+        L.moe_mxfp4_quantize_weights.argtypes = [P, i64, i64, P, P, P]
+        L.moe_mxfp4_quantize_weights.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_mxfp4_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_config(num_experts, d_model, d_ff, top_k, max_tokens, act_mode=ACT_BF16,
+                out_dtype=OUT_BF16, flags=0) -> Config:
+    return Config(ctypes.sizeof(Config), num_experts, d_model, d_ff, top_k, max_tokens,
+                  act_mode, out_dtype, flags)
+
+
+class MoeMxfp4:
+    """One expert layer: borrowed packed weights + configuration.
+
+    ``weights``: dict of uint8 CUDA tensors ``w_gate [E, f, d/2]``,
+    ``w_gate_scale [E, f, d/32]``, ``w_up``, ``w_up_scale`` (same shapes),
+    ``w_down [E, d, f/2]``, ``w_down_scale [E, d, f/32]``.  References are
+    kept for the life of this object.
+    """
+
+    def __init__(self, weights: dict, num_experts: int, d_model: int, d_ff: int, top_k: int,
+                 max_tokens: int, act_mode: int = ACT_BF16, out_dtype: int = OUT_BF16):
+        self.cfg = make_config(num_experts, d_model, d_ff, top_k, max_tokens, act_mode, out_dtype)
+        self.weights = dict(weights)
+        self.out_dtype = out_dtype
+        w = Weights(*[_ptr(self.weights[n]) for n in ("w_gate", "w_gate_scale", "w_up",
+                                                      "w_up_scale", "w_down", "w_down_scale")])
+        h = ctypes.c_void_p()
+        _check(lib().moe_mxfp4_create(ctypes.byref(self.cfg), ctypes.byref(w), ctypes.byref(h)),
+               "moe_mxfp4_create")
+        self._ctx = h
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "_ctx", None) is not None and self._ctx.value:
+            lib().moe_mxfp4_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, num_tokens: int) -> int:
+        return lib().moe_mxfp4_workspace_bytes(self._ctx, num_tokens)
+
+    def workspace(self, num_tokens: int):
+        """A cached uint8 workspace large enough for ``num_tokens``."""
+        import torch
+        need = self.workspace_bytes(num_tokens)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        return self._ws
+
+    def forward(self, hidden, logits, out=None, workspace=None, routing: dict | None = None,
+                stream=None):
+        """hidden: bf16 [T, d] CUDA; logits: float32 [T, E] CUDA -> out [T, d]."""
+        import torch
+        T = hidden.shape[0]
+        if out is None:
+            dt = torch.bfloat16 if self.out_dtype == OUT_BF16 else torch.float32
+            out = torch.empty((T, self.cfg.d_model), dtype=dt, device=hidden.device)
+        ws = self.workspace(T) if workspace is None else workspace
+        r = None
+        if routing is not None:
+            r = Routing(*[_ptr(routing.get(n)) for n in ("topk_ids", "topk_w", "expert_offsets",
+                                                         "sorted_pairs")])
+        st = lib().moe_mxfp4_forward(self._ctx, _ptr(hidden), _ptr(logits), T, _ptr(out), _ptr(ws),
+                                     ws.numel() if ws is not None else 0, _stream(stream),
+                                     ctypes.byref(r) if r is not None else None)
+        _check(st, "moe_mxfp4_forward")
+        return out
+
+    __call__ = forward
+
+    def debug_dequant(self, expert: int, matrix: int, row0: int, nrows: int, out=None, stream=None):
+        import torch
+        K = self.cfg.d_ff if matrix == 2 else self.cfg.d_model
+        if out is None:
+            out = torch.empty((nrows, K), dtype=torch.float32, device="cuda")
+        _check(lib().moe_mxfp4_debug_dequant(self._ctx, expert, matrix, row0, nrows, _ptr(out),
+                                             _stream(stream)), "moe_mxfp4_debug_dequant")
+        return out
+
+
+def quantize_weights(w, packed=None, scales=None, stream=None):
+    """float32 CUDA [rows, K] -> (packed uint8 [rows, K/2], scales uint8 [rows, K/32])."""
+    import torch
+    rows, K = w.shape
+    if packed is None:
+        packed = torch.empty((rows, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_mxfp4_quantize_weights(_ptr(w), rows, K, _ptr(packed), _ptr(scales),
+                                            _stream(stream)), "moe_mxfp4_quantize_weights")
+    return packed, scales

@@ -1,0 +1,199 @@
+// Host side of the C ABI declared in include/moe_mxfp4.h: argument checks,
+// workspace carve-up and the launch sequence of one forward call.
+//
+// A forward call is five launches on the caller's stream and nothing else
+// (no allocation, no host synchronisation, no device-to-host copy), so it can
+// be captured into a HIP graph: the pages stress that at microsecond
+// operator times the gaps between operators matter (techllm.github.io
+// "Xiaomi MiMo x TileRT", section "3. TileRT").
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <new>
+
+#include "common.hpp"
+
+struct moe_mxfp4_ctx {
+    moe_mxfp4_config cfg;
+    moe_mxfp4_weights w;
+};
+
+namespace {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 32;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t ids, w, offsets, sorted, inverse, active, h, o, total;
+};
+
+Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
+    const size_t P = (size_t)T * c.top_k;
+    Layout L{};
+    size_t at = 0;
+    L.ids = at;     at += round256(P * sizeof(int32_t));
+    L.w = at;       at += round256(P * sizeof(float));
+    L.offsets = at; at += round256((size_t)(c.num_experts + 1) * sizeof(int32_t));
+    L.sorted = at;  at += round256(P * sizeof(int32_t));
+    L.inverse = at; at += round256(P * sizeof(int32_t));
+    L.active = at;  at += round256((size_t)(c.num_experts + 1) * sizeof(int32_t));
+    L.h = at;       at += round256(P * (size_t)c.d_ff * sizeof(uint16_t));
+    L.o = at;       at += round256(P * (size_t)c.d_model * sizeof(float));
+    L.total = at;
+    return L;
+}
+
+moe_status check_config(const moe_mxfp4_config* c) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->struct_size != sizeof(moe_mxfp4_config)) return MOE_ERR_INVALID_ARG;
+    if (c->flags != 0) return MOE_ERR_INVALID_ARG;
+    if (c->act_mode != MOE_ACT_BF16 && c->act_mode != MOE_ACT_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
+    if (c->out_dtype != MOE_OUT_BF16 && c->out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARG;
+    if (c->num_experts < 1 || c->top_k < 1 || c->d_model < 1 || c->d_ff < 1 || c->max_tokens < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (c->num_experts > kMaxExperts || c->top_k > kMaxTopK || c->top_k > c->num_experts)
+        return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (c->d_model % 256 != 0 || c->d_ff % 256 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+    if ((int64_t)c->max_tokens * c->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
+    if ((int64_t)c->d_model * c->d_ff > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
+    if (c->act_mode == MOE_ACT_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED_SHAPE;   // not built yet
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_mxfp4_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer, bad enum or size";
+        case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE: dimensions outside the kernels' limits";
+        case MOE_ERR_CAPACITY: return "MOE_ERR_CAPACITY: num_tokens exceeds max_tokens";
+        case MOE_ERR_ALIGNMENT: return "MOE_ERR_ALIGNMENT: device pointer not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or runtime call failed";
+        case MOE_ERR_INTERNAL: return "MOE_ERR_INTERNAL";
+    }
+    return "unknown moe_status";
+}
+
+int32_t moe_mxfp4_abi_version(void) { return MOE_MXFP4_ABI_VERSION; }
+
+moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg, const moe_mxfp4_weights* weights,
+                            moe_mxfp4_ctx** out) {
+    if (!out || !weights) return MOE_ERR_INVALID_ARG;
+    const moe_status st = check_config(cfg);
+    if (st != MOE_OK) return st;
+    const void* ptrs[6] = {weights->w_gate, weights->w_gate_scale, weights->w_up,
+                           weights->w_up_scale, weights->w_down, weights->w_down_scale};
+    for (const void* p : ptrs)
+        if (!p) return MOE_ERR_INVALID_ARG;
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return MOE_ERR_ALIGNMENT;
+    moe_mxfp4_ctx* ctx = new (std::nothrow) moe_mxfp4_ctx;
+    if (!ctx) return MOE_ERR_INTERNAL;
+    ctx->cfg = *cfg;
+    ctx->w = *weights;
+    *out = ctx;
+    return MOE_OK;
+}
+
+moe_status moe_mxfp4_destroy(moe_mxfp4_ctx* ctx) {
+    delete ctx;
+    return MOE_OK;
+}
+
+size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_ctx* ctx, int32_t num_tokens) {
+    if (!ctx || num_tokens <= 0) return 0;
+    return make_layout(ctx->cfg, num_tokens).total;
+}
+
+moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float* router_logits,
+                             int32_t num_tokens, void* out, void* workspace, size_t workspace_bytes,
+                             void* hip_stream, const moe_mxfp4_routing* debug_out) {
+    if (!ctx || num_tokens < 0) return MOE_ERR_INVALID_ARG;
+    const moe_mxfp4_config& c = ctx->cfg;
+    if (num_tokens > c.max_tokens) return MOE_ERR_CAPACITY;
+    if (num_tokens == 0) return MOE_OK;
+    if (!hidden || !router_logits || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(router_logits) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
+    const Layout L = make_layout(c, num_tokens);
+    if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_ERR_ALIGNMENT;
+    if (debug_out) {
+        const void* dp[4] = {debug_out->topk_ids, debug_out->topk_w, debug_out->expert_offsets,
+                             debug_out->sorted_pairs};
+        for (const void* p : dp)
+            if (p && !aligned16(p)) return MOE_ERR_ALIGNMENT;
+    }
+
+    char* base = static_cast<char*>(workspace);
+    moe::Workspace ws;
+    ws.topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
+    ws.topk_w = reinterpret_cast<float*>(base + L.w);
+    ws.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+    ws.sorted_pairs = reinterpret_cast<int32_t*>(base + L.sorted);
+    ws.inverse = reinterpret_cast<int32_t*>(base + L.inverse);
+    ws.active = reinterpret_cast<int32_t*>(base + L.active);
+    ws.h = reinterpret_cast<uint16_t*>(base + L.h);
+    ws.o = reinterpret_cast<float*>(base + L.o);
+
+    moe::Dims dm{num_tokens, c.d_model, c.d_ff, c.num_experts, c.top_k, num_tokens * c.top_k};
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    const uint16_t* x = static_cast<const uint16_t*>(hidden);
+
+    if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_sort(dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup(x, ctx->w, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down(ctx->w, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess) return MOE_ERR_HIP;
+
+    if (debug_out) {
+        const size_t P = (size_t)dm.P;
+        struct { void* dst; const void* src; size_t n; } cp[4] = {
+            {debug_out->topk_ids, ws.topk_ids, P * sizeof(int32_t)},
+            {debug_out->topk_w, ws.topk_w, P * sizeof(float)},
+            {debug_out->expert_offsets, ws.offsets, (size_t)(c.num_experts + 1) * sizeof(int32_t)},
+            {debug_out->sorted_pairs, ws.sorted_pairs, P * sizeof(int32_t)}};
+        for (auto& k : cp)
+            if (k.dst && hipMemcpyAsync(k.dst, k.src, k.n, hipMemcpyDeviceToDevice, s) != hipSuccess)
+                return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert, int32_t matrix,
+                                   int32_t row0, int32_t nrows, float* out, void* hip_stream) {
+    if (!ctx || !out) return MOE_ERR_INVALID_ARG;
+    const moe_mxfp4_config& c = ctx->cfg;
+    if (expert < 0 || expert >= c.num_experts || matrix < 0 || matrix > 2) return MOE_ERR_INVALID_ARG;
+    const int64_t N = matrix == 2 ? c.d_model : c.d_ff;
+    const int64_t K = matrix == 2 ? c.d_ff : c.d_model;
+    if (row0 < 0 || nrows < 0 || (int64_t)row0 + nrows > N) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(out)) return MOE_ERR_ALIGNMENT;
+    if (nrows == 0) return MOE_OK;
+    const uint8_t* P = matrix == 0 ? ctx->w.w_gate : matrix == 1 ? ctx->w.w_up : ctx->w.w_down;
+    const uint8_t* S = matrix == 0 ? ctx->w.w_gate_scale : matrix == 1 ? ctx->w.w_up_scale : ctx->w.w_down_scale;
+    const int64_t row = (int64_t)expert * N + row0;
+    if (moe::launch_debug_dequant(P + row * (K / 2), S + row * (K / MOE_MXFP4_BLOCK), K, nrows, out,
+                                  static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_mxfp4_quantize_weights(const float* w, int64_t rows, int64_t K, uint8_t* packed,
+                                      uint8_t* scales, void* hip_stream) {
+    if (!w || !packed || !scales || rows < 0 || K <= 0 || K % MOE_MXFP4_BLOCK != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(packed) || !aligned16(scales)) return MOE_ERR_ALIGNMENT;
+    if (rows == 0) return MOE_OK;
+    if (moe::launch_quantize(w, rows, K, packed, scales, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Weighted combine of the k expert outputs of every token, and the two
+// helper kernels that sit beside the forward path (decode export, weight
+// quantiser).
+//
+// Combine: y[t] = sum_j w[t][j] * o[t][j]; the down projection has already
+// multiplied each pair's output by its routing weight, so this sums the k
+// rows of a token in slot order j = 0..k-1 (fixed order: deterministic) and
+// rounds once to the output type.
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One thread per 4 consecutive output columns of one token.
+__global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const float* __restrict__ o,
+                                                       const int32_t* __restrict__ inverse,
+                                                       void* __restrict__ out, int out_dtype) {
+    const int q = dm.d / 4;
+    const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= (size_t)dm.T * q) return;
+    const int t = (int)(gid / q), c = (int)(gid % q) * 4;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < dm.k; ++j) {
+        const size_t row = (size_t)inverse[(size_t)t * dm.k + j];
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(o + row * dm.d + c);
+        acc += v;
+    }
+    if (out_dtype == MOE_OUT_F32) {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + (size_t)t * dm.d + c) = acc;
+    } else {
+        const uint32_t lo = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + (size_t)t * dm.d + c);
+        dst[0] = lo;
+        dst[1] = hi;
+    }
+}
+
+// Decode export: one thread per 8 elements (one packed dword), with the
+// forward path's decode8_bf16, widened to float.
+__global__ __launch_bounds__(kThreads) void k_debug_dequant(const uint8_t* __restrict__ packed,
+                                                            const uint8_t* __restrict__ scales,
+                                                            int64_t K, int32_t nrows,
+                                                            float* __restrict__ out) {
+    const int64_t per_row = K / 8;
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= per_row * nrows) return;
+    const int64_t r = gid / per_row, c8 = gid % per_row;
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + r * (K / 2) + c8 * 4);
+    const uint32_t sb = scales[r * (K / kBlock) + (c8 * 8) / kBlock];
+    const bf16x8_t v = decode8_bf16(word, e8m0_as_scale(sb));
+    float* dst = out + r * K + c8 * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = (float)v[i];
+}
+
+// E2M1 code of one already-scaled value: nearest of 0, .5, 1, 1.5, 2, 3, 4, 6
+// with ties to the even code, saturating; the sign of a zero result kept.
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+    const float a = fabsf(q);
+    uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                 (a >= 3.5f) + (a > 5.0f);
+    return m | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+// Weight quantiser: 4 lanes per 32-element block, 8 elements each.
+__global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__ w, int64_t rows,
+                                                       int64_t K, uint8_t* __restrict__ packed,
+                                                       uint8_t* __restrict__ scales) {
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t nblk = rows * (K / kBlock);
+    const int64_t blk = gid / 4;
+    const int part = (int)(gid % 4);
+    const bool valid = blk < nblk;
+    const int64_t r = valid ? blk / (K / kBlock) : 0, b = valid ? blk % (K / kBlock) : 0;
+    float v[8];
+    float amax = 0.f;
+    const float* src = w + r * K + b * kBlock + part * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[i] = valid ? src[i] : 0.f;
+        amax = fmaxf(amax, fabsf(v[i]));
+    }
+    // the 4 lanes of a block are consecutive and 4-aligned within the wave
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    if (!valid) return;
+    // floor(log2(amax)) from the exponent field; a subnormal amax is
+    // mantissa * 2^-149, so its floor(log2) is 31 - clz(mantissa) - 149
+    int fl;
+    const uint32_t bits = __float_as_uint(amax);
+    const int ef = (int)(bits >> 23);
+    if (amax == 0.f) fl = -125;                       // gives the smallest scale, byte 0
+    else if (ef > 0) fl = ef - 127;
+    else fl = -118 - (int)__clz(bits & 0x7FFFFFu);
+    int se = fl - 2;
+    se = se < -127 ? -127 : (se > 127 ? 127 : se);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= e2m1_code(ldexpf(v[i], -se)) << (4 * i);
+    *reinterpret_cast<uint32_t*>(packed + r * (K / 2) + b * 16 + part * 4) = word;
+    if (part == 0) scales[r * (K / kBlock) + b] = (uint8_t)(se + 127);
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, hipStream_t s) {
+    const size_t n = (size_t)dm.T * (dm.d / 4);
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       dm, ws.o, ws.inverse, out, out_dtype);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t nrows,
+                                float* out, hipStream_t s) {
+    const int64_t n = (K / 8) * nrows;
+    hipLaunchKernelGGL(k_debug_dequant, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       packed, scales, K, nrows, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const float* w, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales,
+                           hipStream_t s) {
+    const int64_t n = rows * (K / kBlock) * 4;
+    hipLaunchKernelGGL(k_quantize, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       w, rows, K, packed, scales);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,156 @@
+"""The C-ABI library: loads, exports what the header declares, and rejects
+bad arguments on the host before queueing any device work (CPU only: no
+call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_expert_ffn_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+FAKE = 1 << 20          # a 16-byte-aligned stand-in device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_mxfp4_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_status_strings_and_version():
+    L = moe.lib()
+    for s in range(8):
+        assert moe.status_string(s).startswith(moe.STATUS_NAMES[s])
+    assert "unknown" in moe.status_string(99)
+    assert L.moe_mxfp4_abi_version() == 1
+
+
+def _create(**kw):
+    args = dict(num_experts=4, d_model=256, d_ff=512, top_k=2, max_tokens=8)
+    args.update(kw)
+    flags = args.pop("flags", 0)
+    act = args.pop("act_mode", moe.ACT_BF16)
+    out = args.pop("out_dtype", moe.OUT_BF16)
+    cfg = moe.make_config(**args, act_mode=act, out_dtype=out, flags=flags)
+    ptrs = kw.get("ptrs", [FAKE] * 6)
+    w = moe.Weights(*ptrs)
+    h = ctypes.c_void_p()
+    st = moe.lib().moe_mxfp4_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(num_experts=0), 1), (dict(top_k=0), 1), (dict(max_tokens=0), 1),
+    (dict(d_model=-256), 1), (dict(flags=1), 1), (dict(act_mode=7), 1), (dict(out_dtype=3), 1),
+    (dict(top_k=5), 2), (dict(num_experts=513, top_k=2), 2), (dict(num_experts=64, top_k=33), 2),
+    (dict(d_model=288), 2), (dict(d_ff=384), 2),
+])
+def test_create_validation(kw, status):
+    ptrs = kw.pop("ptrs", None)
+    st, h = _create(**kw) if ptrs is None else _create(ptrs=ptrs, **kw)
+    assert st == status, moe.status_string(st)
+    if st == 0:
+        assert h.value and moe.lib().moe_mxfp4_destroy(h) == 0
+    else:
+        assert not h.value
+
+
+def test_create_rejects_null_and_misaligned_weights():
+    cfg = moe.make_config(4, 256, 512, 2, 8)
+    L = moe.lib()
+    h = ctypes.c_void_p()
+    for i in range(6):
+        ptrs = [FAKE] * 6
+        ptrs[i] = None
+        assert L.moe_mxfp4_create(ctypes.byref(cfg), ctypes.byref(moe.Weights(*ptrs)),
+                                  ctypes.byref(h)) == 1
+        ptrs[i] = FAKE + 8
+        assert L.moe_mxfp4_create(ctypes.byref(cfg), ctypes.byref(moe.Weights(*ptrs)),
+                                  ctypes.byref(h)) == 4
+    assert L.moe_mxfp4_create(None, ctypes.byref(moe.Weights(*[FAKE] * 6)), ctypes.byref(h)) == 1
+    bad = moe.make_config(4, 256, 512, 2, 8)
+    bad.struct_size = 4
+    assert L.moe_mxfp4_create(ctypes.byref(bad), ctypes.byref(moe.Weights(*[FAKE] * 6)),
+                              ctypes.byref(h)) == 1
+    assert L.moe_mxfp4_destroy(None) == 0
+
+
+def test_workspace_bytes_grows_with_tokens():
+    st, h = _create()
+    L = moe.lib()
+    try:
+        assert L.moe_mxfp4_workspace_bytes(h, 0) == 0
+        assert L.moe_mxfp4_workspace_bytes(None, 8) == 0
+        a, b = L.moe_mxfp4_workspace_bytes(h, 1), L.moe_mxfp4_workspace_bytes(h, 8)
+        assert 0 < a < b
+        # holds the per-pair h (bf16, f wide) and weighted outputs (float, d wide)
+        assert b >= 8 * 2 * (512 * 2 + 256 * 4)
+    finally:
+        L.moe_mxfp4_destroy(h)
+
+
+def test_forward_validation_happens_before_any_launch():
+    st, h = _create()
+    L = moe.lib()
+    need = L.moe_mxfp4_workspace_bytes(h, 8)
+    fwd = L.moe_mxfp4_forward
+    try:
+        assert fwd(None, FAKE, FAKE, 1, FAKE, FAKE, need, None, None) == 1
+        assert fwd(h, FAKE, FAKE, -1, FAKE, FAKE, need, None, None) == 1
+        assert fwd(h, FAKE, FAKE, 9, FAKE, FAKE, 10**9, None, None) == 3       # > max_tokens
+        assert fwd(h, None, None, 0, None, None, 0, None, None) == 0           # T = 0 no-op
+        assert fwd(h, None, FAKE, 8, FAKE, FAKE, need, None, None) == 1
+        assert fwd(h, FAKE, FAKE, 8, None, FAKE, need, None, None) == 1
+        assert fwd(h, FAKE + 4, FAKE, 8, FAKE, FAKE, need, None, None) == 4
+        assert fwd(h, FAKE, FAKE, 8, FAKE, FAKE, need - 1, None, None) == 5
+        assert fwd(h, FAKE, FAKE, 8, FAKE, None, need, None, None) == 5
+        assert fwd(h, FAKE, FAKE, 8, FAKE, FAKE + 8, need, None, None) == 4
+        r = moe.Routing(FAKE + 2, None, None, None)
+        assert fwd(h, FAKE, FAKE, 8, FAKE, FAKE, need, None, ctypes.byref(r)) == 4
+    finally:
+        L.moe_mxfp4_destroy(h)
+
+
+def test_debug_dequant_and_quantize_validation():
+    st, h = _create()
+    L = moe.lib()
+    try:
+        dq = L.moe_mxfp4_debug_dequant
+        assert dq(h, 4, 0, 0, 1, FAKE, None) == 1          # expert out of range
+        assert dq(h, 0, 3, 0, 1, FAKE, None) == 1          # matrix out of range
+        assert dq(h, 0, 0, 510, 4, FAKE, None) == 1        # rows past d_ff
+        assert dq(h, 0, 2, 0, 257, FAKE, None) == 1        # rows past d_model
+        assert dq(h, 0, 0, 0, 1, None, None) == 1
+        assert dq(h, 0, 0, 0, 1, FAKE + 4, None) == 4
+        assert dq(h, 0, 0, 0, 0, FAKE, None) == 0          # nothing to do
+        q = L.moe_mxfp4_quantize_weights
+        assert q(FAKE, 4, 48, FAKE, FAKE, None) == 1        # K not a multiple of 32
+        assert q(None, 4, 64, FAKE, FAKE, None) == 1
+        assert q(FAKE, -1, 64, FAKE, FAKE, None) == 1
+        assert q(FAKE + 4, 4, 64, FAKE, FAKE, None) == 4
+        assert q(FAKE, 0, 64, FAKE, FAKE, None) == 0
+    finally:
+        L.moe_mxfp4_destroy(h)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        moe.lib()

@@ -1,0 +1,229 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: routing ids, expert offsets, the permutation, the FP4 decode and the
+weight quantiser are bit-exact; routing weights within 1e-6; the layer
+output within max|y - y_ref| <= 2e-2 * RMS(y_ref) (y_ref in double).  Full
+sizes run the GPU on the whole batch, in the launch configuration the
+benchmark times, and check a sample of tokens against the oracle (tokens are
+independent given their routing) plus the routing of every token.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import problems
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _moe():
+    import mxfp4_expert_ffn_amd as moe
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return moe
+
+
+def _run(w: synth.Workload, acts, wts_dev, out_dtype=None, T=None, routing=True):
+    moe = _moe()
+    T = w.T if T is None else T
+    layer = moe.MoeMxfp4(wts_dev, w.E, w.d, w.f, w.k, max_tokens=max(T, 1),
+                         out_dtype=moe.OUT_F32 if out_dtype is None else out_dtype)
+    x = torch.from_numpy(acts["x_bf16"][:T].view(np.int16)).cuda().view(torch.bfloat16)
+    lg = torch.from_numpy(acts["logits"][:T]).cuda()
+    r = None
+    if routing:
+        P = T * w.k
+        r = {"topk_ids": torch.empty(P, dtype=torch.int32, device="cuda"),
+             "topk_w": torch.empty(P, dtype=torch.float32, device="cuda"),
+             "expert_offsets": torch.empty(w.E + 1, dtype=torch.int32, device="cuda"),
+             "sorted_pairs": torch.empty(P, dtype=torch.int32, device="cuda")}
+    y = layer(x, lg, routing=r)
+    torch.cuda.synchronize()
+    out = {"y": y.float().cpu().numpy()}
+    if r:
+        out.update({k: v.cpu().numpy() for k, v in r.items()})
+    return out, layer
+
+
+def _check_routing(w, acts, got, T=None):
+    T = w.T if T is None else T
+    ids, wts = oracle.route(acts["logits"][:T], w.k)
+    perm = oracle.permute(ids, w.E)
+    assert np.array_equal(got["topk_ids"], ids.reshape(-1))
+    assert np.abs(got["topk_w"] - wts.reshape(-1)).max() <= 1e-6
+    assert np.array_equal(got["expert_offsets"], perm["offsets"])
+    assert np.array_equal(got["sorted_pairs"], perm["sorted_pairs"])
+
+
+# ------------------------------------------------------------- decode ---
+
+def test_debug_dequant_bit_exact_all_bytes_and_scales():
+    moe = _moe()
+    E, d, f = 1, 256, 256
+    rng = np.random.default_rng(40)
+    wts = {}
+    for name, (rows, K) in (("w_gate", (f, d)), ("w_up", (f, d)), ("w_down", (d, f))):
+        packed = ((np.arange(rows * K // 2) * 7 + rng.integers(0, 256)) % 256).astype(np.uint8)
+        scales = (np.arange(rows * K // 32) % 255).astype(np.uint8)     # every finite byte
+        wts[name] = packed.reshape(1, rows, K // 2)
+        wts[name + "_scale"] = rng.permutation(scales).reshape(1, rows, K // 32)
+    dev = problems.to_device(wts)
+    layer = moe.MoeMxfp4(dev, E, d, f, 1, max_tokens=1)
+    for m, name in enumerate(("w_gate", "w_up", "w_down")):
+        rows = wts[name].shape[1]
+        got = layer.debug_dequant(0, m, 0, rows).cpu().numpy()
+        with np.errstate(over="ignore"):
+            ref = oracle.dequant_mxfp4(wts[name][0], wts[name + "_scale"][0]).astype(np.float32)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), name
+    # a row window
+    got = layer.debug_dequant(0, 2, 100, 7).cpu().numpy()
+    with np.errstate(over="ignore"):
+        ref = oracle.dequant_mxfp4(wts["w_down"][0, 100:107], wts["w_down_scale"][0, 100:107])
+    assert np.array_equal(got.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+
+
+def test_quantize_weights_bit_exact():
+    moe = _moe()
+    rng = np.random.default_rng(41)
+    rows = [rng.standard_normal((64, 512)) * 0.02,
+            rng.standard_normal((8, 512)) * 3e4,
+            rng.standard_normal((8, 512)) * 1e-39,                      # subnormal floats
+            np.zeros((2, 512)), -np.zeros((2, 512))]
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.9])
+    base = np.concatenate([ties, -ties, np.nextafter(ties, 0), np.nextafter(ties, 9)])
+    t = np.resize(base, 16 * 512).reshape(16, 512)
+    t[:, ::32] = 4.0                                                   # pin each block's scale
+    rows += [t, t * 2.0 ** -20]
+    w = np.concatenate(rows).astype(np.float32)
+    p, s = moe.quantize_weights(torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    p2, s2 = oracle.quant_mxfp4(w)
+    assert np.array_equal(s.cpu().numpy(), s2)
+    assert np.array_equal(p.cpu().numpy(), p2)
+
+
+# ------------------------------------------------------- small / full ---
+
+def test_tiny_workload_full_parity():
+    w = synth.workload("tiny")
+    acts, wts = problems.problem(w)
+    dev = problems.to_device(wts)
+    got, _ = _run(w, acts, dev)
+    _check_routing(w, acts, got)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, w.k)["y"]
+    err = problems.rel_max_err(got["y"], ref)
+    print(f"tiny f32-out rel max err {err:.3e}")
+    assert err <= TOL
+    got16, _ = _run(w, acts, dev, out_dtype=0, routing=False)
+    err16 = problems.rel_max_err(got16["y"], ref)
+    print(f"tiny bf16-out rel max err {err16:.3e}")
+    assert err16 <= TOL
+    # the bf16 output is the float32 result rounded once to nearest even
+    assert np.array_equal(got16["y"].astype(np.float32),
+                          torch.from_numpy(got["y"]).bfloat16().float().numpy())
+
+
+@pytest.mark.parametrize("name,nsample", [("verify_1seq", 8), ("verify_32seq", 12),
+                                          ("share_64seq", 12)])
+def test_full_size_workload_sampled_parity(name, nsample):
+    w = synth.workload(name)
+    acts, wts = problems.problem(w)
+    dev = problems.to_device(wts)
+    got, _ = _run(w, acts, dev, out_dtype=0)            # bf16 output, as benchmarked
+    _check_routing(w, acts, got)
+    rng = np.random.default_rng(7)
+    sample = np.sort(rng.choice(w.T, size=min(nsample, w.T), replace=False))
+    # include the tokens of the most loaded expert (the multi-chunk path)
+    ids = got["topk_ids"].reshape(w.T, w.k)
+    hot = np.bincount(ids.ravel(), minlength=w.E).argmax()
+    hot_tokens = np.nonzero((ids == hot).any(axis=1))[0][-2:]
+    sample = np.unique(np.concatenate([sample, hot_tokens]))
+    ref = oracle.moe_forward(acts["x_bf16"][sample], acts["logits"][sample], wts, w.k,
+                             nthreads=problems.THREADS)["y"]
+    err = problems.rel_max_err(got["y"][sample], ref)
+    print(f"{name}: bf16-out rel max err over {len(sample)} tokens {err:.3e}")
+    assert err <= TOL
+
+
+# -------------------------------------------------------------- edges ---
+
+def _custom(T, d, f, E, k, seed, logits=None, scale=None):
+    w = synth.Workload("edge", T, d, f, E, k, "bf16", "none", seed)
+    acts = synth.make_activations(w)
+    if logits is not None:
+        acts["logits"] = np.ascontiguousarray(logits, np.float32)
+    wts = problems.pack_experts(w)
+    return w, acts, wts
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (13, 8, 2), (37, 4, 4), (5, 1, 1), (64, 16, 3)])
+def test_edge_shapes(T, E, k):
+    w, acts, wts = _custom(T, 256, 256, E, k, seed=50 + T)
+    got, _ = _run(w, acts, problems.to_device(wts))
+    _check_routing(w, acts, got)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)["y"]
+    assert problems.rel_max_err(got["y"], ref) <= TOL
+
+
+def test_all_tokens_on_the_same_experts_multi_chunk():
+    T, E, k = 150, 8, 2                                  # 150 pairs per expert: 3 chunks
+    logits = np.zeros((T, E), np.float32)
+    logits[:, 5] = 3.0
+    logits[:, 2] = 2.0 + np.linspace(0, 0.5, T, dtype=np.float32)
+    w, acts, wts = _custom(T, 256, 512, E, k, seed=60, logits=logits)
+    got, _ = _run(w, acts, problems.to_device(wts))
+    _check_routing(w, acts, got)
+    assert got["expert_offsets"][E] == T * k
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)["y"]
+    assert problems.rel_max_err(got["y"], ref) <= TOL
+
+
+def test_exact_logit_ties_pick_lowest_experts():
+    T, E, k = 16, 8, 3
+    logits = np.zeros((T, E), np.float32)
+    logits[::2, 7] = 1.0
+    w, acts, wts = _custom(T, 256, 256, E, k, seed=61, logits=logits)
+    got, _ = _run(w, acts, problems.to_device(wts))
+    _check_routing(w, acts, got)
+    ids = got["topk_ids"].reshape(T, k)
+    assert np.array_equal(ids[1], [0, 1, 2]) and np.array_equal(ids[0], [7, 0, 1])
+
+
+def test_zero_weights_give_zero_output():
+    w, acts, wts = _custom(8, 256, 256, 4, 2, seed=62)
+    for n in ("w_gate", "w_up", "w_down"):
+        wts[n][:] = 0
+    got, _ = _run(w, acts, problems.to_device(wts))
+    assert np.all(got["y"] == 0.0)
+
+
+def test_scaled_weights_exercise_far_scale_bytes():
+    w, acts, wts = _custom(16, 256, 256, 4, 2, seed=63)
+    for n, sh in (("w_gate_scale", 40), ("w_up_scale", -30), ("w_down_scale", 50)):
+        wts[n] = (wts[n].astype(np.int32) + sh).astype(np.uint8)
+    got, _ = _run(w, acts, problems.to_device(wts))
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, 2)["y"]
+    assert np.isfinite(ref).all()
+    assert problems.rel_max_err(got["y"], ref) <= TOL
+
+
+def test_deterministic_and_workspace_reuse():
+    moe = _moe()
+    w, acts, wts = _custom(40, 256, 256, 8, 2, seed=64)
+    dev = problems.to_device(wts)
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=40, out_dtype=moe.OUT_F32)
+    x = torch.from_numpy(acts["x_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
+    lg = torch.from_numpy(acts["logits"]).cuda()
+    a = layer(x, lg).clone()
+    b = layer(x, lg).clone()
+    assert torch.equal(a, b)
+    small = layer(x[:7], lg[:7]).clone()               # same workspace, fewer tokens
+    big = layer(x, lg).clone()
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(acts["x_bf16"][:7], acts["logits"][:7], wts, w.k)["y"]
+    assert problems.rel_max_err(small.cpu().numpy(), ref) <= TOL
+    assert torch.equal(big, a)
