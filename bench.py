@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 MoE expert layer on one MI355X.
+
+Metric: MoE expert-layer tokens/s on the 256-token verify step (32 sequences
+x a DFlash block of 8 tokens; d_model 4096, d_ff 1536, 64 experts, top-8,
+router logits with a per-expert N(0, 0.5) bias), with the achieved HBM
+GB/s of the layer and of its dominant kernel against the 8 TB/s peak.
+
+One step = one forward call of the whole path (routing, permutation, gate/up
++ SwiGLU, down, combine) over the synthetic batch; inputs and packed weights
+are resident in HBM before the timed region.  Consecutive steps rotate over
+several copies of the weights so that no step finds another step's weights
+in the 256 MB last-level cache.  The CPU oracle is timed on a bounded token
+sample as a reported baseline (rank 0, one GPU only).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+WNAMES = ("w_gate", "w_gate_scale", "w_up", "w_up_scale", "w_down", "w_down_scale")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_shapes(w):
+    return {"w_gate": (w.E, w.f, w.d // 2), "w_gate_scale": (w.E, w.f, w.d // 32),
+            "w_up": (w.E, w.f, w.d // 2), "w_up_scale": (w.E, w.f, w.d // 32),
+            "w_down": (w.E, w.d, w.f // 2), "w_down_scale": (w.E, w.d, w.f // 32)}
+
+
+def pack_on_gpu(w, copies, moe, torch):
+    """Generate fp32 expert weights (synth), pack them with the library's
+    quantiser on the GPU, and clone into `copies` independent copies."""
+    import synth
+    shapes = weight_shapes(w)
+    packed = {n: torch.empty(s, dtype=torch.uint8, device="cuda") for n, s in shapes.items()}
+    for e, g, u, dn in synth.all_expert_weights_f32(w):
+        for name, m in (("w_gate", g), ("w_up", u), ("w_down", dn)):
+            t = torch.from_numpy(m).cuda()
+            moe.quantize_weights(t, packed=packed[name][e], scales=packed[name + "_scale"][e])
+    torch.cuda.synchronize()
+    out = [packed]
+    for _ in range(copies - 1):
+        out.append({n: t.clone() for n, t in packed.items()})
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(w, acts, ntok):
+    """The oracle, as it stands, on the first `ntok` tokens (oracle-packed weights)."""
+    import numpy as np
+    import oracle
+    import synth
+    from concurrent.futures import ThreadPoolExecutor
+    threads = min(16, os.cpu_count() or 1)
+    x, lg = acts["x_bf16"][:ntok], acts["logits"][:ntok]
+    ids, _ = oracle.route(lg, w.k)
+    need = [int(e) for e in np.unique(ids)]
+    wts = {n: np.zeros(s, np.uint8) for n, s in weight_shapes(w).items()}
+
+    def job(e):
+        g, u, dn = synth.expert_weights_f32(w, e)
+        for name, m in (("w_gate", g), ("w_up", u), ("w_down", dn)):
+            p, s = oracle.quant_mxfp4(m)
+            wts[name][e] = p
+            wts[name + "_scale"][e] = s
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(job, need))
+    t0 = time.perf_counter()
+    r = oracle.moe_forward(x, lg, wts, w.k, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": int(r["threads"]), "kind": "oracle",
+            "sample": f"first {ntok} of {w.T} tokens of {w.name}, all {w.k} experts each; "
+                      f"fp64 C oracle, OpenMP over tokens; {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="verify_32seq")
+    ap.add_argument("--copies", type=int, default=3, help="weight copies rotated across steps")
+    ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no collectives, no sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mxfp4_expert_ffn_amd as moe
+    import synth
+
+    w = synth.workload(args.workload)
+    if w.act != "bf16":
+        print(f"workload {w.name} needs the MXFP8 activation path, which this build lacks",
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    log(f"workload {w}")
+    acts = synth.make_activations(w)
+    t0 = time.time()
+    wcopies = pack_on_gpu(w, args.copies, moe, torch)
+    log(f"weights generated and packed on the GPU ({args.copies} copies) in {time.time() - t0:.1f} s")
+
+    x = torch.from_numpy(acts["x_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
+    lg = torch.from_numpy(acts["logits"]).cuda()
+    out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
+    layers = [moe.MoeMxfp4(c, w.E, w.d, w.f, w.k, max_tokens=w.T) for c in wcopies]
+    ws = torch.empty(layers[0].workspace_bytes(w.T), dtype=torch.uint8, device="cuda")
+
+    # routing of this batch, from the library itself, for the byte counts
+    offs = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    layers[0](x, lg, out=out, workspace=ws, routing={"expert_offsets": offs})
+    torch.cuda.synchronize()
+    counts = np.diff(offs.cpu().numpy())
+    touched = int((counts > 0).sum())
+    per_expert = 3 * w.d * w.f * (1 / 2 + 1 / 32)
+    layer_bytes = touched * per_expert + w.T * w.d * 2 + w.T * w.E * 4 + w.T * w.d * 2
+    gateup_bytes = touched * 2 * w.f * w.d * (1 / 2 + 1 / 32) + w.T * w.d * 2
+    flops = 2.0 * w.P * 3 * w.d * w.f
+
+    for i in range(args.warmup):
+        layers[i % args.copies](x, lg, out=out, workspace=ws)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` forward calls
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        layers[i % args.copies](x, lg, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt * 1e3 / args.steps
+
+    # per-stage HIP-event timing in a second pass (events would perturb the first)
+    for L in layers:
+        L.stage_timing(args.steps)
+    for i in range(args.steps):
+        layers[i % args.copies](x, lg, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    stage_ms, ncalls = {}, 0
+    for L in layers:
+        t, n = L.stage_times()
+        ncalls += n
+        for k, v in t.items():
+            stage_ms[k] = stage_ms.get(k, 0.0) + v
+        L.stage_timing(0)
+    stage_avg_us = {k: 1e3 * v / ncalls for k, v in stage_ms.items()}
+    log(f"stage averages (us): " + ", ".join(f"{k} {v:.1f}" for k, v in stage_avg_us.items()))
+
+    gateup_s = stage_avg_us["gateup"] * 1e-6
+    achieved = gateup_bytes / gateup_s / 1e9
+    result = {
+        "metric": "MoE expert-layer tokens/s + achieved HBM GB/s (% of peak), 256-token verify",
+        "value": w.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.T} tokens ({w.T // 8} sequences x DFlash block 8), "
+                               f"d_model {w.d}, d_ff {w.f}, {w.E} experts, top-{w.k}, "
+                               f"bias {w.bias}, MXFP4 weights (E2M1 + E8M0 per 32), bf16 in/out",
+                   "T": w.T, "d_model": w.d, "d_ff": w.f, "experts": w.E, "top_k": w.k,
+                   "touched_experts": touched, "weight_copies": args.copies},
+        "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+        "layer_hbm_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "layer_algorithmic_bytes": layer_bytes,
+        "layer_tflops": flops / (ms_per_step * 1e-3) / 1e12,
+        "stage_us": stage_avg_us,
+        "roofline": {"bound": "hbm", "kernel": "k_expert<gate/up>", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": gateup_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
+        result["cpu_baseline"] = cpu_baseline(w, acts, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,9 +44,10 @@
  *   - Preconditions that are NOT checked (undefined results if broken):
  *     finite logits and activations; no E8M0 scale byte 0xFF; products of
  *     decoded weights and activations that stay finite in float32.
- *   - Thread safety: a context is immutable after create; concurrent forward
- *     calls on one context are safe when they use distinct workspaces and
- *     outputs.
+ *   - Thread safety: apart from the optional stage timing below, a context
+ *     is immutable after create; concurrent forward calls on one context are
+ *     safe when they use distinct workspaces and outputs and stage timing is
+ *     off.
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -191,6 +192,32 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden,
 moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
                                    int32_t matrix, int32_t row0, int32_t nrows,
                                    float* out, void* hip_stream);
+
+/*
+ * Per-stage timing of forward calls with HIP events, for measurement.  The
+ * pages stress that at these speeds each operator lasts microseconds and the
+ * gaps between operators matter (techllm.github.io "Xiaomi MiMo x TileRT",
+ * section "3. TileRT"), so the stages are timed one by one.  The stages, in
+ * launch order: 0 routing, 1 permutation, 2 gate/up + SwiGLU, 3 down +
+ * routing weight, 4 combine.
+ *
+ * moe_mxfp4_stage_timing(ctx, capacity): capacity > 0 creates capacity *
+ * (MOE_MXFP4_NUM_STAGES + 1) HIP events (host call, never inside forward)
+ * and makes each later forward call record one event before the first stage
+ * and one after each stage, into slot (call index % capacity); capacity 0
+ * destroys the events and stops recording.  Errors: INVALID_ARG, HIP.
+ *
+ * moe_mxfp4_stage_times(ctx, total_ms, calls): waits for the last recorded
+ * event, writes the summed milliseconds of each stage over the recorded
+ * calls still held (at most capacity) into total_ms (host float
+ * [MOE_MXFP4_NUM_STAGES]) and their number into *calls (host), then starts
+ * a new count.  Stage i of a call spans event i to event i+1, so it includes
+ * any launch gap before that stage's kernel.  Errors: INVALID_ARG (null
+ * pointer, timing not enabled), HIP.  Timing calls are not thread safe.
+ */
+#define MOE_MXFP4_NUM_STAGES 5
+moe_status moe_mxfp4_stage_timing(moe_mxfp4_ctx* ctx, int32_t capacity);
+moe_status moe_mxfp4_stage_times(moe_mxfp4_ctx* ctx, float* total_ms, int32_t* calls);
 
 /*
  * Weight preparation (off the forward path): quantise a row-major float

@@ -27,7 +27,10 @@ OUT_BF16, OUT_F32 = 0, 1
 # Every symbol include/moe_mxfp4.h declares.
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create",
            "moe_mxfp4_destroy", "moe_mxfp4_workspace_bytes", "moe_mxfp4_forward",
-           "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights")
+           "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights", "moe_mxfp4_stage_timing",
+           "moe_mxfp4_stage_times")
+NUM_STAGES = 5
+STAGES = ("route", "sort", "gateup", "down", "combine")
 
 
 class MoeError(RuntimeError):
@@ -82,6 +85,11 @@ def lib():
         L.moe_mxfp4_debug_dequant.restype = ctypes.c_int
         L.moe_mxfp4_quantize_weights.argtypes = [P, i64, i64, P, P, P]
         L.moe_mxfp4_quantize_weights.restype = ctypes.c_int
+        L.moe_mxfp4_stage_timing.argtypes = [P, i32]
+        L.moe_mxfp4_stage_timing.restype = ctypes.c_int
+        L.moe_mxfp4_stage_times.argtypes = [P, ctypes.POINTER(ctypes.c_float),
+                                            ctypes.POINTER(i32)]
+        L.moe_mxfp4_stage_times.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -175,6 +183,17 @@ class MoeMxfp4:
         return out
 
     __call__ = forward
+
+    def stage_timing(self, capacity: int):
+        """Record HIP events around each stage of the next forward calls."""
+        _check(lib().moe_mxfp4_stage_timing(self._ctx, capacity), "moe_mxfp4_stage_timing")
+
+    def stage_times(self):
+        """(per-stage summed ms as a dict, number of calls) since the last read."""
+        ms = (ctypes.c_float * NUM_STAGES)()
+        n = ctypes.c_int32()
+        _check(lib().moe_mxfp4_stage_times(self._ctx, ms, ctypes.byref(n)), "moe_mxfp4_stage_times")
+        return dict(zip(STAGES, list(ms))), n.value
 
     def debug_dequant(self, expert: int, matrix: int, row0: int, nrows: int, out=None, stream=None):
         import torch

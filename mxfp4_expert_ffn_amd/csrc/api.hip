@@ -10,12 +10,17 @@
 #include <stdlib.h>
 
 #include <new>
+#include <vector>
 
 #include "common.hpp"
 
 struct moe_mxfp4_ctx {
     moe_mxfp4_config cfg;
     moe_mxfp4_weights w;
+    // optional stage timing: capacity slots of NUM_STAGES + 1 events each
+    std::vector<hipEvent_t> events;
+    int32_t capacity = 0;
+    int64_t ncalls = 0;
 };
 
 namespace {
@@ -103,7 +108,54 @@ moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg, const moe_mxfp4_weights
 }
 
 moe_status moe_mxfp4_destroy(moe_mxfp4_ctx* ctx) {
+    if (ctx)
+        for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
     delete ctx;
+    return MOE_OK;
+}
+
+moe_status moe_mxfp4_stage_timing(moe_mxfp4_ctx* ctx, int32_t capacity) {
+    if (!ctx || capacity < 0) return MOE_ERR_INVALID_ARG;
+    for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
+    ctx->events.clear();
+    ctx->capacity = 0;
+    ctx->ncalls = 0;
+    if (capacity == 0) return MOE_OK;
+    const size_t n = (size_t)capacity * (MOE_MXFP4_NUM_STAGES + 1);
+    ctx->events.reserve(n);
+    for (size_t i = 0; i < n; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (hipEvent_t x : ctx->events) (void)hipEventDestroy(x);
+            ctx->events.clear();
+            return MOE_ERR_HIP;
+        }
+        ctx->events.push_back(e);
+    }
+    ctx->capacity = capacity;
+    return MOE_OK;
+}
+
+moe_status moe_mxfp4_stage_times(moe_mxfp4_ctx* ctx, float* total_ms, int32_t* calls) {
+    if (!ctx || !total_ms || !calls || ctx->capacity == 0) return MOE_ERR_INVALID_ARG;
+    const int64_t held = ctx->ncalls < ctx->capacity ? ctx->ncalls : ctx->capacity;
+    for (int i = 0; i < MOE_MXFP4_NUM_STAGES; ++i) total_ms[i] = 0.f;
+    *calls = (int32_t)held;
+    if (held > 0) {
+        const int64_t last = (ctx->ncalls - 1) % ctx->capacity;
+        if (hipEventSynchronize(ctx->events[last * (MOE_MXFP4_NUM_STAGES + 1) + MOE_MXFP4_NUM_STAGES]) !=
+            hipSuccess)
+            return MOE_ERR_HIP;
+        for (int64_t slot = 0; slot < held; ++slot) {
+            hipEvent_t* ev = &ctx->events[slot * (MOE_MXFP4_NUM_STAGES + 1)];
+            for (int i = 0; i < MOE_MXFP4_NUM_STAGES; ++i) {
+                float ms = 0.f;
+                if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) return MOE_ERR_HIP;
+                total_ms[i] += ms;
+            }
+        }
+    }
+    ctx->ncalls = 0;
     return MOE_OK;
 }
 
@@ -146,11 +198,18 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const uint16_t* x = static_cast<const uint16_t*>(hidden);
 
-    if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_sort(dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_gateup(x, ctx->w, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_down(ctx->w, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess) return MOE_ERR_HIP;
+    hipEvent_t* ev = nullptr;
+    if (ctx->capacity > 0)
+        ev = &ctx->events[(size_t)(ctx->ncalls++ % ctx->capacity) * (MOE_MXFP4_NUM_STAGES + 1)];
+    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+
+    if (mark(0) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_sort(dm, ws, s) != hipSuccess || mark(2) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup(x, ctx->w, dm, ws, s) != hipSuccess || mark(3) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down(ctx->w, dm, ws, s) != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess || mark(5) != hipSuccess)
+        return MOE_ERR_HIP;
 
     if (debug_out) {
         const size_t P = (size_t)dm.P;
