@@ -39,7 +39,8 @@ def weight_shapes(w):
 
 def pack_on_gpu(w, copies, moe, torch):
     """Generate fp32 expert weights (synth), pack them with the library's
-    quantiser on the GPU, and clone into `copies` independent copies."""
+    quantiser on the GPU, convert to the tiled layout the forward path reads,
+    and clone into `copies` independent copies."""
     import synth
     shapes = weight_shapes(w)
     packed = {n: torch.empty(s, dtype=torch.uint8, device="cuda") for n, s in shapes.items()}
@@ -47,10 +48,12 @@ def pack_on_gpu(w, copies, moe, torch):
         for name, m in (("w_gate", g), ("w_up", u), ("w_down", dn)):
             t = torch.from_numpy(m).cuda()
             moe.quantize_weights(t, packed=packed[name][e], scales=packed[name + "_scale"][e])
+    tiled = moe.tile_expert_weights(packed)
+    del packed
     torch.cuda.synchronize()
-    out = [packed]
+    out = [tiled]
     for _ in range(copies - 1):
-        out.append({n: t.clone() for n, t in packed.items()})
+        out.append({n: t.clone() for n, t in tiled.items()})
     torch.cuda.synchronize()
     return out
 

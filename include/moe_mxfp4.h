@@ -84,8 +84,8 @@ typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
 typedef struct {
     uint32_t struct_size;    /* sizeof(moe_mxfp4_config)                        */
     int32_t num_experts;     /* E, 1..512                                       */
-    int32_t d_model;         /* d, multiple of 256                              */
-    int32_t d_ff;            /* f, multiple of 256                              */
+    int32_t d_model;         /* d, 256 or a multiple of 512                     */
+    int32_t d_ff;            /* f, 256 or a multiple of 512                     */
     int32_t top_k;           /* k, 1..min(E, 32)                                */
     int32_t max_tokens;      /* upper bound of num_tokens per forward call, >= 1 */
     int32_t act_mode;        /* moe_act_mode                                    */
@@ -94,15 +94,35 @@ typedef struct {
 } moe_mxfp4_config;
 
 /*
- * Packed MXFP4 expert weights (device, borrowed: the caller keeps them alive
- * and unchanged until moe_mxfp4_destroy).  Each matrix is row-major with one
- * output unit per row and the reduction dimension K along the row:
- *   w_gate, w_up : uint8 [E][d_ff][d_model/2],  scales uint8 [E][d_ff][d_model/32]
- *   w_down       : uint8 [E][d_model][d_ff/2],  scales uint8 [E][d_model][d_ff/32]
- * Element kk of a row is in byte kk/2: the LOW nibble holds even kk, the high
- * nibble odd kk.  A nibble is an E2M1 code (sign bit 3; magnitudes 0, 0.5, 1,
- * 1.5, 2, 3, 4, 6).  Scale byte kk/32 of the same row is the E8M0 exponent of
- * that block: the element's value is E2M1(code) * 2^(byte - 127).
+ * MXFP4 matrices.  Every expert matrix has one output unit per row and the
+ * reduction dimension K along the row: W_gate and W_up are [d_ff][d_model]
+ * (K = d_model), W_down is [d_model][d_ff] (K = d_ff).  An element is a
+ * 4-bit E2M1 code (sign bit 3; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) and
+ * every block of 32 consecutive elements of a row shares one E8M0 scale
+ * byte: value = E2M1(code) * 2^(byte - 127).
+ *
+ * ROW-MAJOR layout (the interchange form; moe_mxfp4_quantize_weights writes
+ * it): packed uint8 [rows][K/2], element k of a row in byte k/2 (LOW nibble
+ * = even k, high nibble = odd k); scales uint8 [rows][K/32], byte k/32.
+ *
+ * TILED layout (what the forward path reads; moe_mxfp4_tile_weights converts
+ * row-major to it).  With ns = K/128 steps and ng = ceil(K/512) scale groups,
+ * the 16-byte block of row-major row n, MX block b (elements 32b..32b+31, in
+ * row-major byte order) is stored at byte
+ *     16 * (64 * ((n/16) * ns + b/4) + (n%16) + 16 * (b%4))
+ * so each 1 KB holds 16 rows x 128 elements in the order the matrix-core
+ * operand consumes them, and a 16-row tile streams contiguously along K.
+ * Scale byte (n, b) is stored at byte
+ *     4 * (64 * ((n/16) * ng + b/16) + (n%16) + 16 * (b%4)) + (b/4) % 4
+ * (unused bytes of a partial last group are zero).  Sizes: packed rows*K/2
+ * bytes (as row-major); scales (rows/16) * ng * 256 bytes.  rows % 16 == 0.
+ * Several experts' matrices stacked along rows convert in one call.
+ *
+ * Expert weights handed to the forward path (device, TILED, borrowed: the
+ * caller keeps them alive and unchanged until moe_mxfp4_destroy):
+ *   w_gate, w_up : E matrices [d_ff][d_model] stacked (rows = E*d_ff)
+ *   w_down       : E matrices [d_model][d_ff] stacked (rows = E*d_model)
+ * each with its tiled scales.
  */
 typedef struct {
     const uint8_t* w_gate;
@@ -184,10 +204,11 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden,
 
 /*
  * Decode rows [row0, row0 + nrows) of one expert matrix (0 gate, 1 up,
- * 2 down) with the forward path's own in-register FP4 decode, widened to
- * float: out (device) float [nrows][K], K = d_model for gate/up, d_ff for
- * down.  For checking the decode bit for bit.  Errors: INVALID_ARG (bad
- * expert, matrix or row range, null out), ALIGNMENT, HIP.
+ * 2 down) from the context's TILED weights with the forward path's own
+ * in-register FP4 decode, widened to float: out (device) float [nrows][K]
+ * in row-major order, K = d_model for gate/up, d_ff for down.  For checking
+ * the layout and the decode bit for bit.  Errors: INVALID_ARG (bad expert,
+ * matrix or row range, null out), ALIGNMENT, HIP.
  */
 moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
                                    int32_t matrix, int32_t row0, int32_t nrows,
@@ -221,17 +242,32 @@ moe_status moe_mxfp4_stage_times(moe_mxfp4_ctx* ctx, float* total_ms, int32_t* c
 
 /*
  * Weight preparation (off the forward path): quantise a row-major float
- * matrix w (device) [rows][K] into the packed layout above -- per block of
- * 32 along K, scale 2^(floor(log2(amax)) - 2) clamped to the E8M0 range
- * (an all-zero block gets byte 0), elements rounded to the nearest E2M1
- * value with ties to the even code, saturating at +-6, the sign of a value
- * that rounds to zero kept.  packed (device) uint8 [rows][K/2], scales
+ * matrix w (device) [rows][K] into the ROW-MAJOR packed layout above -- per
+ * block of 32 along K, scale 2^(floor(log2(amax)) - 2) clamped to the E8M0
+ * range (an all-zero block gets byte 0), elements rounded to the nearest
+ * E2M1 value with ties to the even code, saturating at +-6, the sign of a
+ * value that rounds to zero kept.  packed (device) uint8 [rows][K/2], scales
  * (device) uint8 [rows][K/32].  K must be a positive multiple of 32.
  * Errors: INVALID_ARG, ALIGNMENT, HIP.
  */
 moe_status moe_mxfp4_quantize_weights(const float* w, int64_t rows, int64_t K,
                                       uint8_t* packed, uint8_t* scales,
                                       void* hip_stream);
+
+/* Bytes of the TILED scale array of a rows x K matrix (0 if rows % 16 or
+ * K % 128 is nonzero or a size is not positive). */
+size_t moe_mxfp4_tiled_scale_bytes(int64_t rows, int64_t K);
+
+/*
+ * Weight preparation: convert a ROW-MAJOR packed matrix (device packed
+ * [rows][K/2], scales [rows][K/32]) to the TILED layout (device tiled_packed
+ * rows*K/2 bytes, tiled_scales moe_mxfp4_tiled_scale_bytes(rows, K) bytes).
+ * A pure byte permutation; inputs and outputs must not overlap.  rows % 16
+ * == 0 and K % 128 == 0.  Errors: INVALID_ARG, ALIGNMENT, HIP.
+ */
+moe_status moe_mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales,
+                                  int64_t rows, int64_t K, uint8_t* tiled_packed,
+                                  uint8_t* tiled_scales, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ OUT_BF16, OUT_F32 = 0, 1
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create",
            "moe_mxfp4_destroy", "moe_mxfp4_workspace_bytes", "moe_mxfp4_forward",
            "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights", "moe_mxfp4_stage_timing",
-           "moe_mxfp4_stage_times")
+           "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights")
 NUM_STAGES = 5
 STAGES = ("route", "sort", "gateup", "down", "combine")
 
@@ -85,6 +85,10 @@ def lib():
         L.moe_mxfp4_debug_dequant.restype = ctypes.c_int
         L.moe_mxfp4_quantize_weights.argtypes = [P, i64, i64, P, P, P]
         L.moe_mxfp4_quantize_weights.restype = ctypes.c_int
+        L.moe_mxfp4_tiled_scale_bytes.argtypes = [i64, i64]
+        L.moe_mxfp4_tiled_scale_bytes.restype = sz
+        L.moe_mxfp4_tile_weights.argtypes = [P, P, i64, i64, P, P, P]
+        L.moe_mxfp4_tile_weights.restype = ctypes.c_int
         L.moe_mxfp4_stage_timing.argtypes = [P, i32]
         L.moe_mxfp4_stage_timing.restype = ctypes.c_int
         L.moe_mxfp4_stage_times.argtypes = [P, ctypes.POINTER(ctypes.c_float),
@@ -122,10 +126,10 @@ def make_config(num_experts, d_model, d_ff, top_k, max_tokens, act_mode=ACT_BF16
 class MoeMxfp4:
     """One expert layer: borrowed packed weights + configuration.
 
-    ``weights``: dict of uint8 CUDA tensors ``w_gate [E, f, d/2]``,
-    ``w_gate_scale [E, f, d/32]``, ``w_up``, ``w_up_scale`` (same shapes),
-    ``w_down [E, d, f/2]``, ``w_down_scale [E, d, f/32]``.  References are
-    kept for the life of this object.
+    ``weights``: dict of uint8 CUDA tensors in the TILED layout of the C
+    header (``tile_expert_weights`` converts the row-major form): ``w_gate``,
+    ``w_gate_scale``, ``w_up``, ``w_up_scale``, ``w_down``, ``w_down_scale``.
+    References are kept for the life of this object.
     """
 
     def __init__(self, weights: dict, num_experts: int, d_model: int, d_ff: int, top_k: int,
@@ -216,3 +220,31 @@ def quantize_weights(w, packed=None, scales=None, stream=None):
     _check(lib().moe_mxfp4_quantize_weights(_ptr(w), rows, K, _ptr(packed), _ptr(scales),
                                             _stream(stream)), "moe_mxfp4_quantize_weights")
     return packed, scales
+
+
+def tiled_scale_bytes(rows: int, K: int) -> int:
+    return lib().moe_mxfp4_tiled_scale_bytes(rows, K)
+
+
+def tile_weights(packed, scales, stream=None):
+    """Row-major packed [rows, K/2] + scales [rows, K/32] (uint8 CUDA) -> tiled
+    (packed uint8 [rows*K/2], scales uint8 [tiled_scale_bytes(rows, K)])."""
+    import torch
+    rows, K = packed.shape[0], packed.shape[1] * 2
+    tp = torch.empty(rows * K // 2, dtype=torch.uint8, device=packed.device)
+    ts = torch.empty(tiled_scale_bytes(rows, K), dtype=torch.uint8, device=packed.device)
+    _check(lib().moe_mxfp4_tile_weights(_ptr(packed), _ptr(scales), rows, K, _ptr(tp), _ptr(ts),
+                                        _stream(stream)), "moe_mxfp4_tile_weights")
+    return tp, ts
+
+
+def tile_expert_weights(rowmajor: dict, stream=None) -> dict:
+    """Row-major expert weights (uint8 CUDA tensors shaped [E, N, K/2] and
+    [E, N, K/32]) -> the tiled dict the forward path takes."""
+    out = {}
+    for name in ("w_gate", "w_up", "w_down"):
+        p, sc = rowmajor[name], rowmajor[name + "_scale"]
+        E, N, half = p.shape
+        tp, ts = tile_weights(p.reshape(E * N, half), sc.reshape(E * N, sc.shape[2]), stream)
+        out[name], out[name + "_scale"] = tp, ts
+    return out

@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t ids, w, offsets, sorted, inverse, active, h, o, total;
+    size_t ids, w, offsets, sorted, inverse, active, chunks, nchunks, h, o, total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
@@ -45,6 +45,9 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     L.sorted = at;  at += round256(P * sizeof(int32_t));
     L.inverse = at; at += round256(P * sizeof(int32_t));
     L.active = at;  at += round256((size_t)(c.num_experts + 1) * sizeof(int32_t));
+    moe::Dims dm{(int32_t)T, c.d_model, c.d_ff, c.num_experts, c.top_k, (int32_t)P};
+    L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * 2 * sizeof(int32_t));
+    L.nchunks = at; at += 256;
     L.h = at;       at += round256(P * (size_t)c.d_ff * sizeof(uint16_t));
     L.o = at;       at += round256(P * (size_t)c.d_model * sizeof(float));
     L.total = at;
@@ -61,7 +64,9 @@ moe_status check_config(const moe_mxfp4_config* c) {
         return MOE_ERR_INVALID_ARG;
     if (c->num_experts > kMaxExperts || c->top_k > kMaxTopK || c->top_k > c->num_experts)
         return MOE_ERR_UNSUPPORTED_SHAPE;
-    if (c->d_model % 256 != 0 || c->d_ff % 256 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
+    // K steps per matrix: 2 or a multiple of 4 (the kernels' pipeline depths)
+    for (int32_t K : {c->d_model, c->d_ff})
+        if (K != 256 && K % 512 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->max_tokens * c->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->d_model * c->d_ff > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
     if (c->act_mode == MOE_ACT_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED_SHAPE;   // not built yet
@@ -191,6 +196,8 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     ws.sorted_pairs = reinterpret_cast<int32_t*>(base + L.sorted);
     ws.inverse = reinterpret_cast<int32_t*>(base + L.inverse);
     ws.active = reinterpret_cast<int32_t*>(base + L.active);
+    ws.chunks = reinterpret_cast<int32_t*>(base + L.chunks);
+    ws.nchunks = reinterpret_cast<int32_t*>(base + L.nchunks);
     ws.h = reinterpret_cast<uint16_t*>(base + L.h);
     ws.o = reinterpret_cast<float*>(base + L.o);
 
@@ -237,9 +244,10 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert, int
     if (nrows == 0) return MOE_OK;
     const uint8_t* P = matrix == 0 ? ctx->w.w_gate : matrix == 1 ? ctx->w.w_up : ctx->w.w_down;
     const uint8_t* S = matrix == 0 ? ctx->w.w_gate_scale : matrix == 1 ? ctx->w.w_up_scale : ctx->w.w_down_scale;
-    const int64_t row = (int64_t)expert * N + row0;
-    if (moe::launch_debug_dequant(P + row * (K / 2), S + row * (K / MOE_MXFP4_BLOCK), K, nrows, out,
-                                  static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+    const uint8_t* Pe = P + (int64_t)expert * N * (K / 2);
+    const uint8_t* Se = S + (int64_t)expert * moe::tiled_scale_bytes(N, K);
+    if (moe::launch_debug_dequant(Pe, Se, K, row0, nrows, out, static_cast<hipStream_t>(hip_stream)) !=
+        hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -251,6 +259,25 @@ moe_status moe_mxfp4_quantize_weights(const float* w, int64_t rows, int64_t K, u
     if (!aligned16(w) || !aligned16(packed) || !aligned16(scales)) return MOE_ERR_ALIGNMENT;
     if (rows == 0) return MOE_OK;
     if (moe::launch_quantize(w, rows, K, packed, scales, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+size_t moe_mxfp4_tiled_scale_bytes(int64_t rows, int64_t K) {
+    if (rows <= 0 || K <= 0 || rows % 16 != 0 || K % 128 != 0) return 0;
+    return (size_t)moe::tiled_scale_bytes(rows, K);
+}
+
+moe_status moe_mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K,
+                                  uint8_t* tiled_packed, uint8_t* tiled_scales, void* hip_stream) {
+    if (!packed || !scales || !tiled_packed || !tiled_scales || rows < 0 || K <= 0 || rows % 16 != 0 ||
+        K % 128 != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(packed) || !aligned16(scales) || !aligned16(tiled_packed) || !aligned16(tiled_scales))
+        return MOE_ERR_ALIGNMENT;
+    if (rows == 0) return MOE_OK;
+    if (moe::launch_tile(packed, scales, rows, K, tiled_packed, tiled_scales,
+                         static_cast<hipStream_t>(hip_stream)) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -38,22 +38,63 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const float* __r
     }
 }
 
-// Decode export: one thread per 8 elements (one packed dword), with the
-// forward path's decode8_bf16, widened to float.
+// Tiled-layout addressing (the byte formulas of the header).
+__device__ __forceinline__ int64_t tiled_block_offset(int64_t n, int64_t b, int64_t ns) {
+    return 16 * (64 * ((n / 16) * ns + b / 4) + (n % 16) + 16 * (b % 4));
+}
+__device__ __forceinline__ int64_t tiled_scale_offset(int64_t n, int64_t b, int64_t ng) {
+    return 4 * (64 * ((n / 16) * ng + b / 16) + (n % 16) + 16 * (b % 4)) + (b / 4) % 4;
+}
+
+// Decode export: one thread per 8 elements (one packed dword) of rows
+// [row0, row0 + nrows) of one tiled matrix, with the forward path's
+// decode8_bf16, widened to float, written row-major.
 __global__ __launch_bounds__(kThreads) void k_debug_dequant(const uint8_t* __restrict__ packed,
                                                             const uint8_t* __restrict__ scales,
-                                                            int64_t K, int32_t nrows,
+                                                            int64_t K, int32_t row0, int32_t nrows,
                                                             float* __restrict__ out) {
     const int64_t per_row = K / 8;
     const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= per_row * nrows) return;
-    const int64_t r = gid / per_row, c8 = gid % per_row;
-    const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + r * (K / 2) + c8 * 4);
-    const uint32_t sb = scales[r * (K / kBlock) + (c8 * 8) / kBlock];
+    const int64_t i = gid / per_row, c8 = gid % per_row;
+    const int64_t n = row0 + i, b = c8 / 4;
+    const int64_t ns = K / kKStep, ng = (ns + 3) / 4;
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + tiled_block_offset(n, b, ns) + (c8 % 4) * 4);
+    const uint32_t sb = scales[tiled_scale_offset(n, b, ng)];
     const bf16x8_t v = decode8_bf16(word, e8m0_as_scale(sb));
-    float* dst = out + r * K + c8 * 8;
+    float* dst = out + i * K + c8 * 8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = (float)v[i];
+    for (int k = 0; k < 8; ++k) dst[k] = (float)v[k];
+}
+
+// Row-major -> tiled: one thread per 16-byte MX block of packed data.
+__global__ __launch_bounds__(kThreads) void k_tile_packed(const uint8_t* __restrict__ src, int64_t rows,
+                                                          int64_t K, uint8_t* __restrict__ dst) {
+    const int64_t nb = K / kBlock;
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= rows * nb) return;
+    const int64_t n = gid / nb, b = gid % nb;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src + n * (K / 2) + b * 16);
+    *reinterpret_cast<u32x4_t*>(dst + tiled_block_offset(n, b, K / kKStep)) = v;
+}
+
+// Row-major -> tiled scales: one thread per output dword (16-row tile t,
+// group G, lane L): bytes j = 0..3 are the scales of step 4G + j (zero past
+// the last step).
+__global__ __launch_bounds__(kThreads) void k_tile_scales(const uint8_t* __restrict__ src, int64_t rows,
+                                                          int64_t K, uint8_t* __restrict__ dst) {
+    const int64_t ns = K / kKStep, ng = (ns + 3) / 4, nb = K / kBlock;
+    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= (rows / 16) * ng * 64) return;
+    const int64_t L = gid % 64, G = (gid / 64) % ng, t = gid / (64 * ng);
+    const int64_t n = 16 * t + L % 16;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t step = 4 * G + j;
+        if (step < ns) word |= (uint32_t)src[n * nb + 4 * step + L / 16] << (8 * j);
+    }
+    *reinterpret_cast<uint32_t*>(dst + 4 * gid) = word;
 }
 
 // E2M1 code of one already-scaled value: nearest of 0, .5, 1, 1.5, 2, 3, 4, 6
@@ -113,11 +154,25 @@ hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int o
     return hipGetLastError();
 }
 
-hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t nrows,
-                                float* out, hipStream_t s) {
+hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t row0,
+                                int32_t nrows, float* out, hipStream_t s) {
     const int64_t n = (K / 8) * nrows;
     hipLaunchKernelGGL(k_debug_dequant, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                       packed, scales, K, nrows, out);
+                       packed, scales, K, row0, nrows, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K,
+                       uint8_t* tpacked, uint8_t* tscales, hipStream_t s) {
+    const int64_t nb = rows * (K / kBlock);
+    hipLaunchKernelGGL(k_tile_packed, dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       packed, rows, K, tpacked);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t ns = K / kKStep, ng = (ns + 3) / 4;
+    const int64_t nw = (rows / 16) * ng * 64;
+    hipLaunchKernelGGL(k_tile_scales, dim3((unsigned)((nw + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       scales, rows, K, tscales);
     return hipGetLastError();
 }
 

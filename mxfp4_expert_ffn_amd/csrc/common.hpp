@@ -15,6 +15,7 @@ namespace moe {
 constexpr int kWave = 64;          // CDNA wavefront
 constexpr int kBlock = 32;         // MX block (elements per E8M0 scale)
 constexpr int kKStep = 128;        // K per main-loop step: 4 MX blocks, one per lane group
+constexpr int kChunk = 64;         // token pairs per expert work chunk
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -62,6 +63,8 @@ struct Workspace {
     int32_t* sorted_pairs;    // [P]
     int32_t* inverse;         // [P]   position of pair p in sorted_pairs
     int32_t* active;          // [E+1] active experts (count > 0) by descending count; [E] = how many
+    int32_t* chunks;          // [max_chunks][2] (expert, first pair within the expert)
+    int32_t* nchunks;         // [1] number of chunks
     uint16_t* h;              // [P][f] bf16, rows in sorted order
     float* o;                 // [P][d] weighted expert outputs, rows in sorted order
 };
@@ -70,6 +73,13 @@ struct Workspace {
 struct Dims {
     int32_t T, d, f, E, k, P;
 };
+
+// Upper bound of the chunk list: one partial chunk per active expert plus
+// the full chunks.
+inline int max_chunks(const Dims& dm) {
+    const int active = dm.E < dm.P ? dm.E : dm.P;
+    return active + dm.P / kChunk;
+}
 
 // Kernel launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s);
@@ -80,8 +90,15 @@ hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspa
                        hipStream_t s);
 hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype,
                            hipStream_t s);
-hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K,
+hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t row0,
                                 int32_t nrows, float* out, hipStream_t s);
+hipError_t launch_tile(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K,
+                       uint8_t* tpacked, uint8_t* tscales, hipStream_t s);
+
+// Bytes of the tiled scale array of one rows x K matrix.
+inline int64_t tiled_scale_bytes(int64_t rows, int64_t K) {
+    return (rows / 16) * ((K / kKStep + 3) / 4) * 256;
+}
 hipError_t launch_quantize(const float* w, int64_t rows, int64_t K, uint8_t* packed,
                            uint8_t* scales, hipStream_t s);
 

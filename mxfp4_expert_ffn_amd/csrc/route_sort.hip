@@ -103,12 +103,16 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ sorted,
                                                        int32_t* __restrict__ inverse,
-                                                       int32_t* __restrict__ active) {
+                                                       int32_t* __restrict__ active,
+                                                       int32_t* __restrict__ chunks,
+                                                       int32_t* __restrict__ nchunks) {
     extern __shared__ int32_t sm[];
     const int E = dm.E, P = dm.P;
     int32_t* hist = sm;                               // [kSortWaves][E]
     int32_t* counts = sm + kSortWaves * E;            // [E]
-    int32_t* wsum = counts + E;                       // [16]
+    int32_t* act = counts + E;                        // [E] active experts in rank order
+    int32_t* wsum = act + E;                          // [16]
+    int32_t* wsum2 = wsum + kSortWaves;               // [16]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
 
@@ -164,14 +168,35 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
                 r += (c2 > c) || (c2 == c && e2 < tid);
             }
             active[r] = tid;
+            act[r] = tid;
         }
     }
+    // number of active experts = number of nonzero counts
+    const int nz = __popcll(__ballot(tid < E && c > 0));
+    if (lane == 0) wsum2[wave] = nz;
+    __syncthreads();
+    int na = 0;
+    for (int w = 0; w < kSortWaves; ++w) na += wsum2[w];
     if (tid == 0) {
         offsets[E] = P;
-        int na = 0;
-        for (int e2 = 0; e2 < E; ++e2) na += counts[e2] > 0;
         active[E] = na;
     }
+    // work chunks of <= kChunk pairs, expert by expert in rank order
+    const int nch = tid < na ? (counts[act[tid]] + kChunk - 1) / kChunk : 0;
+    const int nincl = wave_inclusive_scan(nch, lane);
+    __syncthreads();                                   // wsum is reused below
+    if (lane == kWave - 1) wsum[wave] = nincl;
+    __syncthreads();
+    int cbefore = 0;
+    for (int w = 0; w < wave; ++w) cbefore += wsum[w];
+    if (tid < na) {
+        const int first = cbefore + nincl - nch;
+        for (int q = 0; q < nch; ++q) {
+            chunks[2 * (first + q)] = act[tid];
+            chunks[2 * (first + q) + 1] = q * kChunk;
+        }
+    }
+    if (tid == kSortThreads - 1) *nchunks = cbefore + nincl;
     __syncthreads();
 
     // 3) scatter in the same visiting order: stable within each expert
@@ -200,9 +225,9 @@ hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws
 }
 
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, hipStream_t s) {
-    const size_t lds = sizeof(int32_t) * ((size_t)kSortWaves * dm.E + dm.E + 16);
+    const size_t lds = sizeof(int32_t) * ((size_t)kSortWaves * dm.E + 2 * dm.E + 2 * kSortWaves);
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
-                       ws.sorted_pairs, ws.inverse, ws.active);
+                       ws.sorted_pairs, ws.inverse, ws.active, ws.chunks, ws.nchunks);
     return hipGetLastError();
 }
 

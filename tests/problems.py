@@ -46,8 +46,14 @@ def problem(w: synth.Workload):
 
 
 def to_device(weights: dict):
+    """Row-major oracle-packed weights -> the library's tiled layout on the GPU
+    (the conversion is the library's own moe_mxfp4_tile_weights)."""
     import torch
-    return {n: torch.from_numpy(np.ascontiguousarray(weights[n])).cuda() for n in WNAMES}
+    import mxfp4_expert_ffn_amd as moe
+    rm = {n: torch.from_numpy(np.ascontiguousarray(weights[n])).cuda() for n in WNAMES}
+    tiled = moe.tile_expert_weights(rm)
+    torch.cuda.synchronize()
+    return tiled
 
 
 def rel_max_err(y, ref) -> float:

@@ -154,3 +154,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         moe.lib()
+
+
+def test_tiled_scale_bytes_and_tile_validation():
+    L = moe.lib()
+    assert L.moe_mxfp4_tiled_scale_bytes(32, 256) == 2 * 1 * 256
+    assert L.moe_mxfp4_tiled_scale_bytes(16, 4096) == 1 * 8 * 256
+    assert L.moe_mxfp4_tiled_scale_bytes(1536, 1536) == 96 * 3 * 256
+    assert L.moe_mxfp4_tiled_scale_bytes(8, 256) == 0 and L.moe_mxfp4_tiled_scale_bytes(16, 96) == 0
+    t = L.moe_mxfp4_tile_weights
+    assert t(FAKE, FAKE, 8, 256, FAKE, FAKE, None) == 1        # rows % 16
+    assert t(FAKE, FAKE, 16, 96, FAKE, FAKE, None) == 1        # K % 128
+    assert t(None, FAKE, 16, 256, FAKE, FAKE, None) == 1
+    assert t(FAKE, FAKE, 16, 256, FAKE + 4, FAKE, None) == 4
+    assert t(FAKE, FAKE, 0, 256, FAKE, FAKE, None) == 0
+
+
+def test_create_rejects_k_without_a_pipeline():
+    st, _ = _create(d_model=768)           # 6 steps: neither 2 nor a multiple of 4
+    assert st == 2
+    st, _ = _create(d_ff=768)
+    assert st == 2
+    st, h = _create(d_model=1024, d_ff=256)
+    assert st == 0 and moe.lib().moe_mxfp4_destroy(h) == 0

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from tests import problems
+from tests import problems, tiling
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -227,3 +227,15 @@ def test_deterministic_and_workspace_reuse():
     ref = oracle.moe_forward(acts["x_bf16"][:7], acts["logits"][:7], wts, w.k)["y"]
     assert problems.rel_max_err(small.cpu().numpy(), ref) <= TOL
     assert torch.equal(big, a)
+
+
+def test_tile_weights_matches_header_formula():
+    moe = _moe()
+    rng = np.random.default_rng(70)
+    for rows, K in ((32, 256), (48, 512), (16, 1536), (64, 2048)):
+        p = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
+        s = rng.integers(0, 255, (rows, K // 32), dtype=np.uint8)
+        tp, ts = moe.tile_weights(torch.from_numpy(p).cuda(), torch.from_numpy(s).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(tp.cpu().numpy(), tiling.tile_packed(p)), (rows, K)
+        assert np.array_equal(ts.cpu().numpy(), tiling.tile_scales(s)), (rows, K)
