@@ -88,7 +88,7 @@ typedef struct {
     int32_t d_ff;            /* f, 256 or a multiple of 512                     */
     int32_t top_k;           /* k, 1..min(E, 32)                                */
     int32_t max_tokens;      /* upper bound of num_tokens per forward call, >= 1 */
-    int32_t act_mode;        /* moe_act_mode                                    */
+    int32_t act_mode;        /* moe_act_mode (MXFP8: d_model, d_ff <= 8192)     */
     int32_t out_dtype;       /* moe_out_dtype                                   */
     uint32_t flags;          /* reserved, must be 0                             */
 } moe_mxfp4_config;
@@ -219,8 +219,9 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
  * pages stress that at these speeds each operator lasts microseconds and the
  * gaps between operators matter (techllm.github.io "Xiaomi MiMo x TileRT",
  * section "3. TileRT"), so the stages are timed one by one.  The stages, in
- * launch order: 0 routing, 1 permutation, 2 gate/up + SwiGLU, 3 down +
- * routing weight, 4 combine.
+ * launch order: 0 routing, 1 permutation, 2 MXFP8 quantisation of the
+ * activations (empty in bf16 mode), 3 gate/up + SwiGLU, 4 down + routing
+ * weight, 5 combine.
  *
  * moe_mxfp4_stage_timing(ctx, capacity): capacity > 0 creates capacity *
  * (MOE_MXFP4_NUM_STAGES + 1) HIP events (host call, never inside forward)
@@ -236,7 +237,7 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
  * any launch gap before that stage's kernel.  Errors: INVALID_ARG (null
  * pointer, timing not enabled), HIP.  Timing calls are not thread safe.
  */
-#define MOE_MXFP4_NUM_STAGES 5
+#define MOE_MXFP4_NUM_STAGES 6
 moe_status moe_mxfp4_stage_timing(moe_mxfp4_ctx* ctx, int32_t capacity);
 moe_status moe_mxfp4_stage_times(moe_mxfp4_ctx* ctx, float* total_ms, int32_t* calls);
 
@@ -253,6 +254,23 @@ moe_status moe_mxfp4_stage_times(moe_mxfp4_ctx* ctx, float* total_ms, int32_t* c
 moe_status moe_mxfp4_quantize_weights(const float* w, int64_t rows, int64_t K,
                                       uint8_t* packed, uint8_t* scales,
                                       void* hip_stream);
+
+/*
+ * MXFP8 quantisation of bf16 activations, the kernel the forward path runs
+ * in MOE_ACT_MXFP8_E4M3 mode (exposed for callers that quantise ahead and
+ * for checking it bit for bit): x (device) bf16 [rows][K] -> codes (device)
+ * uint8 [rows][K] OCP E4M3, scales (device) uint8 [rows][K/32] E8M0.  Per
+ * block of 32 along K: scale 2^(floor(log2(amax)) - 8) clamped to the E8M0
+ * range (all-zero block: byte 0); element = nearest E4M3 of x / scale, ties
+ * to the even code, saturating at +-448, never NaN; a value rounding to zero
+ * keeps its sign.  The MX block size 32 is the pages' (ai.appwright.xyz
+ * "投機的デコード", section "第1層：FP4量子化（モデル側）"); the element and scale
+ * rules are the OCP MX v1.0 ones.  K must be a positive multiple of 32.
+ * Errors: INVALID_ARG, ALIGNMENT, HIP.
+ */
+moe_status moe_mxfp4_quantize_act_mxfp8(const void* x, int64_t rows, int64_t K,
+                                        uint8_t* codes, uint8_t* scales,
+                                        void* hip_stream);
 
 /* Bytes of the TILED scale array of a rows x K matrix (0 if rows % 16 or
  * K % 128 is nonzero or a size is not positive). */

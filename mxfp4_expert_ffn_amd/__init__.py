@@ -28,9 +28,10 @@ OUT_BF16, OUT_F32 = 0, 1
 EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create",
            "moe_mxfp4_destroy", "moe_mxfp4_workspace_bytes", "moe_mxfp4_forward",
            "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights", "moe_mxfp4_stage_timing",
-           "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights")
-NUM_STAGES = 5
-STAGES = ("route", "sort", "gateup", "down", "combine")
+           "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights",
+           "moe_mxfp4_quantize_act_mxfp8")
+NUM_STAGES = 6
+STAGES = ("route", "sort", "quant", "gateup", "down", "combine")
 
 
 class MoeError(RuntimeError):
@@ -85,6 +86,8 @@ def lib():
         L.moe_mxfp4_debug_dequant.restype = ctypes.c_int
         L.moe_mxfp4_quantize_weights.argtypes = [P, i64, i64, P, P, P]
         L.moe_mxfp4_quantize_weights.restype = ctypes.c_int
+        L.moe_mxfp4_quantize_act_mxfp8.argtypes = [P, i64, i64, P, P, P]
+        L.moe_mxfp4_quantize_act_mxfp8.restype = ctypes.c_int
         L.moe_mxfp4_tiled_scale_bytes.argtypes = [i64, i64]
         L.moe_mxfp4_tiled_scale_bytes.restype = sz
         L.moe_mxfp4_tile_weights.argtypes = [P, P, i64, i64, P, P, P]
@@ -248,3 +251,16 @@ def tile_expert_weights(rowmajor: dict, stream=None) -> dict:
         tp, ts = tile_weights(p.reshape(E * N, half), sc.reshape(E * N, sc.shape[2]), stream)
         out[name], out[name + "_scale"] = tp, ts
     return out
+
+
+def quantize_act_mxfp8(x, codes=None, scales=None, stream=None):
+    """bf16 CUDA [rows, K] -> (E4M3 codes uint8 [rows, K], E8M0 scales uint8 [rows, K/32])."""
+    import torch
+    rows, K = x.shape
+    if codes is None:
+        codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_mxfp4_quantize_act_mxfp8(_ptr(x), rows, K, _ptr(codes), _ptr(scales),
+                                              _stream(stream)), "moe_mxfp4_quantize_act_mxfp8")
+    return codes, scales

@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t ids, w, offsets, sorted, inverse, active, chunks, nchunks, h, o, total;
+    size_t ids, w, offsets, sorted, inverse, active, chunks, nchunks, xq, xs, h, hs, o, total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
@@ -48,7 +48,11 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     moe::Dims dm{(int32_t)T, c.d_model, c.d_ff, c.num_experts, c.top_k, (int32_t)P};
     L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * 2 * sizeof(int32_t));
     L.nchunks = at; at += 256;
-    L.h = at;       at += round256(P * (size_t)c.d_ff * sizeof(uint16_t));
+    const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
+    L.xq = at;      at += mx8 ? round256((size_t)T * c.d_model) : 0;
+    L.xs = at;      at += mx8 ? round256((size_t)T * (c.d_model / MOE_MXFP4_BLOCK)) : 0;
+    L.h = at;       at += round256(P * (size_t)c.d_ff * (mx8 ? 1 : sizeof(uint16_t)));
+    L.hs = at;      at += mx8 ? round256(P * (size_t)(c.d_ff / MOE_MXFP4_BLOCK)) : 0;
     L.o = at;       at += round256(P * (size_t)c.d_model * sizeof(float));
     L.total = at;
     return L;
@@ -69,7 +73,9 @@ moe_status check_config(const moe_mxfp4_config* c) {
         if (K != 256 && K % 512 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->max_tokens * c->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->d_model * c->d_ff > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
-    if (c->act_mode == MOE_ACT_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED_SHAPE;   // not built yet
+    // MXFP8 mode keeps a chunk's activation scales (K/32 bytes per row) in LDS
+    if (c->act_mode == MOE_ACT_MXFP8_E4M3 && (c->d_model > 8192 || c->d_ff > 8192))
+        return MOE_ERR_UNSUPPORTED_SHAPE;
     return MOE_OK;
 }
 
@@ -198,7 +204,10 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     ws.active = reinterpret_cast<int32_t*>(base + L.active);
     ws.chunks = reinterpret_cast<int32_t*>(base + L.chunks);
     ws.nchunks = reinterpret_cast<int32_t*>(base + L.nchunks);
-    ws.h = reinterpret_cast<uint16_t*>(base + L.h);
+    ws.xq = reinterpret_cast<uint8_t*>(base + L.xq);
+    ws.xs = reinterpret_cast<uint8_t*>(base + L.xs);
+    ws.h = reinterpret_cast<uint8_t*>(base + L.h);
+    ws.hs = reinterpret_cast<uint8_t*>(base + L.hs);
     ws.o = reinterpret_cast<float*>(base + L.o);
 
     moe::Dims dm{num_tokens, c.d_model, c.d_ff, c.num_experts, c.top_k, num_tokens * c.top_k};
@@ -210,12 +219,15 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
         ev = &ctx->events[(size_t)(ctx->ncalls++ % ctx->capacity) * (MOE_MXFP4_NUM_STAGES + 1)];
     auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
 
+    const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
     if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess) return MOE_ERR_HIP;
     if (moe::launch_sort(dm, ws, s) != hipSuccess || mark(2) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_gateup(x, ctx->w, dm, ws, s) != hipSuccess || mark(3) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_down(ctx->w, dm, ws, s) != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess || mark(5) != hipSuccess)
+    if (mx8 && moe::launch_quant_x8(x, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
+    if (mark(3) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_gateup(x, ctx->w, dm, ws, mx8, s) != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_down(ctx->w, dm, ws, mx8, s) != hipSuccess || mark(5) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess || mark(6) != hipSuccess)
         return MOE_ERR_HIP;
 
     if (debug_out) {
@@ -259,6 +271,17 @@ moe_status moe_mxfp4_quantize_weights(const float* w, int64_t rows, int64_t K, u
     if (!aligned16(w) || !aligned16(packed) || !aligned16(scales)) return MOE_ERR_ALIGNMENT;
     if (rows == 0) return MOE_OK;
     if (moe::launch_quantize(w, rows, K, packed, scales, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_mxfp4_quantize_act_mxfp8(const void* x, int64_t rows, int64_t K, uint8_t* codes,
+                                        uint8_t* scales, void* hip_stream) {
+    if (!x || !codes || !scales || rows < 0 || K <= 0 || K % MOE_MXFP4_BLOCK != 0) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_ALIGNMENT;
+    if (rows == 0) return MOE_OK;
+    if (moe::launch_quant_act8(static_cast<const uint16_t*>(x), rows, K, codes, scales,
+                               static_cast<hipStream_t>(hip_stream)) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -44,6 +44,42 @@ __device__ __forceinline__ bf16x8_t decode8_bf16(uint32_t packed, float scale) {
     return r;
 }
 
+// Shared scale exponent of an MX block (OCP MX v1.0 scalar-to-MX rule):
+// floor(log2(amax)) - emax_elem, clamped to the E8M0 range [-127, 127]; an
+// all-zero block gets -127.  floor(log2) comes from the exponent field; a
+// subnormal amax is mantissa * 2^-149, so it is 31 - clz(mantissa) - 149.
+__device__ __forceinline__ int mx_scale_exp(float amax, int emax_elem) {
+    if (amax == 0.f) return -127;
+    const uint32_t bits = __float_as_uint(amax);
+    const int ef = (int)(bits >> 23);
+    const int fl = ef > 0 ? ef - 127 : -118 - (int)__clz(bits & 0x7FFFFFu);
+    const int se = fl - emax_elem;
+    return se < -127 ? -127 : (se > 127 ? 127 : se);
+}
+
+// E4M3 code (OCP: bias 7, 3 mantissa bits, largest finite 448, no infinity)
+// of an already-scaled finite value: nearest, ties to the even code,
+// saturating at +-448 (never the NaN code); the sign of a zero result kept.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+    const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+    const float a = fabsf(q);
+    uint32_t mag;
+    if (a < 0.015625f) {                       // below 2^-6: subnormal steps of 2^-9
+        mag = (uint32_t)rintf(a * 512.0f);     // exact product; rint is nearest-even; 8 = 2^-6
+    } else {
+        uint32_t u = __float_as_uint(a);
+        u += 0x7FFFFu + ((u >> 20) & 1u);      // nearest-even at 3 mantissa bits
+        int e = (int)(u >> 23) - 127;          // -6 .. 9
+        uint32_t m = (u >> 20) & 7u;
+        if (e > 8 || (e == 8 && m == 7u)) {    // past 448: saturate
+            e = 8;
+            m = 6u;
+        }
+        mag = ((uint32_t)(e + 7) << 3) | m;
+    }
+    return sign | mag;
+}
+
 // float -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -65,7 +101,10 @@ struct Workspace {
     int32_t* active;          // [E+1] active experts (count > 0) by descending count; [E] = how many
     int32_t* chunks;          // [max_chunks][2] (expert, first pair within the expert)
     int32_t* nchunks;         // [1] number of chunks
-    uint16_t* h;              // [P][f] bf16, rows in sorted order
+    uint8_t* xq;              // MXFP8 mode: [T][d] E4M3 codes of x
+    uint8_t* xs;              // MXFP8 mode: [T][d/32] E8M0 scales of x
+    uint8_t* h;               // [P][f] bf16 (or E4M3 codes in MXFP8 mode), rows in sorted order
+    uint8_t* hs;              // MXFP8 mode: [P][f/32] E8M0 scales of h
     float* o;                 // [P][d] weighted expert outputs, rows in sorted order
 };
 
@@ -84,9 +123,12 @@ inline int max_chunks(const Dims& dm) {
 // Kernel launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, hipStream_t s);
+hipError_t launch_quant_x8(const uint16_t* x, const Dims& dm, const Workspace& ws, hipStream_t s);
+hipError_t launch_quant_act8(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s);
 hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm,
-                         const Workspace& ws, hipStream_t s);
-hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
+                         const Workspace& ws, bool mx8, hipStream_t s);
+hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, bool mx8,
                        hipStream_t s);
 hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype,
                            hipStream_t s);

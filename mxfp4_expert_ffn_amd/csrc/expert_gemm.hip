@@ -1,5 +1,5 @@
-// Expert projections: packed MXFP4 weights streamed from HBM, decoded in
-// registers and multiplied on the matrix cores.
+// Expert projections: packed MXFP4 weights streamed from HBM and multiplied
+// on the matrix cores.
 //
 // The pages' point is that decoding a huge MoE is bound by the bytes of
 // expert weights it must stream, which FP4 on the experts cuts
@@ -7,8 +7,8 @@
 // techllm.github.io "Xiaomi MiMo x TileRT", section "1. MXFP4 — MoE에만 걸린
 // 양자화"), and that the next tile should stream in while the current one
 // computes (dothoosh.com article, section "TileRT: عصر فشار بر GPU").  So
-// every kernel here is one pipelined HBM pass over the weights of the
-// experts a verify batch touches:
+// every kernel here is one pipelined pass over the weights of the experts a
+// batch touches:
 //
 //   work unit = (chunk of <= 64 token pairs of one expert, tile of output
 //   columns).  The permutation kernel lists the chunks; chunks of a hot
@@ -21,22 +21,30 @@
 //   The weights are stored tiled (see the header), so that is one
 //   contiguous 1 KB buffer load per tile and step, plus one contiguous
 //   256-byte load of the dword of scales that covers the lane's 4 steps.
-//   Weights run D steps ahead in a register ring; activations run D - 1 steps ahead in an LDS ring filled by direct-to-LDS loads (no
-//   register staging), in a layout whose 16-byte chunks are XOR-swizzled by
-//   row so that the MFMA operand reads are free of bank conflicts.
+//   Weights run D steps ahead in a register ring; activations run D - 1
+//   steps ahead in an LDS ring filled by direct-to-LDS loads (no register
+//   staging), in a layout whose 16-byte chunks are XOR-swizzled by row so
+//   that the matrix-core operand reads are free of bank conflicts.
 //
-//   The 32 nibbles of a block feed four v_mfma_f32_16x16x32_bf16 steps: the
-//   hardware scaled convert turns 8 nibbles and the block's E8M0 scale into
-//   the 8 bf16 of the B operand (exact).  The reduction index only has to
-//   agree between A and B, so the A operand (activations) is read in the
-//   same block order.
+//   bf16 activations: the 32 nibbles of a block feed four
+//   v_mfma_f32_16x16x32_bf16 steps; the hardware scaled convert turns 8
+//   nibbles and the block's E8M0 scale into the 8 bf16 of the B operand
+//   (exact).  The reduction index only has to agree between A and B, so the
+//   A operand is read in the same block order.
+//
+//   MXFP8 activations: one v_mfma_scale_f32_16x16x128_f8f6f4 per step takes
+//   the tiled 1 KB of FP4 weights as its B operand unchanged (lane L: row
+//   L%16, MX block L/16, low nibble first) with the block scales as E8M0
+//   operands, and E4M3 activations as A (lane: row, bytes k 16g..16g+15 and
+//   64+16g..64+16g+15 of the step), with their block scales.
 //
 //   Gate/up: tiles 0..RT/2-1 come from W_gate and RT/2.. from W_up, so the
 //   gate and up accumulators of a (token, column) sit in the same lane and
-//   SwiGLU h = silu(g) * u runs in the epilogue; h is stored in bf16, rows in
-//   expert-sorted order.  Down: A = those h rows; the epilogue multiplies by
-//   the pair's routing weight and stores float32 per pair (combined later in
-//   a fixed order, so the result is deterministic).
+//   SwiGLU h = silu(g) * u runs in the epilogue; h is stored in bf16 (or
+//   re-quantised to MXFP8 along d_ff, a wave's 32 columns being exactly one
+//   block), rows in expert-sorted order.  Down: A = those h rows; the
+//   epilogue multiplies by the pair's routing weight and stores float32 per
+//   pair (combined later in a fixed order, so the result is deterministic).
 //
 // Memory ordering is explicit: the loads of a step are always issued in the
 // same order (activations, then weights) and pinned there, so a fixed vmcnt
@@ -50,29 +58,38 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxMs = kChunk / 16;            // token sub-tiles of 16 per chunk
-constexpr int kSlotBytes = kMaxMs * 16 * 256;  // one LDS ring slot: 64 rows x 128 bf16
 constexpr int kRsrcWord3 = 0x00020000;         // gfx9 raw buffer descriptor, dword 3
 
 enum { kGateUp = 0, kDown = 1 };
+enum { kBf16 = 0, kMx8 = 1 };
+
+// Bytes of one activation row per K step, and of one LDS ring slot.
+constexpr int row_bytes(int act) { return act == kBf16 ? kKStep * 2 : kKStep; }
+constexpr int slot_bytes(int act) { return kMaxMs * 16 * row_bytes(act); }
+// Row stride (bytes) of the per-chunk activation-scale table in LDS: one
+// byte per MX block, padded to an odd number of dwords against bank conflicts.
+constexpr int xs_stride(int K) { return K / kBlock + 4; }
 
 struct GemmArgs {
-    const uint16_t* act;        // gate/up: x [T][K]; down: h [P][K] (sorted rows)
-    const uint8_t* w0;          // gate / down packed
+    const uint8_t* act;         // gate/up: x [T][K]; down: h [P][K] (sorted rows); bf16 or E4M3
+    const uint8_t* act_scale;   // MXFP8: [rows][K/32] E8M0 scales of `act`
+    const uint8_t* w0;          // gate / down tiled packed
     const uint8_t* s0;
-    const uint8_t* w1;          // up packed (gate/up only)
+    const uint8_t* w1;          // up tiled packed (gate/up only)
     const uint8_t* s1;
     const int32_t* offsets;     // [E+1]
     const int32_t* sorted;      // [P]
     const int32_t* chunks;      // [n][2]: (expert, first pair of the chunk within the expert)
     const int32_t* nchunks;     // device count of chunks
     const float* topk_w;        // [P]
-    uint16_t* h_out;            // [P][f]
-    float* o_out;               // [P][d]
+    uint8_t* h_out;             // gate/up: h [P][f] (bf16 or E4M3 codes)
+    uint8_t* h_scale_out;       // gate/up MXFP8: [P][f/32]
+    float* o_out;               // down: [P][d]
     int32_t K;                  // reduction length
     int32_t N;                  // rows per weight matrix
     int32_t n_tiles;            // column tiles per expert
     int32_t k_top;
-    int32_t ldo;                // output row length
+    int32_t ldo;                // output row length (elements)
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -91,12 +108,19 @@ __device__ __forceinline__ void step_barrier() {
 __device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 
-template <int MODE, int RT, int MS, int D>
+template <int MODE, int ACT, int RT, int MS, int D>
 struct Pipe {
     static constexpr int kHalf = MODE == kGateUp ? RT / 2 : RT;
     static constexpr int kColsPerWave = kHalf * 16;
-    static constexpr int kNx = MS;         // direct-to-LDS loads per wave per step
+    static constexpr int kRow = row_bytes(ACT);           // activation bytes per row and step
+    static constexpr int kSlot = slot_bytes(ACT);
+    static constexpr int kChunksPerRow = kRow / 16;       // 16 (bf16) or 8 (E4M3)
+    static constexpr int kRowsPerKb = 1024 / kRow;        // rows one direct-to-LDS load fills
+    // direct-to-LDS loads per wave per step: MS*16 rows over 4 waves
+    static constexpr int kNx = MS * 16 / (kRowsPerKb * kWaves);
+    static_assert(kNx * kRowsPerKb * kWaves == MS * 16, "MXFP8 chunks use an even number of sub-tiles");
 
     // weight loads of step j: one 16-byte block and one scale dword per tile
     // (the dword holds the scales of 4 steps; each step reads its own copy so
@@ -116,14 +140,20 @@ struct Pipe {
         return cnt;
     }
 
+    // Physical 16-byte chunk of logical chunk c in LDS row r.
+    __device__ static int swz(int r, int c) {
+        return ACT == kBf16 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+    }
+
     struct Ctx {
         __amdgpu_buffer_rsrc_t rw[2], rs[2];
         int32_t lane16, lane4;            // lane offsets within a 1 KB tile step / 256 B scale group
         int32_t tile0;                    // first 16-row tile of this wave (per matrix)
         int32_t ns, ng;                   // K steps, scale groups
         const uint8_t* xbase;             // activation rows (bytes)
-        uint32_t xoff[MS];                // this lane's direct-to-LDS source offsets
-        uint8_t* lds;
+        uint32_t xoff[kNx > 0 ? kNx : 1]; // this lane's direct-to-LDS source offsets
+        uint8_t* lds;                     // activation ring
+        const uint8_t* xs;                // MXFP8: per-chunk activation scale table in LDS
         int wave;
     };
 
@@ -140,31 +170,52 @@ struct Pipe {
 
     __device__ static void issue_x(const Ctx& c, int slot, int step) {
 #pragma unroll
-        for (int q = 0; q < MS; ++q)
+        for (int q = 0; q < kNx; ++q)
             __builtin_amdgcn_global_load_lds(
-                c.xbase + c.xoff[q] + step * (kKStep * 2),
-                (lds_void*)(c.lds + slot * kSlotBytes + (q * kWaves + c.wave) * 1024), 16, 0, 0);
+                c.xbase + c.xoff[q] + step * kRow,
+                (lds_void*)(c.lds + slot * kSlot + (q * kWaves + c.wave) * 1024), 16, 0, 0);
     }
 
     template <int S4>
     __device__ static void compute(f32x4_t (&acc)[MS][RT], const u32x4_t (&w)[RT], const uint32_t (&sg)[RT],
-                                   const uint8_t* xs, int li, int g) {
-        float sc[RT];
+                                   const uint8_t* xs, int li, int g, int step, const Ctx& c) {
+        if constexpr (ACT == kBf16) {
+            float sc[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) sc[rt] = e8m0_as_scale((sg[rt] >> (8 * S4)) & 0xFFu);
+            for (int rt = 0; rt < RT; ++rt) sc[rt] = e8m0_as_scale((sg[rt] >> (8 * S4)) & 0xFFu);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf16x8_t b[RT];
+            for (int i = 0; i < 4; ++i) {
+                bf16x8_t b[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) b[rt] = decode8_bf16(w[rt][i], sc[rt]);
-            const int chunk = (4 * g + i) ^ li;
+                for (int rt = 0; rt < RT; ++rt) b[rt] = decode8_bf16(w[rt][i], sc[rt]);
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const int r = ms * 16 + li;
+                    const bf16x8_t a =
+                        *reinterpret_cast<const bf16x8_t*>(xs + r * kRow + swz(r, 4 * g + i) * 16);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        acc[ms][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[rt], acc[ms][rt], 0, 0, 0);
+                }
+            }
+        } else {
+            uint32_t sb[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sb[rt] = (sg[rt] >> (8 * S4)) & 0xFFu;
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) {
-                const bf16x8_t a =
-                    *reinterpret_cast<const bf16x8_t*>(xs + (ms * 16 + li) * 256 + chunk * 16);
+                const int r = ms * 16 + li;
+                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(xs + r * kRow + swz(r, g) * 16);
+                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(xs + r * kRow + swz(r, 4 + g) * 16);
+                const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const int sa = c.xs[r * xs_stride(c.ns * kKStep) + 4 * step + g];
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    acc[ms][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[rt], acc[ms][rt], 0, 0, 0);
+                for (int rt = 0; rt < RT; ++rt) {
+                    // FP4 B operand: only the low 4 registers are read
+                    const i32x8_t b = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(w[rt], w[rt], 0, 1, 2, 3, 0, 1, 2, 3));
+                    acc[ms][rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, b, acc[ms][rt], 0 /* A: E4M3 */, 4 /* B: E2M1 */, 0, sa, 0, (int)sb[rt]);
+                }
             }
         }
     }
@@ -182,13 +233,14 @@ struct Pipe {
         pin();
         if (R < 0 || R >= D - 1) issue_x(c, (SLOT + D - 1) % D, s + D - 1);
         pin();
-        compute<S4>(acc, w, sg, c.lds + SLOT * kSlotBytes, li, g);
+        compute<S4>(acc, w, sg, c.lds + SLOT * kSlot, li, g, s, c);
         pin();
         if (R < 0) issue_w(c, w, sg, s + D);
         pin();
     }
 
-    __device__ static void run(const GemmArgs& a, uint8_t* lds, int e, int nt, int m0, int c0, int M) {
+    __device__ static void run(const GemmArgs& a, uint8_t* lds, uint8_t* lds_xs, int e, int nt, int m0,
+                               int c0, int M) {
         const int tid = threadIdx.x, lane = tid % kWave;
         const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
         const int li = lane % 16, g = lane / 16;
@@ -212,20 +264,34 @@ struct Pipe {
         c.lane16 = lane * 16;
         c.lane4 = lane * 4;
         c.tile0 = col0 / 16;
-        c.xbase = reinterpret_cast<const uint8_t*>(a.act);
+        c.xbase = a.act;
         c.lds = lds;
+        c.xs = lds_xs;
         c.wave = wave;
-        // Direct-to-LDS load q of this wave fills LDS rows 4 * (q * 4 + wave) +
-        // lane / 16 at physical chunk lane % 16, which holds logical chunk
-        // (lane % 16) ^ (row % 16).  Rows past the chunk's last pair repeat
-        // it: their results are computed and never stored.
-#pragma unroll
-        for (int q = 0; q < MS; ++q) {
-            const int r = 4 * (q * kWaves + wave) + lane / 16;
+        // Source row of chunk row r: rows past the chunk's last pair repeat
+        // it; their results are computed and never stored.
+        auto src_row = [&](int r) {
             const int idx = min(c0 + r, M - 1);
-            const int row = MODE == kGateUp ? a.sorted[m0 + idx] / a.k_top : m0 + idx;
-            const int lchunk = (lane % 16) ^ (r % 16);
-            c.xoff[q] = (uint32_t)row * (uint32_t)(a.K * 2) + (uint32_t)(lchunk * 16);
+            return MODE == kGateUp ? a.sorted[m0 + idx] / a.k_top : m0 + idx;
+        };
+        // Direct-to-LDS load q of this wave fills the 1 KB at slot offset
+        // (q * 4 + wave) KB: rows kRowsPerKb * (q * 4 + wave) + lane /
+        // kChunksPerRow, physical chunk lane % kChunksPerRow, which holds the
+        // logical chunk that swz() maps there (swz is an involution).
+#pragma unroll
+        for (int q = 0; q < kNx; ++q) {
+            const int r = kRowsPerKb * (q * kWaves + wave) + lane / kChunksPerRow;
+            const int lchunk = swz(r, lane % kChunksPerRow);
+            c.xoff[q] = (uint32_t)src_row(r) * (uint32_t)(a.K * (ACT == kBf16 ? 2 : 1)) + (uint32_t)(lchunk * 16);
+        }
+        if constexpr (ACT == kMx8) {
+            // the chunk's activation scales, all of K, into LDS (row stride padded)
+            const int nb = a.K / kBlock;
+            for (int i = tid; i < MS * 16 * nb; i += kThreads) {
+                const int r = i / nb, b = i % nb;
+                lds_xs[r * xs_stride(a.K) + b] = a.act_scale[(size_t)src_row(r) * nb + b];
+            }
+            __syncthreads();
         }
 
         f32x4_t acc[MS][RT];
@@ -266,28 +332,48 @@ struct Pipe {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int idx = c0 + ms * 16 + 4 * g + r;
-                if (idx >= M) continue;
                 const size_t orow = (size_t)(m0 + idx);
-                if (MODE == kGateUp) {
+                if constexpr (MODE == kGateUp && ACT == kBf16) {
+                    if (idx < M) {
+                        uint16_t* h = reinterpret_cast<uint16_t*>(a.h_out);
 #pragma unroll
-                    for (int rt = 0; rt < RT / 2; ++rt) {
-                        const float hv = silu(acc[ms][rt][r]) * acc[ms][rt + RT / 2][r];
-                        a.h_out[orow * a.ldo + col0 + rt * 16 + li] = f32_to_bf16_rne(hv);
+                        for (int rt = 0; rt < RT / 2; ++rt) {
+                            const float hv = silu(acc[ms][rt][r]) * acc[ms][rt + RT / 2][r];
+                            h[orow * a.ldo + col0 + rt * 16 + li] = f32_to_bf16_rne(hv);
+                        }
+                    }
+                } else if constexpr (MODE == kGateUp) {
+                    // the wave's 32 columns of this token row are one MX block
+                    static_assert(RT == 4, "one MXFP8 block per wave row");
+                    const float h0 = silu(acc[ms][0][r]) * acc[ms][2][r];
+                    const float h1 = silu(acc[ms][1][r]) * acc[ms][3][r];
+                    float amax = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+                    const int se = mx_scale_exp(amax, 8);
+                    if (idx < M) {
+                        a.h_out[orow * a.ldo + col0 + li] = (uint8_t)e4m3_code(ldexpf(h0, -se));
+                        a.h_out[orow * a.ldo + col0 + 16 + li] = (uint8_t)e4m3_code(ldexpf(h1, -se));
+                        if (li == 0) a.h_scale_out[orow * (a.ldo / kBlock) + col0 / kBlock] = (uint8_t)(se + 127);
                     }
                 } else {
-                    const float wgt = a.topk_w[a.sorted[m0 + idx]];
+                    if (idx < M) {
+                        const float wgt = a.topk_w[a.sorted[m0 + idx]];
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        a.o_out[orow * a.ldo + col0 + rt * 16 + li] = wgt * acc[ms][rt][r];
+                        for (int rt = 0; rt < RT; ++rt)
+                            a.o_out[orow * a.ldo + col0 + rt * 16 + li] = wgt * acc[ms][rt][r];
+                    }
                 }
             }
         }
     }
 };
 
-template <int MODE, int RT, int D>
+template <int MODE, int ACT, int RT, int D>
 __global__ __launch_bounds__(kThreads, 2) void k_expert(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[D * kSlotBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[D * slot_bytes(ACT)];
+    // MXFP8: the chunk's activation scales (64 rows x (K/32 + 4) bytes, K <= 8192)
+    __shared__ __attribute__((aligned(16))) uint8_t lds_xs[ACT == kMx8 ? kMaxMs * 16 * xs_stride(8192) : 16];
     const int unit = blockIdx.x;
     const int chunk = unit / a.n_tiles;
     const int nt = unit % a.n_tiles;
@@ -298,26 +384,34 @@ __global__ __launch_bounds__(kThreads, 2) void k_expert(GemmArgs a) {
     const int c0 = __builtin_amdgcn_readfirstlane(a.chunks[2 * chunk + 1]);
     const int m0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
     const int M = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - m0;
-    const int nsub = min(kMaxMs, (M - c0 + 15) / 16);
-    switch (nsub) {
-        case 1: Pipe<MODE, RT, 1, D>::run(a, lds, e, nt, m0, c0, M); break;
-        case 2: Pipe<MODE, RT, 2, D>::run(a, lds, e, nt, m0, c0, M); break;
-        case 3: Pipe<MODE, RT, 3, D>::run(a, lds, e, nt, m0, c0, M); break;
-        default: Pipe<MODE, RT, 4, D>::run(a, lds, e, nt, m0, c0, M); break;
+    int nsub = min(kMaxMs, (M - c0 + 15) / 16);
+    if constexpr (ACT == kMx8) {
+        nsub = nsub <= 2 ? 2 : 4;                     // E4M3 rows fill 1 KB loads in pairs of sub-tiles
+        switch (nsub) {
+            case 2: Pipe<MODE, ACT, RT, 2, D>::run(a, lds, lds_xs, e, nt, m0, c0, M); break;
+            default: Pipe<MODE, ACT, RT, 4, D>::run(a, lds, lds_xs, e, nt, m0, c0, M); break;
+        }
+    } else {
+        switch (nsub) {
+            case 1: Pipe<MODE, ACT, RT, 1, D>::run(a, lds, lds_xs, e, nt, m0, c0, M); break;
+            case 2: Pipe<MODE, ACT, RT, 2, D>::run(a, lds, lds_xs, e, nt, m0, c0, M); break;
+            case 3: Pipe<MODE, ACT, RT, 3, D>::run(a, lds, lds_xs, e, nt, m0, c0, M); break;
+            default: Pipe<MODE, ACT, RT, 4, D>::run(a, lds, lds_xs, e, nt, m0, c0, M); break;
+        }
     }
 }
 
 constexpr int kRtGateUp = 4;     // 2 gate + 2 up tiles per wave: 128 h columns per workgroup
 constexpr int kRtDown = 4;       // 4 tiles per wave: 256 output columns per workgroup
 
-template <int MODE, int RT>
+template <int MODE, int ACT, int RT>
 hipError_t launch(const GemmArgs& a, int max_units, hipStream_t s) {
     const int nsteps = a.K / kKStep;          // 2 (K = 256) or a multiple of 4
     const dim3 grid(max_units), block(kThreads);
     if (nsteps % 4 == 0)
-        hipLaunchKernelGGL((k_expert<MODE, RT, 4>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_expert<MODE, ACT, RT, 4>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((k_expert<MODE, RT, 2>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((k_expert<MODE, ACT, RT, 2>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -327,30 +421,35 @@ int gateup_cols_per_block() { return kWaves * (kRtGateUp / 2) * 16; }
 int down_cols_per_block() { return kWaves * kRtDown * 16; }
 
 hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm,
-                         const Workspace& ws, hipStream_t s) {
+                         const Workspace& ws, bool mx8, hipStream_t s) {
     GemmArgs a{};
-    a.act = x;
+    a.act = mx8 ? ws.xq : reinterpret_cast<const uint8_t*>(x);
+    a.act_scale = mx8 ? ws.xs : nullptr;
     a.w0 = w.w_gate; a.s0 = w.w_gate_scale;
     a.w1 = w.w_up;   a.s1 = w.w_up_scale;
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.topk_w = ws.topk_w;
-    a.h_out = ws.h; a.o_out = nullptr;
+    a.h_out = ws.h; a.h_scale_out = ws.hs; a.o_out = nullptr;
     a.K = dm.d; a.N = dm.f; a.n_tiles = dm.f / gateup_cols_per_block();
     a.k_top = dm.k; a.ldo = dm.f;
-    return launch<kGateUp, kRtGateUp>(a, max_chunks(dm) * a.n_tiles, s);
+    const int units = max_chunks(dm) * a.n_tiles;
+    return mx8 ? launch<kGateUp, kMx8, kRtGateUp>(a, units, s) : launch<kGateUp, kBf16, kRtGateUp>(a, units, s);
 }
 
-hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, hipStream_t s) {
+hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, bool mx8,
+                       hipStream_t s) {
     GemmArgs a{};
     a.act = ws.h;
+    a.act_scale = mx8 ? ws.hs : nullptr;
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.topk_w = ws.topk_w;
-    a.h_out = nullptr; a.o_out = ws.o;
+    a.h_out = nullptr; a.h_scale_out = nullptr; a.o_out = ws.o;
     a.K = dm.f; a.N = dm.d; a.n_tiles = dm.d / down_cols_per_block();
     a.k_top = dm.k; a.ldo = dm.d;
-    return launch<kDown, kRtDown>(a, max_chunks(dm) * a.n_tiles, s);
+    const int units = max_chunks(dm) * a.n_tiles;
+    return mx8 ? launch<kDown, kMx8, kRtDown>(a, units, s) : launch<kDown, kBf16, kRtDown>(a, units, s);
 }
 
 }  // namespace moe

@@ -60,6 +60,7 @@ def _create(**kw):
     (dict(d_model=-256), 1), (dict(flags=1), 1), (dict(act_mode=7), 1), (dict(out_dtype=3), 1),
     (dict(top_k=5), 2), (dict(num_experts=513, top_k=2), 2), (dict(num_experts=64, top_k=33), 2),
     (dict(d_model=288), 2), (dict(d_ff=384), 2),
+    (dict(act_mode=1), 0), (dict(act_mode=1, d_model=8704), 2),
 ])
 def test_create_validation(kw, status):
     ptrs = kw.pop("ptrs", None)
@@ -177,3 +178,12 @@ def test_create_rejects_k_without_a_pipeline():
     assert st == 2
     st, h = _create(d_model=1024, d_ff=256)
     assert st == 0 and moe.lib().moe_mxfp4_destroy(h) == 0
+
+
+def test_quantize_act_validation():
+    q = moe.lib().moe_mxfp4_quantize_act_mxfp8
+    assert q(FAKE, 4, 48, FAKE, FAKE, None) == 1
+    assert q(None, 4, 64, FAKE, FAKE, None) == 1
+    assert q(FAKE, -1, 64, FAKE, FAKE, None) == 1
+    assert q(FAKE + 2, 4, 64, FAKE, FAKE, None) == 4
+    assert q(FAKE, 0, 64, FAKE, FAKE, None) == 0

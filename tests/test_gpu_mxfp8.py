@@ -1,0 +1,101 @@
+"""GPU parity of the MXFP8-activation path (the 8192-token chunk's mode).
+
+The activation quantiser must match the oracle's MXFP8 quantiser bit for bit
+(every rounding decision is taken on a bf16 value scaled by a power of two).
+h is re-quantised on both sides from differently rounded float values, so a
+few of its E4M3 codes may differ by one step; the layer output is checked
+against the tolerance max|y - y_ref| <= 2e-2 * RMS(y_ref).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import problems
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _moe():
+    import mxfp4_expert_ffn_amd as moe
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return moe
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def test_quantize_act_mxfp8_bit_exact():
+    moe = _moe()
+    rng = np.random.default_rng(80)
+    x = rng.standard_normal((64, 512)).astype(np.float32)
+    x[0] = 0.0
+    x[1, :32] = -0.0
+    x[2] *= 1e-30                                            # tiny blocks
+    x[3] *= 1e30                                             # huge blocks
+    x[4, ::32] = 448.0                                       # ties and saturation near the top
+    x[4, 1::32] = 464.0
+    x[5] = np.resize(np.array([0.0137, -0.0146, 1.0625, 3.3e-3, 5e-4, -7e-4], np.float32), 512)
+    xb = synth.bf16_bits_from_f32(x)
+    codes, scales = moe.quantize_act_mxfp8(_bf16(xb))
+    torch.cuda.synchronize()
+    c2, s2 = oracle.quant_mxfp8(synth.bf16_bits_to_f32(xb).astype(np.float64))
+    assert np.array_equal(scales.cpu().numpy(), s2)
+    assert np.array_equal(codes.cpu().numpy(), c2)
+
+
+def _run(w, acts, dev, out_dtype, T=None):
+    moe = _moe()
+    T = w.T if T is None else T
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=T, act_mode=moe.ACT_MXFP8_E4M3,
+                         out_dtype=out_dtype)
+    P = T * w.k
+    r = {"topk_ids": torch.empty(P, dtype=torch.int32, device="cuda"),
+         "expert_offsets": torch.empty(w.E + 1, dtype=torch.int32, device="cuda"),
+         "sorted_pairs": torch.empty(P, dtype=torch.int32, device="cuda")}
+    y = layer(_bf16(acts["x_bf16"][:T]), torch.from_numpy(acts["logits"][:T]).cuda(), routing=r)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in r.items()}
+
+
+@pytest.mark.parametrize("T,E,k", [(40, 4, 2), (100, 2, 2), (13, 8, 3)])
+def test_mxfp8_small_forward(T, E, k):
+    moe = _moe()
+    w = synth.Workload("mx8", T, 256, 512, E, k, "mxfp8", "none", 90 + T)
+    acts = synth.make_activations(w)
+    wts = problems.pack_experts(w)
+    dev = problems.to_device(wts)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k, act_mode=oracle.ACT_MXFP8)
+    y32, r = _run(w, acts, dev, moe.OUT_F32)
+    ids, _ = oracle.route(acts["logits"], k)
+    assert np.array_equal(r["topk_ids"], ids.reshape(-1))
+    err = problems.rel_max_err(y32, ref["y"])
+    print(f"mxfp8 T={T} E={E} k={k}: f32-out rel max err {err:.3e}")
+    assert err <= TOL
+
+
+def test_chunk_8192_sampled_parity():
+    moe = _moe()
+    w = synth.workload("chunk_8192")
+    acts, wts = problems.problem(w)
+    dev = problems.to_device(wts)
+    y16, r = _run(w, acts, dev, moe.OUT_BF16)
+    ids, _ = oracle.route(acts["logits"], w.k)
+    assert np.array_equal(r["topk_ids"], ids.reshape(-1))
+    perm = oracle.permute(ids, w.E)
+    assert np.array_equal(r["expert_offsets"], perm["offsets"])
+    assert np.array_equal(r["sorted_pairs"], perm["sorted_pairs"])
+    rng = np.random.default_rng(8)
+    sample = np.sort(rng.choice(w.T, size=12, replace=False))
+    ref = oracle.moe_forward(acts["x_bf16"][sample], acts["logits"][sample], wts, w.k,
+                             act_mode=oracle.ACT_MXFP8, nthreads=problems.THREADS)["y"]
+    err = problems.rel_max_err(y16[sample], ref)
+    floor = problems.rel_max_err(torch.from_numpy(ref).bfloat16().double().numpy(), ref)
+    print(f"chunk_8192: bf16-out rel max err {err:.3e} over {len(sample)} tokens "
+          f"(bf16 rounding of the reference alone: {floor:.3e})")
+    assert err <= TOL
