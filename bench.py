@@ -24,6 +24,8 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense FP4/FP6 matrix peak
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (the rate of FP8 x FP4 scaled MFMA)
 WNAMES = ("w_gate", "w_gate_scale", "w_up", "w_up_scale", "w_down", "w_down_scale")
 
 
@@ -108,10 +110,7 @@ def main():
     import synth
 
     w = synth.workload(args.workload)
-    if w.act != "bf16":
-        print(f"workload {w.name} needs the MXFP8 activation path, which this build lacks",
-              file=sys.stderr)
-        sys.exit(2)
+    mx8 = w.act == "mxfp8"
     torch.cuda.set_device(0)
     log(f"workload {w}")
     acts = synth.make_activations(w)
@@ -122,7 +121,8 @@ def main():
     x = torch.from_numpy(acts["x_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
     lg = torch.from_numpy(acts["logits"]).cuda()
     out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
-    layers = [moe.MoeMxfp4(c, w.E, w.d, w.f, w.k, max_tokens=w.T) for c in wcopies]
+    act_mode = moe.ACT_MXFP8_E4M3 if mx8 else moe.ACT_BF16
+    layers = [moe.MoeMxfp4(c, w.E, w.d, w.f, w.k, max_tokens=w.T, act_mode=act_mode) for c in wcopies]
     ws = torch.empty(layers[0].workspace_bytes(w.T), dtype=torch.uint8, device="cuda")
 
     # routing of this batch, from the library itself, for the byte counts
@@ -165,7 +165,18 @@ def main():
     log(f"stage averages (us): " + ", ".join(f"{k} {v:.1f}" for k, v in stage_avg_us.items()))
 
     gateup_s = stage_avg_us["gateup"] * 1e-6
-    achieved = gateup_bytes / gateup_s / 1e9
+    gateup_flops = 2.0 * w.P * 2 * w.d * w.f
+    if mx8:
+        achieved = gateup_flops / gateup_s / 1e12
+        roofline = {"bound": "mfma", "kernel": "k_expert<gate/up, MXFP8 x MXFP4>", "achieved": achieved,
+                    "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MXFP4_PEAK_TFLOPS,
+                    "frac_of_fp8_rate": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                    "algorithmic_flops": gateup_flops}
+    else:
+        achieved = gateup_bytes / gateup_s / 1e9
+        roofline = {"bound": "hbm", "kernel": "k_expert<gate/up>", "achieved": achieved,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": None, "algorithmic_bytes": gateup_bytes}
     result = {
         "metric": "MoE expert-layer tokens/s + achieved HBM GB/s (% of peak), 256-token verify",
         "value": w.T / (ms_per_step * 1e-3),
@@ -177,11 +188,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8xmxfp4" if mx8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.T} tokens ({w.T // 8} sequences x DFlash block 8), "
                                f"d_model {w.d}, d_ff {w.f}, {w.E} experts, top-{w.k}, "
-                               f"bias {w.bias}, MXFP4 weights (E2M1 + E8M0 per 32), bf16 in/out",
+                               f"bias {w.bias}, MXFP4 weights (E2M1 + E8M0 per 32), "
+                               f"{'MXFP8 (E4M3 + E8M0 per 32)' if mx8 else 'bf16'} activations, bf16 out",
                    "T": w.T, "d_model": w.d, "d_ff": w.f, "experts": w.E, "top_k": w.k,
                    "touched_experts": touched, "weight_copies": args.copies},
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -189,9 +201,7 @@ def main():
         "layer_algorithmic_bytes": layer_bytes,
         "layer_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "stage_us": stage_avg_us,
-        "roofline": {"bound": "hbm", "kernel": "k_expert<gate/up>", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": gateup_bytes},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens")

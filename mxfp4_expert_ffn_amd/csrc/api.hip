@@ -46,7 +46,7 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     L.inverse = at; at += round256(P * sizeof(int32_t));
     L.active = at;  at += round256((size_t)(c.num_experts + 1) * sizeof(int32_t));
     moe::Dims dm{(int32_t)T, c.d_model, c.d_ff, c.num_experts, c.top_k, (int32_t)P};
-    L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * 2 * sizeof(int32_t));
+    L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * moe::kChunkRec * sizeof(int32_t));
     L.nchunks = at; at += 256;
     const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
     L.xq = at;      at += mx8 ? round256((size_t)T * c.d_model) : 0;

@@ -16,6 +16,8 @@ constexpr int kWave = 64;          // CDNA wavefront
 constexpr int kBlock = 32;         // MX block (elements per E8M0 scale)
 constexpr int kKStep = 128;        // K per main-loop step: 4 MX blocks, one per lane group
 constexpr int kChunk = 64;         // token pairs per expert work chunk
+constexpr int kChunkRec = 4;       // ints per chunk record
+constexpr int kXcds = 8;           // MI355X accelerator complex dies (one L2 each)
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -99,7 +101,8 @@ struct Workspace {
     int32_t* sorted_pairs;    // [P]
     int32_t* inverse;         // [P]   position of pair p in sorted_pairs
     int32_t* active;          // [E+1] active experts (count > 0) by descending count; [E] = how many
-    int32_t* chunks;          // [max_chunks][2] (expert, first pair within the expert)
+    int32_t* chunks;          // [max_chunks][4] (expert, first pair within the expert,
+                              //   first chunk of the expert, number of chunks of the expert)
     int32_t* nchunks;         // [1] number of chunks
     uint8_t* xq;              // MXFP8 mode: [T][d] E4M3 codes of x
     uint8_t* xs;              // MXFP8 mode: [T][d/32] E8M0 scales of x

@@ -374,14 +374,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_expert(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[D * slot_bytes(ACT)];
     // MXFP8: the chunk's activation scales (64 rows x (K/32 + 4) bytes, K <= 8192)
     __shared__ __attribute__((aligned(16))) uint8_t lds_xs[ACT == kMx8 ? kMaxMs * 16 * xs_stride(8192) : 16];
+    // Work unit = (chunk, column tile), chunk-major: the column tiles of a
+    // chunk (same activation rows) are adjacent.  Chunks are listed expert
+    // by expert, hottest expert first.  Workgroup-uniform values are kept in
+    // scalar registers so that the buffer descriptors built from them are
+    // scalar too.
     const int unit = blockIdx.x;
     const int chunk = unit / a.n_tiles;
     const int nt = unit % a.n_tiles;
     if (chunk >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;     // uniform per workgroup
-    // workgroup-uniform values: keep them in scalar registers so that the
-    // buffer descriptors built from them are scalar too
-    const int e = __builtin_amdgcn_readfirstlane(a.chunks[2 * chunk]);
-    const int c0 = __builtin_amdgcn_readfirstlane(a.chunks[2 * chunk + 1]);
+    const int* rec = a.chunks + kChunkRec * chunk;
+    const int e = __builtin_amdgcn_readfirstlane(rec[0]);
+    const int c0 = __builtin_amdgcn_readfirstlane(rec[1]);
     const int m0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
     const int M = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - m0;
     int nsub = min(kMaxMs, (M - c0 + 15) / 16);

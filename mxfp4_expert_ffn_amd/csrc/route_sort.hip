@@ -21,6 +21,7 @@ constexpr int kRouteWaves = 4;          // tokens per routing workgroup
 constexpr int kMaxPerLane = 8;          // E <= 512
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kPrefetch = 8;            // rounds of pair ids loaded ahead per wave
 
 // One wavefront per token.  Lane l holds logits l, l+64, ...
 __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __restrict__ logits,
@@ -126,14 +127,24 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     const int p1 = min(P, p0 + per_wave);
     int32_t* my = hist + wave * E;
 
-    // 1) per-wave histograms, pairs visited in ascending order
-    for (int base = p0; base < p1; base += kWave) {
-        const int p = base + lane;
-        const bool valid = p < p1;
-        const int e = valid ? ids[p] : 0;
-        const uint64_t peers = match_peers(e, valid, nbits);
-        const int rank = __popcll(peers & lt_mask);
-        if (valid && rank == 0) my[e] += __popcll(peers);
+    // 1) per-wave histograms, pairs visited in ascending order; the ids of
+    //    kPrefetch rounds are loaded together so that their latencies overlap
+    for (int base = p0; base < p1; base += kPrefetch * kWave) {
+        int ev[kPrefetch];
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) {
+            const int p = base + q * kWave + lane;
+            ev[q] = p < p1 ? ids[p] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) {
+            if (base + q * kWave >= p1) break;            // uniform: past this wave's pairs
+            const int p = base + q * kWave + lane;
+            const bool valid = p < p1;
+            const uint64_t peers = match_peers(ev[q], valid, nbits);
+            const int rank = __popcll(peers & lt_mask);
+            if (valid && rank == 0) my[ev[q]] += __popcll(peers);
+        }
     }
     __syncthreads();
 
@@ -190,28 +201,42 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     int cbefore = 0;
     for (int w = 0; w < wave; ++w) cbefore += wsum[w];
     if (tid < na) {
+        // record: expert, first pair of the chunk, first chunk of the expert, chunks of the expert
         const int first = cbefore + nincl - nch;
         for (int q = 0; q < nch; ++q) {
-            chunks[2 * (first + q)] = act[tid];
-            chunks[2 * (first + q) + 1] = q * kChunk;
+            int32_t* rec = chunks + kChunkRec * (first + q);
+            rec[0] = act[tid];
+            rec[1] = q * kChunk;
+            rec[2] = first;
+            rec[3] = nch;
         }
     }
     if (tid == kSortThreads - 1) *nchunks = cbefore + nincl;
     __syncthreads();
 
     // 3) scatter in the same visiting order: stable within each expert
-    for (int base = p0; base < p1; base += kWave) {
-        const int p = base + lane;
-        const bool valid = p < p1;
-        const int e = valid ? ids[p] : 0;
-        const uint64_t peers = match_peers(e, valid, nbits);
-        const int rank = __popcll(peers & lt_mask);
-        const int pos = valid ? my[e] + rank : 0;
-        if (valid) {
-            sorted[pos] = p;
-            inverse[p] = pos;
+    for (int base = p0; base < p1; base += kPrefetch * kWave) {
+        int ev[kPrefetch];
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) {
+            const int p = base + q * kWave + lane;
+            ev[q] = p < p1 ? ids[p] : 0;
         }
-        if (valid && rank == 0) my[e] += __popcll(peers);
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) {
+            if (base + q * kWave >= p1) break;            // uniform: past this wave's pairs
+            const int p = base + q * kWave + lane;
+            const bool valid = p < p1;
+            const int e = ev[q];
+            const uint64_t peers = match_peers(e, valid, nbits);
+            const int rank = __popcll(peers & lt_mask);
+            const int pos = valid ? my[e] + rank : 0;
+            if (valid) {
+                sorted[pos] = p;
+                inverse[p] = pos;
+            }
+            if (valid && rank == 0) my[e] += __popcll(peers);
+        }
     }
 }
 
