@@ -25,8 +25,8 @@ struct moe_mxfp4_ctx {
 
 namespace {
 
-constexpr int kMaxExperts = 512;
-constexpr int kMaxTopK = 32;
+using moe::kMaxExperts;
+using moe::kMaxTopK;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -222,11 +222,15 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
     if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_sort(dm, ws, s) != hipSuccess || mark(2) != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_sort(dm, ws, mx8 ? moe::kDenseChunk : moe::kChunk, s) != hipSuccess || mark(2) != hipSuccess)
+        return MOE_ERR_HIP;
     if (mx8 && moe::launch_quant_x8(x, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
     if (mark(3) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_gateup(x, ctx->w, dm, ws, mx8, s) != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_down(ctx->w, dm, ws, mx8, s) != hipSuccess || mark(5) != hipSuccess) return MOE_ERR_HIP;
+    const hipError_t gu = mx8 ? moe::launch_gateup_dense(ctx->w, dm, ws, s)
+                              : moe::launch_gateup(x, ctx->w, dm, ws, false, s);
+    if (gu != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
+    const hipError_t dn = mx8 ? moe::launch_down_dense(ctx->w, dm, ws, s) : moe::launch_down(ctx->w, dm, ws, false, s);
+    if (dn != hipSuccess || mark(5) != hipSuccess) return MOE_ERR_HIP;
     if (moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess || mark(6) != hipSuccess)
         return MOE_ERR_HIP;
 

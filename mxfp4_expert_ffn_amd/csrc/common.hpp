@@ -15,9 +15,11 @@ namespace moe {
 constexpr int kWave = 64;          // CDNA wavefront
 constexpr int kBlock = 32;         // MX block (elements per E8M0 scale)
 constexpr int kKStep = 128;        // K per main-loop step: 4 MX blocks, one per lane group
-constexpr int kChunk = 64;         // token pairs per expert work chunk
+constexpr int kChunk = 64;         // token pairs per expert work chunk (bf16 activations)
+constexpr int kDenseChunk = 128;   // token pairs per expert work chunk (MXFP8 activations)
 constexpr int kChunkRec = 4;       // ints per chunk record
-constexpr int kXcds = 8;           // MI355X accelerator complex dies (one L2 each)
+constexpr int kMaxExperts = 512;  // E limit of the library
+constexpr int kMaxTopK = 32;      // k limit of the library
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -125,7 +127,7 @@ inline int max_chunks(const Dims& dm) {
 
 // Kernel launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s);
-hipError_t launch_sort(const Dims& dm, const Workspace& ws, hipStream_t s);
+hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s);
 hipError_t launch_quant_x8(const uint16_t* x, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_quant_act8(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);
@@ -133,6 +135,12 @@ hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Di
                          const Workspace& ws, bool mx8, hipStream_t s);
 hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, bool mx8,
                        hipStream_t s);
+// MXFP8 activations (dense regime): 128-pair x 256-weight-row tiles, both
+// operands staged in LDS, scaled MFMA.
+hipError_t launch_gateup_dense(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
+                               hipStream_t s);
+hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
+                             hipStream_t s);
 hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype,
                            hipStream_t s);
 hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t row0,

@@ -3,7 +3,9 @@
 // Routing: techllm.github.io "Xiaomi MiMo x TileRT", section "3. TileRT",
 // names the expert-routing step whose pattern the runtime knows ahead; the
 // pages give no rule, so: the k largest logits (ties to the lower expert
-// index), weights = softmax over the k selected logits.
+// index), weights = softmax over the k selected logits.  Up to 64 experts,
+// a wave ranks all of a token's logits at once (each lane counts the logits
+// that beat its own); beyond that, k rounds of a wave-wide argmax.
 //
 // Permutation: a stable counting sort of the pairs p = t*k + j by expert,
 // built from wavefront ballots (lanes holding the same expert find each
@@ -23,7 +25,77 @@ constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kPrefetch = 8;            // rounds of pair ids loaded ahead per wave
 
-// One wavefront per token.  Lane l holds logits l, l+64, ...
+// One wavefront per token, E <= 64 * NV.  Lane l holds logits l and l + 64.
+// The rank of logit e is the number of logits that come before it in the
+// order (value descending, expert index ascending); the experts of ranks
+// 0..k-1 are the selection, already in order.
+template <int NV>
+__global__ __launch_bounds__(kRouteWaves * kWave) void k_route_rank(const float* __restrict__ logits,
+                                                                    Dims dm, int32_t* __restrict__ ids,
+                                                                    float* __restrict__ wts) {
+    __shared__ float sv[kRouteWaves][NV * kWave];
+    __shared__ int32_t sid[kRouteWaves][kMaxTopK];
+    __shared__ float sval[kRouteWaves][kMaxTopK];
+    __shared__ float sex[kRouteWaves][kMaxTopK];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * kRouteWaves + wave;
+    if (t >= dm.T) return;                       // whole wave exits; waves share no LDS
+    const float* l = logits + (size_t)t * dm.E;
+    float v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        // padding sorts after every logit: it never beats one (-inf included)
+        v[i] = e < dm.E ? l[e] : -INFINITY;
+        sv[wave][e] = v[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int rank[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) rank[i] = 0;
+    const float4* row = reinterpret_cast<const float4*>(sv[wave]);
+#pragma unroll 4
+    for (int q = 0; q < NV * kWave / 4; ++q) {
+        const float4 u4 = row[q];
+        const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e2 = 4 * q + j;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                rank[i] += (u[j] > v[i]) || (u[j] == v[i] && e2 < lane + kWave * i);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        if (e < dm.E && rank[i] < dm.k) {
+            sid[wave][rank[i]] = e;
+            sval[wave][rank[i]] = v[i];
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float ex = 0.0f;
+    if (lane < dm.k) {
+        ex = expf(sval[wave][lane] - sval[wave][0]);
+        sex[wave][lane] = ex;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < dm.k) {
+        float sum = 0.0f;
+        for (int j = 0; j < dm.k; ++j) sum += sex[wave][j];
+        ids[(size_t)t * dm.k + lane] = sid[wave][lane];
+        wts[(size_t)t * dm.k + lane] = ex / sum;
+    }
+}
+
+// One wavefront per token, any E <= 512.  Lane l holds logits l, l+64, ...
 __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __restrict__ logits,
                                                                Dims dm, int32_t* __restrict__ ids,
                                                                float* __restrict__ wts) {
@@ -99,19 +171,21 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) 
     return m;
 }
 
-// Single workgroup.  LDS: hist[kSortWaves][E] + counts[E] + 16 ints.
+// Single workgroup.  LDS: hist[kSortWaves][E] + counts[E rounded up to 4]
+// + act[E] + 32 ints.
 __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ sorted,
                                                        int32_t* __restrict__ inverse,
                                                        int32_t* __restrict__ active,
                                                        int32_t* __restrict__ chunks,
-                                                       int32_t* __restrict__ nchunks) {
+                                                       int32_t* __restrict__ nchunks, int chunk_rows) {
     extern __shared__ int32_t sm[];
     const int E = dm.E, P = dm.P;
     int32_t* hist = sm;                               // [kSortWaves][E]
-    int32_t* counts = sm + kSortWaves * E;            // [E]
-    int32_t* act = counts + E;                        // [E] active experts in rank order
+    const int E4 = (E + 3) & ~3;
+    int32_t* counts = sm + kSortWaves * E;            // [E4], zero past E
+    int32_t* act = counts + E4;                       // [E] active experts in rank order
     int32_t* wsum = act + E;                          // [16]
     int32_t* wsum2 = wsum + kSortWaves;               // [16]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -126,6 +200,10 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     const int p0 = wave * per_wave;
     const int p1 = min(P, p0 + per_wave);
     int32_t* my = hist + wave * E;
+    // a wave whose pairs fit one prefetch round keeps their ids in registers
+    // for the scatter instead of loading them again
+    const bool one_round = per_wave <= kPrefetch * kWave;
+    int keep[kPrefetch];
 
     // 1) per-wave histograms, pairs visited in ascending order; the ids of
     //    kPrefetch rounds are loaded together so that their latencies overlap
@@ -135,6 +213,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
         for (int q = 0; q < kPrefetch; ++q) {
             const int p = base + q * kWave + lane;
             ev[q] = p < p1 ? ids[p] : 0;
+            keep[q] = ev[q];
         }
 #pragma unroll
         for (int q = 0; q < kPrefetch; ++q) {
@@ -158,6 +237,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
         }
         counts[e] = run;
     }
+    if (tid >= E && tid < E4) counts[tid] = 0;
     __syncthreads();
 
     // exclusive scan of counts over experts (E <= 512 <= 1024 threads)
@@ -174,9 +254,14 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
         // active experts by descending pair count, ties to the lower index
         if (c > 0) {
             int r = 0;
-            for (int e2 = 0; e2 < E; ++e2) {
-                const int c2 = counts[e2];
-                r += (c2 > c) || (c2 == c && e2 < tid);
+            const int4* c4 = reinterpret_cast<const int4*>(counts);
+            for (int q = 0; q < E4 / 4; ++q) {
+                const int4 cc = c4[q];
+                const int e2 = 4 * q;
+                r += (cc.x > c) || (cc.x == c && e2 < tid);
+                r += (cc.y > c) || (cc.y == c && e2 + 1 < tid);
+                r += (cc.z > c) || (cc.z == c && e2 + 2 < tid);
+                r += (cc.w > c) || (cc.w == c && e2 + 3 < tid);
             }
             active[r] = tid;
             act[r] = tid;
@@ -192,8 +277,8 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
         offsets[E] = P;
         active[E] = na;
     }
-    // work chunks of <= kChunk pairs, expert by expert in rank order
-    const int nch = tid < na ? (counts[act[tid]] + kChunk - 1) / kChunk : 0;
+    // work chunks of <= chunk_rows pairs, expert by expert in rank order
+    const int nch = tid < na ? (counts[act[tid]] + chunk_rows - 1) / chunk_rows : 0;
     const int nincl = wave_inclusive_scan(nch, lane);
     __syncthreads();                                   // wsum is reused below
     if (lane == kWave - 1) wsum[wave] = nincl;
@@ -206,7 +291,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
         for (int q = 0; q < nch; ++q) {
             int32_t* rec = chunks + kChunkRec * (first + q);
             rec[0] = act[tid];
-            rec[1] = q * kChunk;
+            rec[1] = q * chunk_rows;
             rec[2] = first;
             rec[3] = nch;
         }
@@ -220,7 +305,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
 #pragma unroll
         for (int q = 0; q < kPrefetch; ++q) {
             const int p = base + q * kWave + lane;
-            ev[q] = p < p1 ? ids[p] : 0;
+            ev[q] = one_round ? keep[q] : (p < p1 ? ids[p] : 0);
         }
 #pragma unroll
         for (int q = 0; q < kPrefetch; ++q) {
@@ -244,15 +329,21 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
 
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s) {
     const int grid = (dm.T + kRouteWaves - 1) / kRouteWaves;
-    hipLaunchKernelGGL(k_route, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
-                       ws.topk_ids, ws.topk_w);
+    // ranking costs E compares per logit: it wins for one logit per lane;
+    // with more, the k argmax rounds are cheaper
+    if (dm.E <= kWave)
+        hipLaunchKernelGGL(k_route_rank<1>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
+                           ws.topk_ids, ws.topk_w);
+    else
+        hipLaunchKernelGGL(k_route, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
+                           ws.topk_ids, ws.topk_w);
     return hipGetLastError();
 }
 
-hipError_t launch_sort(const Dims& dm, const Workspace& ws, hipStream_t s) {
-    const size_t lds = sizeof(int32_t) * ((size_t)kSortWaves * dm.E + 2 * dm.E + 2 * kSortWaves);
+hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s) {
+    const size_t lds = sizeof(int32_t) * ((size_t)kSortWaves * dm.E + ((dm.E + 3) & ~3) + dm.E + 2 * kSortWaves);
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
-                       ws.sorted_pairs, ws.inverse, ws.active, ws.chunks, ws.nchunks);
+                       ws.sorted_pairs, ws.inverse, ws.active, ws.chunks, ws.nchunks, chunk_rows);
     return hipGetLastError();
 }
 

@@ -169,6 +169,29 @@ def test_edge_shapes(T, E, k):
     assert problems.rel_max_err(got["y"], ref) <= TOL
 
 
+@pytest.mark.parametrize("T,E,k,coarse", [
+    (20, 100, 6, False),      # E not a multiple of 64
+    (24, 128, 8, True),       # many exact ties
+    (33, 64, 8, True),
+    (17, 200, 8, False),      # wave-wide argmax rounds (E > 128)
+    (9, 512, 32, True),       # largest E and k the library accepts
+])
+def test_routing_across_expert_counts(T, E, k, coarse):
+    rng = np.random.default_rng(70 + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    if coarse:
+        logits = np.round(logits * 2) / 2                     # values on a grid of 0.5
+        logits[0, :] = 0.0                                     # a token with all logits tied
+        logits[1, ::2] = -0.0                                  # signed zeros tie with +0
+    w, acts, wts = _custom(T, 256, 256, E, k, seed=70 + E, logits=logits)
+    got, _ = _run(w, acts, problems.to_device(wts))
+    _check_routing(w, acts, got)
+    if coarse:
+        assert np.array_equal(got["topk_ids"].reshape(T, k)[0], np.arange(k))
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)["y"]
+    assert problems.rel_max_err(got["y"], ref) <= TOL
+
+
 def test_all_tokens_on_the_same_experts_multi_chunk():
     T, E, k = 150, 8, 2                                  # 150 pairs per expert: 3 chunks
     logits = np.zeros((T, E), np.float32)
