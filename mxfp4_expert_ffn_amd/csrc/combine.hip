@@ -13,7 +13,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One thread per 4 consecutive output columns of one token.
+// One thread per 4 consecutive output columns of one token.  KK > 0: k is
+// KK and the k row loads are all issued before the sum (the rows are read
+// once, so they bypass the caches' retention).
+template <int KK>
 __global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const float* __restrict__ o,
                                                        const int32_t* __restrict__ inverse,
                                                        void* __restrict__ out, int out_dtype) {
@@ -21,11 +24,22 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const float* __r
     const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= (size_t)dm.T * q) return;
     const int t = (int)(gid / q), c = (int)(gid % q) * 4;
+    const int k = KK > 0 ? KK : dm.k;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < dm.k; ++j) {
-        const size_t row = (size_t)inverse[(size_t)t * dm.k + j];
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(o + row * dm.d + c);
-        acc += v;
+    if constexpr (KK > 0) {
+        f32x4_t v[KK];
+#pragma unroll
+        for (int j = 0; j < KK; ++j) {
+            const size_t row = (size_t)inverse[(size_t)t * KK + j];
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(o + row * dm.d + c));
+        }
+#pragma unroll
+        for (int j = 0; j < KK; ++j) acc += v[j];
+    } else {
+        for (int j = 0; j < k; ++j) {
+            const size_t row = (size_t)inverse[(size_t)t * k + j];
+            acc += *reinterpret_cast<const f32x4_t*>(o + row * dm.d + c);
+        }
     }
     if (out_dtype == MOE_OUT_F32) {
         *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + (size_t)t * dm.d + c) = acc;
@@ -149,8 +163,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 
 hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, hipStream_t s) {
     const size_t n = (size_t)dm.T * (dm.d / 4);
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                       dm, ws.o, ws.inverse, out, out_dtype);
+    const dim3 grid((unsigned)((n + kThreads - 1) / kThreads)), block(kThreads);
+    if (dm.k == 8)
+        hipLaunchKernelGGL(k_finalize<8>, grid, block, 0, s, dm, ws.o, ws.inverse, out, out_dtype);
+    else
+        hipLaunchKernelGGL(k_finalize<0>, grid, block, 0, s, dm, ws.o, ws.inverse, out, out_dtype);
     return hipGetLastError();
 }
 

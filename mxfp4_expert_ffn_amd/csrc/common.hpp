@@ -64,24 +64,13 @@ __device__ __forceinline__ int mx_scale_exp(float amax, int emax_elem) {
 // E4M3 code (OCP: bias 7, 3 mantissa bits, largest finite 448, no infinity)
 // of an already-scaled finite value: nearest, ties to the even code,
 // saturating at +-448 (never the NaN code); the sign of a zero result kept.
+// The gfx950 convert rounds to nearest-even but turns magnitudes from 464 up
+// into the NaN code, so the value is clamped to +-448 first (values in
+// (448, 464) round to 448 either way).  Checked against a bitwise
+// implementation of the rule on every finite float below 2^10 in magnitude.
 __device__ __forceinline__ uint32_t e4m3_code(float q) {
-    const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-    const float a = fabsf(q);
-    uint32_t mag;
-    if (a < 0.015625f) {                       // below 2^-6: subnormal steps of 2^-9
-        mag = (uint32_t)rintf(a * 512.0f);     // exact product; rint is nearest-even; 8 = 2^-6
-    } else {
-        uint32_t u = __float_as_uint(a);
-        u += 0x7FFFFu + ((u >> 20) & 1u);      // nearest-even at 3 mantissa bits
-        int e = (int)(u >> 23) - 127;          // -6 .. 9
-        uint32_t m = (u >> 20) & 7u;
-        if (e > 8 || (e == 8 && m == 7u)) {    // past 448: saturate
-            e = 8;
-            m = 6u;
-        }
-        mag = ((uint32_t)(e + 7) << 3) | m;
-    }
-    return sign | mag;
+    const float c = fminf(fmaxf(q, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
 
 // float -> bf16 bits, round to nearest even (finite inputs).

@@ -14,40 +14,39 @@
 //
 // Work unit = (chunk of <= 128 pairs of one expert, 256 weight rows).  Both
 // operands of a 128-wide K step go through LDS by direct-to-LDS buffer
-// loads, double buffered: 16 KB of E4M3 rows (16-byte chunks XOR-swizzled
-// by row, so the operand reads are free of bank conflicts) and 16 KB of FP4
-// weight tiles in their stored order, which is already the B-operand order
-// of the matrix core (lane L: weight row L%16, MX block L/16).  Scales go
-// through LDS once per 4 steps: 4 KB of weight scales (the stored dword of a
-// lane holds its 4 steps; the MFMA's op_sel picks the step's byte) and 2 KB
-// of activation scales.
+// loads into a ring of 4 step buffers, so the loads of a step are issued 3
+// steps before it computes (a weight tile read for the first time comes
+// from HBM, slower than one step): 16 KB of E4M3 rows (16-byte chunks
+// XOR-swizzled by row, so the operand reads are free of bank conflicts) and
+// 16 KB of FP4 weight tiles in their stored order, which is already the
+// B-operand order of the matrix core (lane L: weight row L%16, MX block
+// L/16).  Scales go through LDS once per 4 steps: 4 KB of weight scales (the
+// stored dword of a lane holds its 4 steps; the MFMA's op_sel picks the
+// step's byte) and 2 KB of activation scales.  140 KB of LDS: one workgroup
+// of 8 wavefronts per CU, two per SIMD.
 //
-// Four wavefronts in a 2 x 2 grid; each computes 64 pairs x 128 weight rows
-// (4 x 8 MFMA tiles, 32 accumulators).  Sharing both operands through LDS
-// halves the L2-to-CU bytes per MFMA against streaming the weights into each
-// wave's registers, which is what the verify-batch kernels do.
+// The 8 wavefronts form a 2 x 4 grid; each computes 64 pairs x 64 weight
+// rows (4 x 4 MFMA tiles).  Sharing both operands through LDS halves the
+// L2-to-CU bytes per MFMA against streaming the weights into each wave's
+// registers, which is what the verify-batch kernels do.
 //
 // Gate/up: weight rows 0..127 of a unit are W_gate rows (h columns), 128..255
-// the W_up rows of the same columns, and a wave's tiles j and j + 4 meet in
+// the W_up rows of the same columns, and a wave's tiles j and j + 2 meet in
 // one lane, so SwiGLU and the MXFP8 re-quantisation of h (a wave row's 32
-// columns x 2 are two MX blocks) run in the epilogue.  Down: the epilogue
+// columns are one MX block) run in the epilogue.  Down: the epilogue
 // multiplies by the pair's routing weight and stores float32 per pair.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kW = 4;                       // wavefronts per workgroup
-constexpr int kT = kW * kWave;
 constexpr int kTM = kDenseChunk;            // pair rows per unit
 constexpr int kTiles = 16;                  // 16-row weight tiles per unit
-constexpr int kJ = 8;                       // weight tiles per wavefront
-constexpr int kMs = 4;                      // 16-row pair sub-tiles per wavefront
+constexpr int kMs = 4;                      // 16-row pair sub-tiles per wavefront (64 pairs)
 constexpr int kASlot = kTM * kKStep;        // E4M3 rows of one step
 constexpr int kBSlot = kTiles * 1024;       // FP4 tiles of one step
 constexpr int kBsSlot = kTiles * 256;       // weight scales of 4 steps
 constexpr int kAsSlot = kTM * 16;           // activation scales of 4 steps
-constexpr int kLds = 2 * (kASlot + kBSlot + kBsSlot + kAsSlot);
 constexpr int kRsrcWord3 = 0x00020000;      // gfx9 raw buffer descriptor, dword 3
 
 enum { kGateUp = 0, kDown = 1 };
@@ -75,12 +74,16 @@ typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g), with the hardware reciprocal (1 ulp)
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-// Wait for all of this wave's outstanding loads and LDS reads, then a
-// workgroup barrier (gfx9 s_waitcnt: vmcnt 0, expcnt 7, lgkmcnt 0).
-__device__ __forceinline__ void drain_barrier() {
-    __builtin_amdgcn_s_waitcnt(7 << 4);
+// Wait until at most N of this wave's loads are outstanding and its LDS
+// reads have returned, then a workgroup barrier (gfx9 s_waitcnt encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in bits 15:14).
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
     __builtin_amdgcn_s_barrier();
 }
 
@@ -88,12 +91,37 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
 }
 
-template <int MODE>
+// Tile shape: 2 x WN wavefronts, each 64 pairs x (256 / WN) weight rows;
+// STAGES step buffers in the LDS ring (loads issued STAGES - 1 steps ahead).
+template <int WN, int STAGES>
+struct Shape {
+    static constexpr int kW = 2 * WN;                  // wavefronts per workgroup
+    static constexpr int kT = kW * kWave;
+    static constexpr int kJ = kTiles / WN;             // weight tiles per wavefront
+    static constexpr int kQ = kTiles / kW;             // 1 KB loads per wave per step, A and B each
+    static constexpr int kLds = STAGES * (kASlot + kBSlot) + 2 * (kBsSlot + kAsSlot);
+    static constexpr int kPerCu = kLds <= 80 * 1024 ? 2 : 1;
+    static_assert(kLds <= 160 * 1024, "LDS of one CU");
+    static_assert(STAGES >= 2 && STAGES <= 5, "the 2-slot scale ring needs STAGES <= 5");
+    // loads a wave issues for step j: A and B, plus 2 scale loads at the
+    // first step of a 4-step group
+    static constexpr int loads_of_step(int j) { return 2 * kQ + (j % 4 == 0 ? 2 : 0); }
+    static constexpr int pending(int s4, int n) {
+        int c = 0;
+        for (int i = 1; i <= n; ++i) c += loads_of_step(s4 + i);
+        return c;
+    }
+};
+
+template <int MODE, int WN, int STAGES>
 struct Dense {
+    using S = Shape<WN, STAGES>;
+    static constexpr int kW = S::kW, kJ = S::kJ, kQ = S::kQ;
+
     struct Ctx {
         __amdgpu_buffer_rsrc_t ra, ras, rw, rs;   // activations, their scales, this wave's B matrix + scales
-        uint32_t avoff[4];                        // A row loads of this lane
-        uint32_t asoff;                           // A scale row of this lane (waves 0, 1)
+        uint32_t avoff[kQ];                       // A row loads of this lane
+        uint32_t asoff;                           // A scale row of this lane
         uint32_t bvs;                             // lane offset of the B-scale load
         int btile0;                               // first weight tile this wave loads
         int ns, ng, wave;
@@ -102,63 +130,85 @@ struct Dense {
 
     // weight-tile slot of the unit that this wave's tile jj uses
     __device__ static int wslot(int wn, int jj) {
-        if constexpr (MODE == kGateUp) return jj < 4 ? wn * 4 + jj : 8 + wn * 4 + (jj - 4);
-        else return wn * 8 + jj;
+        constexpr int h = kJ / 2;
+        if constexpr (MODE == kGateUp) return jj < h ? wn * h + jj : 8 + wn * h + (jj - h);
+        else return wn * kJ + jj;
     }
 
-    __device__ static void issue_ab(const Ctx& c, int step, int slot, int lane) {
+    __device__ static void issue_ab(const Ctx& c, int step, int lane) {
+        const int slot = step % STAGES;
         uint8_t* dA = c.lA + slot * kASlot;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lds_dma16(c.ra, dA + (q * kW + c.wave) * 1024, c.avoff[q], step * kKStep);
-        uint8_t* dB = c.lB + slot * kBSlot + c.wave * 4 * 1024;
+        for (int q = 0; q < kQ; ++q) lds_dma16(c.ra, dA + (q * kW + c.wave) * 1024, c.avoff[q], step * kKStep);
+        uint8_t* dB = c.lB + slot * kBSlot + c.wave * kQ * 1024;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16(c.rw, dB + i * 1024, lane * 16, ((c.btile0 + i) * c.ns + step) * 1024);
+        for (int i = 0; i < kQ; ++i) lds_dma16(c.rw, dB + i * 1024, lane * 16, ((c.btile0 + i) * c.ns + step) * 1024);
     }
 
-    __device__ static void issue_scales(const Ctx& c, int grp, int gs) {
-        lds_dma16(c.rs, c.lBs + gs * kBsSlot + c.wave * 4 * 256, c.bvs, (c.btile0 * c.ng + grp) * 256);
-        if (c.wave < 2) lds_dma16(c.ras, c.lAs + gs * kAsSlot + c.wave * 1024, c.asoff, grp * 16);
+    // B scales: this wave's kQ tiles x 256 B; A scales: 128 / kW rows of 16 B.
+    __device__ static void issue_scales(const Ctx& c, int grp, int lane) {
+        const int gs = grp & 1;
+        if (lane < 16 * kQ)
+            lds_dma16(c.rs, c.lBs + gs * kBsSlot + c.wave * kQ * 256, c.bvs, (c.btile0 * c.ng + grp) * 256);
+        if (lane < kTM / kW) lds_dma16(c.ras, c.lAs + gs * kAsSlot + c.wave * (kTM / kW) * 16, c.asoff, grp * 16);
     }
 
-    template <int S4>
+    // The A operands of the step are read first (they serve every MFMA), then
+    // the weight tiles one ahead of the MFMAs that use them.  FULL: every
+    // sub-tile of the wave holds pairs (otherwise only the first nms are
+    // multiplied).
+    template <int S4, bool FULL>
     __device__ static void compute(const Ctx& c, f32x4_t (&acc)[kMs][kJ], const uint32_t (&sbw)[kJ], int slot,
                                    int gs, int nms, int wm, int wn, int lane) {
         const int li = lane % 16, g = lane / 16;
         const uint8_t* A = c.lA + slot * kASlot;
-        const uint8_t* B = c.lB + slot * kBSlot;
+        const uint8_t* B = c.lB + slot * kBSlot + lane * 16;
         const uint8_t* As = c.lAs + gs * kAsSlot;
-        u32x4_t b[kJ];
-#pragma unroll
-        for (int jj = 0; jj < kJ; ++jj) b[jj] = *reinterpret_cast<const u32x4_t*>(B + wslot(wn, jj) * 1024 + lane * 16);
+        i32x8_t a[kMs];
+        int sa[kMs];
 #pragma unroll
         for (int ms = 0; ms < kMs; ++ms) {
-            if (ms < nms) {
-                const int r = wm * 64 + ms * 16 + li;
-                const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(A + r * kKStep + swz(r, g) * 16);
-                const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(A + r * kKStep + swz(r, 4 + g) * 16);
-                const i32x8_t a = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                const int sa = As[r * 16 + S4 * 4 + g];
+            const int r = wm * 64 + ms * 16 + li;
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(A + r * kKStep + swz(r, g) * 16);
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(A + r * kKStep + swz(r, 4 + g) * 16);
+            a[ms] = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            sa[ms] = As[r * 16 + S4 * 4 + g];
+        }
+        u32x4_t b = *reinterpret_cast<const u32x4_t*>(B + wslot(wn, 0) * 1024);
 #pragma unroll
-                for (int jj = 0; jj < kJ; ++jj) {
-                    // FP4 B operand: only the low 4 registers are read
-                    const i32x8_t bb = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(b[jj], b[jj], 0, 1, 2, 3, 0, 1, 2, 3));
+        for (int jj = 0; jj < kJ; ++jj) {
+            u32x4_t bn = b;
+            if (jj + 1 < kJ) bn = *reinterpret_cast<const u32x4_t*>(B + wslot(wn, jj + 1) * 1024);
+            // FP4 B operand: only the low 4 registers are read
+            const i32x8_t bb = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3));
+#pragma unroll
+            for (int ms = 0; ms < kMs; ++ms)
+                if (FULL || ms < nms)
                     acc[ms][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        a, bb, acc[ms][jj], 0 /* A: E4M3 */, 4 /* B: E2M1 */, 0, sa, S4, (int)sbw[jj]);
-                }
-            }
+                        a[ms], bb, acc[ms][jj], 0 /* A: E4M3 */, 4 /* B: E2M1 */, 0, sa[ms], S4, (int)sbw[jj]);
+            b = bn;
         }
     }
 
-    // Step s (s mod 4 == S4): its loads have landed once every wave drains
-    // and meets at the barrier; the next step's loads then go to the other
-    // buffer, which every wave finished reading before the barrier.
-    template <int S4>
+    // Step s (s mod 4 == S4).  The loads of step s were issued STAGES - 1
+    // steps earlier; those of the (up to STAGES - 2) steps after it may
+    // still be in flight and the issue order is fixed, so a vmcnt wait on
+    // their number plus the barrier (every wave's direct-to-LDS writes done)
+    // makes step s's buffer valid.  The barrier also means every wave has
+    // finished step s-1, whose buffer then takes step s + STAGES - 1.
+    template <int S4, bool FULL>
     __device__ static void step(const Ctx& c, f32x4_t (&acc)[kMs][kJ], uint32_t (&sbw)[kJ], int s, int nms,
                                 int wm, int wn, int lane) {
-        drain_barrier();
-        if (s + 1 < c.ns) {
-            if (S4 == 3) issue_scales(c, (s + 1) / 4, ((s + 1) / 4) & 1);
-            issue_ab(c, s + 1, (s + 1) & 1, lane);
+        const int ahead = min(STAGES - 2, c.ns - 1 - s);
+        if (STAGES >= 4 && ahead >= 2)
+            wait_barrier<S::pending(S4, STAGES >= 4 ? 2 : 0)>();
+        else if (STAGES >= 3 && ahead >= 1)
+            wait_barrier<S::pending(S4, STAGES >= 3 ? 1 : 0)>();
+        else
+            wait_barrier<0>();
+        if (s + STAGES - 1 < c.ns) {
+            if ((S4 + STAGES - 1) % 4 == 0) issue_scales(c, (s + STAGES - 1) / 4, lane);
+            issue_ab(c, s + STAGES - 1, lane);
         }
         const int gs = (s / 4) & 1;
         if (S4 == 0) {
@@ -166,7 +216,18 @@ struct Dense {
             for (int jj = 0; jj < kJ; ++jj)
                 sbw[jj] = *reinterpret_cast<const uint32_t*>(c.lBs + gs * kBsSlot + wslot(wn, jj) * 256 + lane * 4);
         }
-        compute<S4>(c, acc, sbw, s & 1, gs, nms, wm, wn, lane);
+        compute<S4, FULL>(c, acc, sbw, s % STAGES, gs, nms, wm, wn, lane);
+    }
+
+    template <bool FULL>
+    __device__ static void main_loop(const Ctx& c, f32x4_t (&acc)[kMs][kJ], uint32_t (&sbw)[kJ], int nms, int wm,
+                                     int wn, int lane) {
+        for (int s = 0; s < c.ns; s += 4) {
+            step<0, FULL>(c, acc, sbw, s, nms, wm, wn, lane);
+            if (s + 1 < c.ns) step<1, FULL>(c, acc, sbw, s + 1, nms, wm, wn, lane);
+            if (s + 2 < c.ns) step<2, FULL>(c, acc, sbw, s + 2, nms, wm, wn, lane);
+            if (s + 3 < c.ns) step<3, FULL>(c, acc, sbw, s + 3, nms, wm, wn, lane);
+        }
     }
 
     __device__ static void run(const DenseArgs& a, uint8_t* smem, int e, int nt, int m0, int c0, int M) {
@@ -182,13 +243,13 @@ struct Dense {
         c.ng = (c.ns + 3) / 4;
         c.wave = wave;
         c.lA = smem;
-        c.lB = c.lA + 2 * kASlot;
-        c.lBs = c.lB + 2 * kBSlot;
+        c.lB = c.lA + STAGES * kASlot;
+        c.lBs = c.lB + STAGES * kBSlot;
         c.lAs = c.lBs + 2 * kBsSlot;
         const uint32_t wbytes = (uint32_t)a.N * (uint32_t)(a.K / 2);
         const uint32_t sbytes = (uint32_t)(a.N / 16) * (uint32_t)c.ng * 256u;
-        // the 4 weight tiles this wave loads: one matrix, consecutive tiles
-        const int jb = wave * 4;
+        // the kQ weight tiles this wave loads: one matrix, consecutive tiles
+        const int jb = wave * kQ;
         const bool up = MODE == kGateUp && jb >= 8;
         c.btile0 = MODE == kGateUp ? nt * 8 + (jb & 7) : nt * 16 + jb;
         const uint8_t* wm_ptr = up ? a.w1 : a.w0;
@@ -198,7 +259,7 @@ struct Dense {
         c.ra = __builtin_amdgcn_make_buffer_rsrc((void*)a.act, 0, a.act_rows * (uint32_t)a.K, kRsrcWord3);
         c.ras = __builtin_amdgcn_make_buffer_rsrc((void*)a.act_scale, 0, a.act_rows * (uint32_t)(a.K / kBlock),
                                                   kRsrcWord3);
-        c.bvs = (uint32_t)((lane / 16) * c.ng * 256 + (lane % 16) * 16);
+        c.bvs = (uint32_t)(((lane / 16) % kQ) * c.ng * 256 + (lane % 16) * 16);
 
         // Source row of unit row r; rows past the chunk's last pair repeat
         // it (their results are computed and never stored).
@@ -206,15 +267,15 @@ struct Dense {
             const int idx = min(c0 + r, M - 1);
             return MODE == kGateUp ? (uint32_t)(a.sorted[m0 + idx] / a.k_top) : (uint32_t)(m0 + idx);
         };
-        // A load q of this wave fills LDS bytes (q*4 + wave) KB of the step
+        // A load q of this wave fills LDS bytes (q*kW + wave) KB of the step
         // buffer: 8 rows, lane -> row lane/8, physical chunk lane%8, which
         // holds the logical chunk swz() maps there (swz is an involution).
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kQ; ++q) {
             const int r = 8 * (q * kW + wave) + lane / 8;
             c.avoff[q] = src_row(r) * (uint32_t)a.K + (uint32_t)(swz(r, lane % 8) * 16);
         }
-        c.asoff = wave < 2 ? src_row(wave * 64 + lane) * (uint32_t)(a.K / kBlock) : 0u;
+        c.asoff = src_row(wave * (kTM / kW) + lane % (kTM / kW)) * (uint32_t)(a.K / kBlock);
 
         f32x4_t acc[kMs][kJ];
 #pragma unroll
@@ -223,14 +284,18 @@ struct Dense {
             for (int jj = 0; jj < kJ; ++jj) acc[ms][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         uint32_t sbw[kJ];
 
-        issue_scales(c, 0, 0);
-        issue_ab(c, 0, 0, lane);
-        for (int s = 0; s < c.ns; s += 4) {
-            step<0>(c, acc, sbw, s, nms, wm, wn, lane);
-            if (s + 1 < c.ns) step<1>(c, acc, sbw, s + 1, nms, wm, wn, lane);
-            if (s + 2 < c.ns) step<2>(c, acc, sbw, s + 2, nms, wm, wn, lane);
-            if (s + 3 < c.ns) step<3>(c, acc, sbw, s + 3, nms, wm, wn, lane);
+        // prologue: steps 0 .. STAGES-2, the first group's scales first
+        // (sched_barrier keeps the issue order that the vmcnt waits count on)
+        issue_scales(c, 0, lane);
+#pragma unroll
+        for (int j = 0; j < STAGES - 1; ++j) {
+            if (j < c.ns) issue_ab(c, j, lane);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (nms == kMs)
+            main_loop<true>(c, acc, sbw, nms, wm, wn, lane);
+        else
+            main_loop<false>(c, acc, sbw, nms, wm, wn, lane);
 
         // Epilogue.  Lane holds D[pair wm*64 + ms*16 + 4g + r][column li] of
         // tile jj.
@@ -242,34 +307,31 @@ struct Dense {
                 const int idx = c0 + wm * 64 + ms * 16 + 4 * g + r;
                 const size_t orow = (size_t)(m0 + idx);
                 if constexpr (MODE == kGateUp) {
-                    const int col0 = nt * 128 + wn * 64;          // h columns of this wave
-                    float h[4];
+                    // the wave's h columns: kJ/2 tiles of 16, MX blocks of 2 tiles
+                    constexpr int h = kJ / 2;
+                    const int col0 = nt * 128 + wn * h * 16;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) h[jj] = silu(acc[ms][jj][r]) * acc[ms][jj + 4][r];
-                    float am0 = fmaxf(fabsf(h[0]), fabsf(h[1]));
-                    float am1 = fmaxf(fabsf(h[2]), fabsf(h[3]));
+                    for (int bk = 0; bk < h / 2; ++bk) {
+                        const float h0 = silu(acc[ms][2 * bk][r]) * acc[ms][2 * bk + h][r];
+                        const float h1 = silu(acc[ms][2 * bk + 1][r]) * acc[ms][2 * bk + 1 + h][r];
+                        float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
-                    for (int off = 1; off < 16; off <<= 1) {
-                        am0 = fmaxf(am0, __shfl_xor(am0, off));
-                        am1 = fmaxf(am1, __shfl_xor(am1, off));
-                    }
-                    const int se0 = mx_scale_exp(am0, 8), se1 = mx_scale_exp(am1, 8);
-                    if (idx < M) {
-                        uint8_t* hr = a.h_out + orow * a.ldo + col0 + li;
-                        hr[0] = (uint8_t)e4m3_code(ldexpf(h[0], -se0));
-                        hr[16] = (uint8_t)e4m3_code(ldexpf(h[1], -se0));
-                        hr[32] = (uint8_t)e4m3_code(ldexpf(h[2], -se1));
-                        hr[48] = (uint8_t)e4m3_code(ldexpf(h[3], -se1));
-                        if (li < 2)
-                            a.h_scale_out[orow * (a.ldo / kBlock) + col0 / kBlock + li] =
-                                (uint8_t)((li == 0 ? se0 : se1) + 127);
+                        for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+                        const int se = mx_scale_exp(amax, 8);
+                        if (idx < M) {
+                            uint8_t* hr = a.h_out + orow * a.ldo + col0 + bk * 32 + li;
+                            hr[0] = (uint8_t)e4m3_code(ldexpf(h0, -se));
+                            hr[16] = (uint8_t)e4m3_code(ldexpf(h1, -se));
+                            if (li == 0)
+                                a.h_scale_out[orow * (a.ldo / kBlock) + col0 / kBlock + bk] = (uint8_t)(se + 127);
+                        }
                     }
                 } else {
                     if (idx < M) {
                         const float wgt = a.topk_w[a.sorted[m0 + idx]];
-                        float* orow_p = a.o_out + orow * a.ldo + nt * 256 + wn * 128 + li;
+                        float* orow_p = a.o_out + orow * a.ldo + nt * 256 + wn * kJ * 16 + li;
 #pragma unroll
-                        for (int jj = 0; jj < kJ; ++jj) orow_p[jj * 16] = wgt * acc[ms][jj][r];
+                        for (int jj = 0; jj < kJ; ++jj) __builtin_nontemporal_store(wgt * acc[ms][jj][r], orow_p + jj * 16);
                     }
                 }
             }
@@ -277,9 +339,9 @@ struct Dense {
     }
 };
 
-template <int MODE>
-__global__ __launch_bounds__(kT, 2) void k_dense(DenseArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+template <int MODE, int WN, int STAGES>
+__global__ __launch_bounds__((Shape<WN, STAGES>::kT), (Shape<WN, STAGES>::kPerCu)) void k_dense(DenseArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Shape<WN, STAGES>::kLds];
     // Work unit = (chunk, column tile), chunk-major; chunks are listed
     // expert by expert, hottest first.  Uniform values go to scalar
     // registers so that the buffer descriptors built from them are scalar.
@@ -292,7 +354,7 @@ __global__ __launch_bounds__(kT, 2) void k_dense(DenseArgs a) {
     const int c0 = __builtin_amdgcn_readfirstlane(rec[1]);
     const int m0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
     const int M = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - m0;
-    Dense<MODE>::run(a, smem, e, nt, m0, c0, M);
+    Dense<MODE, WN, STAGES>::run(a, smem, e, nt, m0, c0, M);
 }
 
 // Upper bound of the chunk list at kDenseChunk pairs per chunk.
@@ -301,9 +363,17 @@ int max_dense_chunks(const Dims& dm) {
     return active + dm.P / kDenseChunk;
 }
 
+#ifndef DENSE_WN
+#define DENSE_WN 2
+#endif
+#ifndef DENSE_STAGES
+#define DENSE_STAGES 2
+#endif
+
 template <int MODE>
 hipError_t launch(const DenseArgs& a, int units, hipStream_t s) {
-    hipLaunchKernelGGL(k_dense<MODE>, dim3(units), dim3(kT), 0, s, a);
+    constexpr int WN = DENSE_WN, ST = DENSE_STAGES;
+    hipLaunchKernelGGL((k_dense<MODE, WN, ST>), dim3(units), dim3(Shape<WN, ST>::kT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -92,7 +92,8 @@ struct GemmArgs {
     int32_t ldo;                // output row length (elements)
 };
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g), with the hardware reciprocal (1 ulp)
+__device__ __forceinline__ float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and its LDS reads have returned, then a workgroup barrier
