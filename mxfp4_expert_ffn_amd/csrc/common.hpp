@@ -90,6 +90,7 @@ struct Workspace {
     float* topk_w;            // [P]
     int32_t* offsets;         // [E+1]
     int32_t* sorted_pairs;    // [P]
+    float* sorted_w;          // [P]   routing weight of sorted_pairs[i]
     int32_t* inverse;         // [P]   position of pair p in sorted_pairs
     int32_t* active;          // [E+1] active experts (count > 0) by descending count; [E] = how many
     int32_t* chunks;          // [max_chunks][4] (expert, first pair within the expert,
@@ -120,10 +121,10 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
 hipError_t launch_quant_x8(const uint16_t* x, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_quant_act8(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);
+// bf16 activations (verify batches): weights streamed through registers.
 hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm,
-                         const Workspace& ws, bool mx8, hipStream_t s);
-hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, bool mx8,
-                       hipStream_t s);
+                         const Workspace& ws, hipStream_t s);
+hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, hipStream_t s);
 // MXFP8 activations (dense regime): 128-pair x 256-weight-row tiles, both
 // operands staged in LDS, scaled MFMA.
 hipError_t launch_gateup_dense(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,

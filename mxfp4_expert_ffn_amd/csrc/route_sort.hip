@@ -176,6 +176,8 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) 
 __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ sorted,
+                                                       const float* __restrict__ topk_w,
+                                                       float* __restrict__ sorted_w,
                                                        int32_t* __restrict__ inverse,
                                                        int32_t* __restrict__ active,
                                                        int32_t* __restrict__ chunks,
@@ -204,6 +206,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     // for the scatter instead of loading them again
     const bool one_round = per_wave <= kPrefetch * kWave;
     int keep[kPrefetch];
+    float keepw[kPrefetch];
 
     // 1) per-wave histograms, pairs visited in ascending order; the ids of
     //    kPrefetch rounds are loaded together so that their latencies overlap
@@ -214,6 +217,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
             const int p = base + q * kWave + lane;
             ev[q] = p < p1 ? ids[p] : 0;
             keep[q] = ev[q];
+            keepw[q] = p < p1 ? topk_w[p] : 0.0f;
         }
 #pragma unroll
         for (int q = 0; q < kPrefetch; ++q) {
@@ -302,10 +306,12 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     // 3) scatter in the same visiting order: stable within each expert
     for (int base = p0; base < p1; base += kPrefetch * kWave) {
         int ev[kPrefetch];
+        float wv[kPrefetch];
 #pragma unroll
         for (int q = 0; q < kPrefetch; ++q) {
             const int p = base + q * kWave + lane;
             ev[q] = one_round ? keep[q] : (p < p1 ? ids[p] : 0);
+            wv[q] = one_round ? keepw[q] : (p < p1 ? topk_w[p] : 0.0f);
         }
 #pragma unroll
         for (int q = 0; q < kPrefetch; ++q) {
@@ -318,6 +324,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
             const int pos = valid ? my[e] + rank : 0;
             if (valid) {
                 sorted[pos] = p;
+                sorted_w[pos] = wv[q];
                 inverse[p] = pos;
             }
             if (valid && rank == 0) my[e] += __popcll(peers);
@@ -343,7 +350,7 @@ hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s) {
     const size_t lds = sizeof(int32_t) * ((size_t)kSortWaves * dm.E + ((dm.E + 3) & ~3) + dm.E + 2 * kSortWaves);
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
-                       ws.sorted_pairs, ws.inverse, ws.active, ws.chunks, ws.nchunks, chunk_rows);
+                       ws.sorted_pairs, ws.topk_w, ws.sorted_w, ws.inverse, ws.active, ws.chunks, ws.nchunks, chunk_rows);
     return hipGetLastError();
 }
 
