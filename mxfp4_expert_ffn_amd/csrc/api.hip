@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t ids, w, offsets, sorted, sorted_w, inverse, active, chunks, nchunks, xq, xs, h, hs, o, total;
+    size_t ids, w, offsets, sorted, sorted_w, inverse, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
@@ -49,6 +49,7 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     moe::Dims dm{(int32_t)T, c.d_model, c.d_ff, c.num_experts, c.top_k, (int32_t)P};
     L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * moe::kChunkRec * sizeof(int32_t));
     L.nchunks = at; at += 256;
+    L.sort_part = at; at += round256((size_t)moe::sort_tiles((int)P) * c.num_experts * sizeof(int32_t));
     const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
     L.xq = at;      at += mx8 ? round256((size_t)T * c.d_model) : 0;
     L.xs = at;      at += mx8 ? round256((size_t)T * (c.d_model / MOE_MXFP4_BLOCK)) : 0;
@@ -206,6 +207,7 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     ws.active = reinterpret_cast<int32_t*>(base + L.active);
     ws.chunks = reinterpret_cast<int32_t*>(base + L.chunks);
     ws.nchunks = reinterpret_cast<int32_t*>(base + L.nchunks);
+    ws.sort_part = reinterpret_cast<int32_t*>(base + L.sort_part);
     ws.xq = reinterpret_cast<uint8_t*>(base + L.xq);
     ws.xs = reinterpret_cast<uint8_t*>(base + L.xs);
     ws.h = reinterpret_cast<uint8_t*>(base + L.h);

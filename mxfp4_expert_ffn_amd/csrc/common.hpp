@@ -96,6 +96,7 @@ struct Workspace {
     int32_t* chunks;          // [max_chunks][4] (expert, first pair within the expert,
                               //   first chunk of the expert, number of chunks of the expert)
     int32_t* nchunks;         // [1] number of chunks
+    int32_t* sort_part;       // [sort_tiles(P)][E] per-tile expert histograms / first positions
     uint8_t* xq;              // MXFP8 mode: [T][d] E4M3 codes of x
     uint8_t* xs;              // MXFP8 mode: [T][d/32] E8M0 scales of x
     uint8_t* h;               // [P][f] bf16 (or E4M3 codes in MXFP8 mode), rows in sorted order
@@ -107,6 +108,11 @@ struct Workspace {
 struct Dims {
     int32_t T, d, f, E, k, P;
 };
+
+// Pair counts up to this are sorted by one workgroup; above, by tiles of
+// 2048 pairs (sort_tiles of them).
+constexpr int kSortSingleMax = 8192;
+inline int sort_tiles(int P) { return P <= kSortSingleMax ? 0 : (P + 2047) / 2048; }
 
 // Upper bound of the chunk list: one partial chunk per active expert plus
 // the full chunks.

@@ -171,79 +171,54 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) 
     return m;
 }
 
-// Single workgroup.  LDS: hist[kSortWaves][E] + counts[E rounded up to 4]
-// + act[E] + 32 ints.
-__global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
-                                                       int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ sorted,
-                                                       const float* __restrict__ topk_w,
-                                                       float* __restrict__ sorted_w,
-                                                       int32_t* __restrict__ inverse,
-                                                       int32_t* __restrict__ active,
-                                                       int32_t* __restrict__ chunks,
-                                                       int32_t* __restrict__ nchunks, int chunk_rows) {
-    extern __shared__ int32_t sm[];
-    const int E = dm.E, P = dm.P;
-    int32_t* hist = sm;                               // [kSortWaves][E]
-    const int E4 = (E + 3) & ~3;
-    int32_t* counts = sm + kSortWaves * E;            // [E4], zero past E
-    int32_t* act = counts + E4;                       // [E] active experts in rank order
-    int32_t* wsum = act + E;                          // [16]
-    int32_t* wsum2 = wsum + kSortWaves;               // [16]
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+// Visit the pairs [p0, p1) of one wave in ascending order, kPrefetch rounds
+// of 64 at a time (their id loads overlap), and call f(q, valid, e, rank,
+// peers, p) per lane and pair: rank = lanes of this round before it with the
+// same expert, peers = those lanes' mask.  keep/keepw: the round's ids and
+// weights, reused instead of reloading when `reuse` (one round per wave).
+template <typename F>
+__device__ __forceinline__ void wave_pairs(const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
+                                           int p0, int p1, int nbits, int lane, bool reuse, int (&keep)[kPrefetch],
+                                           float (&keepw)[kPrefetch], F&& f) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-
-    for (int i = tid; i < kSortWaves * E; i += kSortThreads) hist[i] = 0;
-    __syncthreads();
-
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    const int per_wave = ((P + kSortWaves * kWave - 1) / (kSortWaves * kWave)) * kWave;
-    const int p0 = wave * per_wave;
-    const int p1 = min(P, p0 + per_wave);
-    int32_t* my = hist + wave * E;
-    // a wave whose pairs fit one prefetch round keeps their ids in registers
-    // for the scatter instead of loading them again
-    const bool one_round = per_wave <= kPrefetch * kWave;
-    int keep[kPrefetch];
-    float keepw[kPrefetch];
-
-    // 1) per-wave histograms, pairs visited in ascending order; the ids of
-    //    kPrefetch rounds are loaded together so that their latencies overlap
     for (int base = p0; base < p1; base += kPrefetch * kWave) {
-        int ev[kPrefetch];
+        if (!reuse) {
 #pragma unroll
-        for (int q = 0; q < kPrefetch; ++q) {
-            const int p = base + q * kWave + lane;
-            ev[q] = p < p1 ? ids[p] : 0;
-            keep[q] = ev[q];
-            keepw[q] = p < p1 ? topk_w[p] : 0.0f;
+            for (int q = 0; q < kPrefetch; ++q) {
+                const int p = base + q * kWave + lane;
+                keep[q] = p < p1 ? ids[p] : 0;
+                keepw[q] = (topk_w != nullptr && p < p1) ? topk_w[p] : 0.0f;
+            }
         }
 #pragma unroll
         for (int q = 0; q < kPrefetch; ++q) {
             if (base + q * kWave >= p1) break;            // uniform: past this wave's pairs
             const int p = base + q * kWave + lane;
             const bool valid = p < p1;
-            const uint64_t peers = match_peers(ev[q], valid, nbits);
-            const int rank = __popcll(peers & lt_mask);
-            if (valid && rank == 0) my[ev[q]] += __popcll(peers);
+            const uint64_t peers = match_peers(keep[q], valid, nbits);
+            f(q, valid, keep[q], __popcll(peers & lt_mask), __popcll(peers), p);
         }
     }
-    __syncthreads();
+}
 
-    // 2) per-expert totals; hist[w][e] becomes the count of waves before w
-    for (int e = tid; e < E; e += kSortThreads) {
-        int run = 0;
-        for (int w = 0; w < kSortWaves; ++w) {
-            const int c = hist[w * E + e];
-            hist[w * E + e] = run;
-            run += c;
-        }
-        counts[e] = run;
-    }
-    if (tid >= E && tid < E4) counts[tid] = 0;
-    __syncthreads();
+__device__ __forceinline__ int id_bits(int E) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    return nbits;
+}
 
+// From the per-expert pair counts (LDS counts[E4], zero past E) of all P
+// pairs, with every thread of a kSortThreads workgroup: expert offsets
+// [E+1], the active experts by descending count (ties to the lower index)
+// with their number at active[E], and the chunk records, expert by expert in
+// that order, with their number.  Returns the exclusive offset of expert
+// `threadIdx.x` (0 past E).  LDS: act[E] + 32 ints of scratch.
+__device__ int expert_lists(const int32_t* counts, int32_t* act, int32_t* wsum, int E, int P, int chunk_rows,
+                            int32_t* __restrict__ offsets, int32_t* __restrict__ active,
+                            int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    int32_t* wsum2 = wsum + kSortWaves;
+    const int E4 = (E + 3) & ~3;
     // exclusive scan of counts over experts (E <= 512 <= 1024 threads)
     const int c = tid < E ? counts[tid] : 0;
     const int incl = wave_inclusive_scan(c, lane);
@@ -254,8 +229,6 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     const int excl = before + incl - c;
     if (tid < E) {
         offsets[tid] = excl;
-        for (int w = 0; w < kSortWaves; ++w) hist[w * E + tid] += excl;
-        // active experts by descending pair count, ties to the lower index
         if (c > 0) {
             int r = 0;
             const int4* c4 = reinterpret_cast<const int4*>(counts);
@@ -302,34 +275,187 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     }
     if (tid == kSortThreads - 1) *nchunks = cbefore + nincl;
     __syncthreads();
+    return tid < E ? excl : 0;
+}
+
+// Single workgroup, up to kSortSingleMax pairs.  LDS: hist[kSortWaves][E] +
+// counts[E rounded up to 4] + act[E] + 32 ints.
+__global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted,
+                                                       const float* __restrict__ topk_w,
+                                                       float* __restrict__ sorted_w,
+                                                       int32_t* __restrict__ inverse,
+                                                       int32_t* __restrict__ active,
+                                                       int32_t* __restrict__ chunks,
+                                                       int32_t* __restrict__ nchunks, int chunk_rows) {
+    extern __shared__ int32_t sm[];
+    const int E = dm.E, P = dm.P;
+    const int E4 = (E + 3) & ~3;
+    int32_t* hist = sm;                               // [kSortWaves][E]
+    int32_t* counts = sm + kSortWaves * E;            // [E4], zero past E
+    int32_t* act = counts + E4;                       // [E] active experts in rank order
+    int32_t* wsum = act + E;                          // [32]
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+    for (int i = tid; i < kSortWaves * E; i += kSortThreads) hist[i] = 0;
+    __syncthreads();
+
+    const int nbits = id_bits(E);
+    const int per_wave = ((P + kSortWaves * kWave - 1) / (kSortWaves * kWave)) * kWave;
+    const int p0 = wave * per_wave;
+    const int p1 = min(P, p0 + per_wave);
+    int32_t* my = hist + wave * E;
+    // a wave whose pairs fit one prefetch round keeps their ids in registers
+    // for the scatter instead of loading them again
+    const bool one_round = per_wave <= kPrefetch * kWave;
+    int keep[kPrefetch];
+    float keepw[kPrefetch];
+
+    // 1) per-wave histograms
+    wave_pairs(ids, topk_w, p0, p1, nbits, lane, false, keep, keepw,
+               [&](int, bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
+    __syncthreads();
+
+    // 2) per-expert totals; hist[w][e] becomes the count of waves before w
+    for (int e = tid; e < E; e += kSortThreads) {
+        int run = 0;
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int c = hist[w * E + e];
+            hist[w * E + e] = run;
+            run += c;
+        }
+        counts[e] = run;
+    }
+    if (tid >= E && tid < E4) counts[tid] = 0;
+    __syncthreads();
+    const int excl = expert_lists(counts, act, wsum, E, P, chunk_rows, offsets, active, chunks, nchunks);
+    if (tid < E)
+        for (int w = 0; w < kSortWaves; ++w) hist[w * E + tid] += excl;
+    __syncthreads();
 
     // 3) scatter in the same visiting order: stable within each expert
-    for (int base = p0; base < p1; base += kPrefetch * kWave) {
-        int ev[kPrefetch];
-        float wv[kPrefetch];
+    wave_pairs(ids, topk_w, p0, p1, nbits, lane, one_round, keep, keepw,
+               [&](int q, bool valid, int e, int rank, int n, int p) {
+                   if (valid) {
+                       const int pos = my[e] + rank;
+                       sorted[pos] = p;
+                       sorted_w[pos] = keepw[q];
+                       inverse[p] = pos;
+                       if (rank == 0) my[e] += n;
+                   }
+               });
+}
+
+// Many pairs: tiles of kSortTile pairs, one 256-thread workgroup each (the
+// 4 waves split the tile in order).  k_sort_hist stores each tile's expert
+// histogram; k_sort_scan turns them into every tile's first position per
+// expert and writes the expert lists; k_sort_scatter places the pairs.  The
+// visiting order is the single-workgroup one (tiles, waves, rounds, lanes in
+// pair order), so the result is the same stable permutation.
+constexpr int kTileWaves = 4;
+constexpr int kSortTile = kTileWaves * kPrefetch * kWave;
+static_assert(kSortTile == 2048, "sort_tiles() counts tiles of 2048 pairs");
+
+__global__ __launch_bounds__(kTileWaves * kWave) void k_sort_hist(Dims dm, const int32_t* __restrict__ ids,
+                                                                  int32_t* __restrict__ part) {
+    extern __shared__ int32_t sm[];                   // [kTileWaves][E]
+    const int E = dm.E, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    for (int i = tid; i < kTileWaves * E; i += kTileWaves * kWave) sm[i] = 0;
+    __syncthreads();
+    const int p0 = blockIdx.x * kSortTile + wave * kPrefetch * kWave;
+    const int p1 = min(dm.P, p0 + kPrefetch * kWave);
+    int keep[kPrefetch];
+    float keepw[kPrefetch];
+    int32_t* my = sm + wave * E;
+    wave_pairs(ids, nullptr, p0, p1, id_bits(E), lane, false, keep, keepw,
+               [&](int, bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
+    __syncthreads();
+    for (int e = tid; e < E; e += kTileWaves * kWave) {
+        int c = 0;
+        for (int w = 0; w < kTileWaves; ++w) c += sm[w * E + e];
+        part[(size_t)blockIdx.x * E + e] = c;
+    }
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles, int32_t* __restrict__ part,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ active,
+                                                            int32_t* __restrict__ chunks,
+                                                            int32_t* __restrict__ nchunks, int chunk_rows) {
+    extern __shared__ int32_t sm[];
+    const int E = dm.E, E4 = (E + 3) & ~3, tid = threadIdx.x;
+    int32_t* counts = sm;                             // [E4]
+    int32_t* act = counts + E4;                       // [E]
+    int32_t* wsum = act + E;                          // [32]
+    // per expert: exclusive prefix over tiles (tile-major part[b][e])
+    if (tid < E) {
+        int run = 0;
+        int b = 0;
+        for (; b + 8 <= ntiles; b += 8) {
+            int v[8];
 #pragma unroll
-        for (int q = 0; q < kPrefetch; ++q) {
-            const int p = base + q * kWave + lane;
-            ev[q] = one_round ? keep[q] : (p < p1 ? ids[p] : 0);
-            wv[q] = one_round ? keepw[q] : (p < p1 ? topk_w[p] : 0.0f);
-        }
+            for (int i = 0; i < 8; ++i) v[i] = part[(size_t)(b + i) * E + tid];
 #pragma unroll
-        for (int q = 0; q < kPrefetch; ++q) {
-            if (base + q * kWave >= p1) break;            // uniform: past this wave's pairs
-            const int p = base + q * kWave + lane;
-            const bool valid = p < p1;
-            const int e = ev[q];
-            const uint64_t peers = match_peers(e, valid, nbits);
-            const int rank = __popcll(peers & lt_mask);
-            const int pos = valid ? my[e] + rank : 0;
-            if (valid) {
-                sorted[pos] = p;
-                sorted_w[pos] = wv[q];
-                inverse[p] = pos;
+            for (int i = 0; i < 8; ++i) {
+                part[(size_t)(b + i) * E + tid] = run;
+                run += v[i];
             }
-            if (valid && rank == 0) my[e] += __popcll(peers);
+        }
+        for (; b < ntiles; ++b) {
+            const int v = part[(size_t)b * E + tid];
+            part[(size_t)b * E + tid] = run;
+            run += v;
+        }
+        counts[tid] = run;
+    } else if (tid < E4) {
+        counts[tid] = 0;
+    }
+    __syncthreads();
+    const int excl = expert_lists(counts, act, wsum, E, dm.P, chunk_rows, offsets, active, chunks, nchunks);
+    if (tid < E)
+        for (int b = 0; b < ntiles; ++b) part[(size_t)b * E + tid] += excl;
+}
+
+__global__ __launch_bounds__(kTileWaves * kWave) void k_sort_scatter(Dims dm, const int32_t* __restrict__ ids,
+                                                                     const float* __restrict__ topk_w,
+                                                                     const int32_t* __restrict__ part,
+                                                                     int32_t* __restrict__ sorted,
+                                                                     float* __restrict__ sorted_w,
+                                                                     int32_t* __restrict__ inverse) {
+    extern __shared__ int32_t sm[];                   // [kTileWaves][E]
+    const int E = dm.E, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    for (int i = tid; i < kTileWaves * E; i += kTileWaves * kWave) sm[i] = 0;
+    __syncthreads();
+    const int nbits = id_bits(E);
+    const int p0 = blockIdx.x * kSortTile + wave * kPrefetch * kWave;
+    const int p1 = min(dm.P, p0 + kPrefetch * kWave);
+    int keep[kPrefetch];
+    float keepw[kPrefetch];
+    int32_t* my = sm + wave * E;
+    wave_pairs(ids, topk_w, p0, p1, nbits, lane, false, keep, keepw,
+               [&](int, bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
+    __syncthreads();
+    // my[w][e] <- first position of wave w's pairs of expert e
+    for (int e = tid; e < E; e += kTileWaves * kWave) {
+        int run = part[(size_t)blockIdx.x * E + e];
+        for (int w = 0; w < kTileWaves; ++w) {
+            const int c = sm[w * E + e];
+            sm[w * E + e] = run;
+            run += c;
         }
     }
+    __syncthreads();
+    wave_pairs(ids, topk_w, p0, p1, nbits, lane, true, keep, keepw,
+               [&](int q, bool valid, int e, int rank, int n, int p) {
+                   if (valid) {
+                       const int pos = my[e] + rank;
+                       sorted[pos] = p;
+                       sorted_w[pos] = keepw[q];
+                       inverse[p] = pos;
+                       if (rank == 0) my[e] += n;
+                   }
+               });
 }
 
 }  // namespace
@@ -348,9 +474,24 @@ hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws
 }
 
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s) {
-    const size_t lds = sizeof(int32_t) * ((size_t)kSortWaves * dm.E + ((dm.E + 3) & ~3) + dm.E + 2 * kSortWaves);
-    hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
-                       ws.sorted_pairs, ws.topk_w, ws.sorted_w, ws.inverse, ws.active, ws.chunks, ws.nchunks, chunk_rows);
+    const size_t E = dm.E, E4 = (E + 3) & ~3;
+    if (dm.P <= kSortSingleMax) {
+        const size_t lds = sizeof(int32_t) * (kSortWaves * E + E4 + E + 2 * kSortWaves);
+        hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
+                           ws.sorted_pairs, ws.topk_w, ws.sorted_w, ws.inverse, ws.active, ws.chunks, ws.nchunks,
+                           chunk_rows);
+        return hipGetLastError();
+    }
+    const int ntiles = sort_tiles(dm.P);
+    const size_t tile_lds = sizeof(int32_t) * kTileWaves * E;
+    hipLaunchKernelGGL(k_sort_hist, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
+                       ws.sort_part);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortThreads), sizeof(int32_t) * (E4 + E + 2 * kSortWaves), s, dm,
+                       ntiles, ws.sort_part, ws.offsets, ws.active, ws.chunks, ws.nchunks, chunk_rows);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
+                       ws.topk_w, ws.sort_part, ws.sorted_pairs, ws.sorted_w, ws.inverse);
     return hipGetLastError();
 }
 

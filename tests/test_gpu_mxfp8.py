@@ -63,7 +63,11 @@ def _run(w, acts, dev, out_dtype, T=None):
     return y.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in r.items()}
 
 
-@pytest.mark.parametrize("T,E,k", [(40, 4, 2), (100, 2, 2), (13, 8, 3)])
+@pytest.mark.parametrize("T,E,k", [
+    (40, 4, 2), (100, 2, 2), (13, 8, 3),
+    (300, 2, 2),              # 300 pairs per expert: two full 128-pair chunks and a 44-pair tail
+    (64, 1, 1),               # one expert, exactly half a chunk
+])
 def test_mxfp8_small_forward(T, E, k):
     moe = _moe()
     w = synth.Workload("mx8", T, 256, 512, E, k, "mxfp8", "none", 90 + T)

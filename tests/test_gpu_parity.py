@@ -160,7 +160,8 @@ def _custom(T, d, f, E, k, seed, logits=None, scale=None):
     return w, acts, wts
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (13, 8, 2), (37, 4, 4), (5, 1, 1), (64, 16, 3)])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (13, 8, 2), (37, 4, 4), (5, 1, 1), (64, 16, 3),
+                                   (1100, 64, 8)])         # 8800 pairs: the tiled sort, last tile partial
 def test_edge_shapes(T, E, k):
     w, acts, wts = _custom(T, 256, 256, E, k, seed=50 + T)
     got, _ = _run(w, acts, problems.to_device(wts))
