@@ -89,6 +89,28 @@ def cpu_baseline(w, acts, ntok):
                       f"fp64 C oracle, OpenMP over tokens; {dt:.2f} s wall"}
 
 
+def measured_traffic(workload, mx8):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy
+    of known size), or None when there is none or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"hbm_traffic_{workload}.md")
+    src = os.path.join(root, "mxfp4_expert_ffn_amd", "csrc", "dense_gemm.hip" if mx8 else "expert_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel source sha256") != digest or "traffic bytes per launch" not in fields:
+        return None
+    return float(fields["traffic bytes per launch"])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,6 +120,9 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated across steps")
     ap.add_argument("--cpu-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the measurements, run a plain device copy (torch.neg, float32) of this many "
+                         "MiB: the reference dispatch for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -166,17 +191,18 @@ def main():
 
     gateup_s = stage_avg_us["gateup"] * 1e-6
     gateup_flops = 2.0 * w.P * 2 * w.d * w.f
+    traffic = measured_traffic(w.name, mx8)
     if mx8:
         achieved = gateup_flops / gateup_s / 1e12
-        roofline = {"bound": "mfma", "kernel": "k_expert<gate/up, MXFP8 x MXFP4>", "achieved": achieved,
+        roofline = {"bound": "mfma", "kernel": "k_dense<gate/up> (MXFP8 x MXFP4 scaled MFMA)", "achieved": achieved,
                     "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MXFP4_PEAK_TFLOPS,
-                    "frac_of_fp8_rate": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                    "frac_of_fp8_rate": achieved / FP8_PEAK_TFLOPS, "traffic": traffic,
                     "algorithmic_flops": gateup_flops}
     else:
         achieved = gateup_bytes / gateup_s / 1e9
         roofline = {"bound": "hbm", "kernel": "k_expert<gate/up>", "achieved": achieved,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                    "traffic": None, "algorithmic_bytes": gateup_bytes}
+                    "traffic": traffic, "algorithmic_bytes": gateup_bytes}
     result = {
         "metric": "MoE expert-layer tokens/s + achieved HBM GB/s (% of peak), 256-token verify",
         "value": w.T / (ms_per_step * 1e-3),
@@ -203,6 +229,14 @@ def main():
         "stage_us": stage_avg_us,
         "roofline": roofline,
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 18                   # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.copy_calibration_mib} MiB read + written, 3 dispatches")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(w, acts, args.cpu_tokens)
