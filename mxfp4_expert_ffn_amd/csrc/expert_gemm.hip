@@ -304,8 +304,9 @@ struct Pipe {
     }
 };
 
+// RT = 4 fits two workgroups per CU (registers), RT = 2 three.
 template <int MODE, int RT, int D>
-__global__ __launch_bounds__(kThreads, 2) void k_expert(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kSlot];
     // Work unit = (chunk, column tile), chunk-major: the column tiles of a
     // chunk (same activation rows) are adjacent.  Chunks are listed expert
@@ -329,13 +330,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_expert(GemmArgs a) {
     }
 }
 
-constexpr int kRtGateUp = 4;     // 2 gate + 2 up tiles per wave: 128 h columns per workgroup
-constexpr int kRtDown = 4;       // 4 tiles per wave: 256 output columns per workgroup
+// Weight tiles per wave.  4 (gate/up: 2 gate + 2 up, 128 h columns per
+// workgroup; down: 256 output columns) normally; 2 when the batch has at most
+// one pair per expert on average: every touched expert is then one small
+// chunk, the grid is about one round of 4-tile workgroups, and the last of
+// them would stream alone -- halving the tile doubles the workgroups.
+inline int tiles_per_wave(const Dims& dm) { return dm.P <= dm.E ? 2 : 4; }
 
 template <int MODE, int RT>
-hipError_t launch(const GemmArgs& a, int max_units, hipStream_t s) {
+hipError_t launch_rt(GemmArgs a, const Dims& dm, hipStream_t s) {
+    a.n_tiles = a.N / (kWaves * (MODE == kGateUp ? RT / 2 : RT) * 16);
     const int nsteps = a.K / kKStep;          // 2 (K = 256) or a multiple of 4
-    const dim3 grid(max_units), block(kThreads);
+    const dim3 grid(max_chunks(dm) * a.n_tiles), block(kThreads);
     if (nsteps % 4 == 0)
         hipLaunchKernelGGL((k_expert<MODE, RT, 4>), grid, block, 0, s, a);
     else
@@ -343,10 +349,12 @@ hipError_t launch(const GemmArgs& a, int max_units, hipStream_t s) {
     return hipGetLastError();
 }
 
-}  // namespace
+template <int MODE>
+hipError_t launch(const GemmArgs& a, const Dims& dm, hipStream_t s) {
+    return tiles_per_wave(dm) == 2 ? launch_rt<MODE, 2>(a, dm, s) : launch_rt<MODE, 4>(a, dm, s);
+}
 
-int gateup_cols_per_block() { return kWaves * (kRtGateUp / 2) * 16; }
-int down_cols_per_block() { return kWaves * kRtDown * 16; }
+}  // namespace
 
 hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm,
                          const Workspace& ws, hipStream_t s) {
@@ -357,9 +365,9 @@ hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Di
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.sorted_w = ws.sorted_w;
     a.h_out = ws.h; a.o_out = nullptr;
-    a.K = dm.d; a.N = dm.f; a.n_tiles = dm.f / gateup_cols_per_block();
+    a.K = dm.d; a.N = dm.f;
     a.k_top = dm.k; a.ldo = dm.f;
-    return launch<kGateUp, kRtGateUp>(a, max_chunks(dm) * a.n_tiles, s);
+    return launch<kGateUp>(a, dm, s);
 }
 
 hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, hipStream_t s) {
@@ -370,9 +378,9 @@ hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspa
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.sorted_w = ws.sorted_w;
     a.h_out = nullptr; a.o_out = ws.o;
-    a.K = dm.f; a.N = dm.d; a.n_tiles = dm.d / down_cols_per_block();
+    a.K = dm.f; a.N = dm.d;
     a.k_top = dm.k; a.ldo = dm.d;
-    return launch<kDown, kRtDown>(a, max_chunks(dm) * a.n_tiles, s);
+    return launch<kDown>(a, dm, s);
 }
 
 }  // namespace moe
