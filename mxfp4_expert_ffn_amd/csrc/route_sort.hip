@@ -213,14 +213,16 @@ __device__ __forceinline__ int id_bits(int E) {
 // with their number at active[E], and the chunk records, expert by expert in
 // that order, with their number.  Returns the exclusive offset of expert
 // `threadIdx.x` (0 past E).  LDS: act[E] + 32 ints of scratch.
-__device__ int expert_lists(const int32_t* counts, int32_t* act, int32_t* wsum, int E, int P, int chunk_rows,
+__device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act, int32_t* wsum, int E, int P,
+                            int chunk_rows,
                             int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                             int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     int32_t* wsum2 = wsum + kSortWaves;
-    const int E4 = (E + 3) & ~3;
-    // exclusive scan of counts over experts (E <= 512 <= 1024 threads)
+    // exclusive scan of counts over experts (E <= 512 <= 1024 threads), and
+    // each expert's unique ranking key: pair count, then lower index first
     const int c = tid < E ? counts[tid] : 0;
+    if (tid < E) keys[tid] = ((uint64_t)(uint32_t)c << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)tid);
     const int incl = wave_inclusive_scan(c, lane);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
@@ -230,16 +232,11 @@ __device__ int expert_lists(const int32_t* counts, int32_t* act, int32_t* wsum, 
     if (tid < E) {
         offsets[tid] = excl;
         if (c > 0) {
+            // rank = number of experts whose key is larger
+            const uint64_t mine = keys[tid];
             int r = 0;
-            const int4* c4 = reinterpret_cast<const int4*>(counts);
-            for (int q = 0; q < E4 / 4; ++q) {
-                const int4 cc = c4[q];
-                const int e2 = 4 * q;
-                r += (cc.x > c) || (cc.x == c && e2 < tid);
-                r += (cc.y > c) || (cc.y == c && e2 + 1 < tid);
-                r += (cc.z > c) || (cc.z == c && e2 + 2 < tid);
-                r += (cc.w > c) || (cc.w == c && e2 + 3 < tid);
-            }
+#pragma unroll 8
+            for (int e2 = 0; e2 < E; ++e2) r += keys[e2] > mine;
             active[r] = tid;
             act[r] = tid;
         }
@@ -289,9 +286,11 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
                                                        int32_t* __restrict__ active,
                                                        int32_t* __restrict__ chunks,
                                                        int32_t* __restrict__ nchunks, int chunk_rows) {
-    extern __shared__ int32_t sm[];
+    extern __shared__ uint64_t sm64[];
     const int E = dm.E, P = dm.P;
     const int E4 = (E + 3) & ~3;
+    uint64_t* keys = sm64;                            // [E]
+    int32_t* sm = reinterpret_cast<int32_t*>(sm64 + E);
     int32_t* hist = sm;                               // [kSortWaves][E]
     int32_t* counts = sm + kSortWaves * E;            // [E4], zero past E
     int32_t* act = counts + E4;                       // [E] active experts in rank order
@@ -329,7 +328,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     }
     if (tid >= E && tid < E4) counts[tid] = 0;
     __syncthreads();
-    const int excl = expert_lists(counts, act, wsum, E, P, chunk_rows, offsets, active, chunks, nchunks);
+    const int excl = expert_lists(counts, keys, act, wsum, E, P, chunk_rows, offsets, active, chunks, nchunks);
     if (tid < E)
         for (int w = 0; w < kSortWaves; ++w) hist[w * E + tid] += excl;
     __syncthreads();
@@ -383,8 +382,10 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles,
                                                             int32_t* __restrict__ active,
                                                             int32_t* __restrict__ chunks,
                                                             int32_t* __restrict__ nchunks, int chunk_rows) {
-    extern __shared__ int32_t sm[];
+    extern __shared__ uint64_t sm64[];
     const int E = dm.E, E4 = (E + 3) & ~3, tid = threadIdx.x;
+    uint64_t* keys = sm64;                            // [E]
+    int32_t* sm = reinterpret_cast<int32_t*>(sm64 + E);
     int32_t* counts = sm;                             // [E4]
     int32_t* act = counts + E4;                       // [E]
     int32_t* wsum = act + E;                          // [32]
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles,
         counts[tid] = 0;
     }
     __syncthreads();
-    const int excl = expert_lists(counts, act, wsum, E, dm.P, chunk_rows, offsets, active, chunks, nchunks);
+    const int excl = expert_lists(counts, keys, act, wsum, E, dm.P, chunk_rows, offsets, active, chunks, nchunks);
     if (tid < E)
         for (int b = 0; b < ntiles; ++b) part[(size_t)b * E + tid] += excl;
 }
@@ -476,7 +477,7 @@ hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s) {
     const size_t E = dm.E, E4 = (E + 3) & ~3;
     if (dm.P <= kSortSingleMax) {
-        const size_t lds = sizeof(int32_t) * (kSortWaves * E + E4 + E + 2 * kSortWaves);
+        const size_t lds = sizeof(uint64_t) * E + sizeof(int32_t) * (kSortWaves * E + E4 + E + 2 * kSortWaves);
         hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
                            ws.sorted_pairs, ws.topk_w, ws.sorted_w, ws.inverse, ws.active, ws.chunks, ws.nchunks,
                            chunk_rows);
@@ -487,7 +488,7 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
     hipLaunchKernelGGL(k_sort_hist, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
                        ws.sort_part);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortThreads), sizeof(int32_t) * (E4 + E + 2 * kSortWaves), s, dm,
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortThreads), sizeof(uint64_t) * E + sizeof(int32_t) * (E4 + E + 2 * kSortWaves), s, dm,
                        ntiles, ws.sort_part, ws.offsets, ws.active, ws.chunks, ws.nchunks, chunk_rows);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
