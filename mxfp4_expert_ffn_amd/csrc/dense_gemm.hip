@@ -14,26 +14,27 @@
 //
 // Work unit = (chunk of <= 128 pairs of one expert, 256 weight rows).  Both
 // operands of a 128-wide K step go through LDS by direct-to-LDS buffer
-// loads into a ring of 4 step buffers, so the loads of a step are issued 3
-// steps before it computes (a weight tile read for the first time comes
-// from HBM, slower than one step): 16 KB of E4M3 rows (16-byte chunks
-// XOR-swizzled by row, so the operand reads are free of bank conflicts) and
-// 16 KB of FP4 weight tiles in their stored order, which is already the
-// B-operand order of the matrix core (lane L: weight row L%16, MX block
-// L/16).  Scales go through LDS once per 4 steps: 4 KB of weight scales (the
-// stored dword of a lane holds its 4 steps; the MFMA's op_sel picks the
-// step's byte) and 2 KB of activation scales.  140 KB of LDS: one workgroup
-// of 8 wavefronts per CU, two per SIMD.
+// loads into two step buffers (the loads of step s+1 are issued when step s
+// starts): 16 KB of E4M3 rows (16-byte chunks XOR-swizzled by row, so the
+// operand reads are free of bank conflicts) and 16 KB of FP4 weight tiles in
+// their stored order, which is already the B-operand order of the matrix
+// core (lane L: weight row L%16, MX block L/16).  Scales go through LDS once
+// per 4 steps: 4 KB of weight scales (the stored dword of a lane holds its 4
+// steps; the MFMA's op_sel picks the step's byte) and 2 KB of activation
+// scales.  76 KB of LDS per workgroup of 4 wavefronts: two workgroups per CU,
+// so one's barrier and load waits overlap the other's MFMAs.
 //
-// The 8 wavefronts form a 2 x 4 grid; each computes 64 pairs x 64 weight
-// rows (4 x 4 MFMA tiles).  Sharing both operands through LDS halves the
-// L2-to-CU bytes per MFMA against streaming the weights into each wave's
-// registers, which is what the verify-batch kernels do.
+// The 4 wavefronts form a 2 x 2 grid; each computes 64 pairs x 128 weight
+// rows (4 x 8 MFMA tiles, 32 accumulators).  Sharing both operands through
+// LDS halves the L2-to-CU bytes per MFMA against streaming the weights into
+// each wave's registers, which is what the verify-batch kernels do.  The
+// shape and ring depth are template parameters (Shape<WN, STAGES>); the
+// other shapes tried were slower on this GPU.
 //
 // Gate/up: weight rows 0..127 of a unit are W_gate rows (h columns), 128..255
-// the W_up rows of the same columns, and a wave's tiles j and j + 2 meet in
-// one lane, so SwiGLU and the MXFP8 re-quantisation of h (a wave row's 32
-// columns are one MX block) run in the epilogue.  Down: the epilogue
+// the W_up rows of the same columns, and a wave's tiles j and j + kJ/2 meet
+// in one lane, so SwiGLU and the MXFP8 re-quantisation of h (each run of 32
+// h columns is one MX block) run in the epilogue.  Down: the epilogue
 // multiplies by the pair's routing weight and stores float32 per pair.
 #include "common.hpp"
 
@@ -373,16 +374,11 @@ int max_dense_chunks(const Dims& dm) {
     return active + dm.P / kDenseChunk;
 }
 
-#ifndef DENSE_WN
-#define DENSE_WN 2
-#endif
-#ifndef DENSE_STAGES
-#define DENSE_STAGES 2
-#endif
-
+// 2 x 2 wavefronts, two step buffers: the fastest shape measured (2 x 4
+// wavefronts and 3- or 4-deep rings leave one workgroup per CU).
 template <int MODE>
 hipError_t launch(const DenseArgs& a, int units, hipStream_t s) {
-    constexpr int WN = DENSE_WN, ST = DENSE_STAGES;
+    constexpr int WN = 2, ST = 2;
     hipLaunchKernelGGL((k_dense<MODE, WN, ST>), dim3(units), dim3(Shape<WN, ST>::kT), 0, s, a);
     return hipGetLastError();
 }
