@@ -88,7 +88,8 @@ typedef struct {
     int32_t d_ff;            /* f, 256 or a multiple of 512                     */
     int32_t top_k;           /* k, 1..min(E, 32)                                */
     int32_t max_tokens;      /* upper bound of num_tokens per forward call, >= 1 */
-    int32_t act_mode;        /* moe_act_mode (MXFP8: d_model, d_ff <= 8192)     */
+    int32_t act_mode;        /* moe_act_mode; MXFP8 needs max_tokens*d and
+                                max_tokens*k*f below 2^32                       */
     int32_t out_dtype;       /* moe_out_dtype                                   */
     uint32_t flags;          /* reserved, must be 0                             */
 } moe_mxfp4_config;

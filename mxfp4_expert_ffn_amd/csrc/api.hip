@@ -75,8 +75,11 @@ moe_status check_config(const moe_mxfp4_config* c) {
         if (K != 256 && K % 512 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->max_tokens * c->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->d_model * c->d_ff > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
-    // MXFP8 mode keeps a chunk's activation scales (K/32 bytes per row) in LDS
-    if (c->act_mode == MOE_ACT_MXFP8_E4M3 && (c->d_model > 8192 || c->d_ff > 8192))
+    // MXFP8 activation codes (x: T x d bytes, h: P x f bytes) are read through
+    // buffer resources, whose offsets and record counts are 32-bit
+    if (c->act_mode == MOE_ACT_MXFP8_E4M3 &&
+        ((int64_t)c->max_tokens * c->d_model >= (int64_t)1 << 32 ||
+         (int64_t)c->max_tokens * c->top_k * c->d_ff >= (int64_t)1 << 32))
         return MOE_ERR_UNSUPPORTED_SHAPE;
     return MOE_OK;
 }

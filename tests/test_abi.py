@@ -60,7 +60,11 @@ def _create(**kw):
     (dict(d_model=-256), 1), (dict(flags=1), 1), (dict(act_mode=7), 1), (dict(out_dtype=3), 1),
     (dict(top_k=5), 2), (dict(num_experts=513, top_k=2), 2), (dict(num_experts=64, top_k=33), 2),
     (dict(d_model=288), 2), (dict(d_ff=384), 2),
-    (dict(act_mode=1), 0), (dict(act_mode=1, d_model=8704), 2),
+    (dict(act_mode=1), 0), (dict(act_mode=1, d_model=8704), 0), (dict(act_mode=1, d_model=8448), 2),
+    # MXFP8 codes are addressed with 32-bit offsets: P x f and T x d below 2^32
+    (dict(max_tokens=1 << 20, d_ff=2048), 0), (dict(act_mode=1, max_tokens=1 << 20, d_ff=2048), 2),
+    (dict(act_mode=1, max_tokens=(1 << 20) - 1, d_ff=2048), 0),
+    (dict(act_mode=1, max_tokens=1 << 20, top_k=1, d_model=4096, d_ff=256), 2),
 ])
 def test_create_validation(kw, status):
     ptrs = kw.pop("ptrs", None)
