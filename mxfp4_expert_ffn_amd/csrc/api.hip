@@ -32,7 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t ids, w, offsets, sorted, sorted_w, inverse, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, total;
+    size_t ids, w, offsets, sorted, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
@@ -43,8 +43,6 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     L.w = at;       at += round256(P * sizeof(float));
     L.offsets = at; at += round256((size_t)(c.num_experts + 1) * sizeof(int32_t));
     L.sorted = at;  at += round256(P * sizeof(int32_t));
-    L.sorted_w = at; at += round256(P * sizeof(float));
-    L.inverse = at; at += round256(P * sizeof(int32_t));
     L.active = at;  at += round256((size_t)(c.num_experts + 1) * sizeof(int32_t));
     moe::Dims dm{(int32_t)T, c.d_model, c.d_ff, c.num_experts, c.top_k, (int32_t)P};
     L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * moe::kChunkRec * sizeof(int32_t));
@@ -205,8 +203,6 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     ws.topk_w = reinterpret_cast<float*>(base + L.w);
     ws.offsets = reinterpret_cast<int32_t*>(base + L.offsets);
     ws.sorted_pairs = reinterpret_cast<int32_t*>(base + L.sorted);
-    ws.sorted_w = reinterpret_cast<float*>(base + L.sorted_w);
-    ws.inverse = reinterpret_cast<int32_t*>(base + L.inverse);
     ws.active = reinterpret_cast<int32_t*>(base + L.active);
     ws.chunks = reinterpret_cast<int32_t*>(base + L.chunks);
     ws.nchunks = reinterpret_cast<int32_t*>(base + L.nchunks);

@@ -2,10 +2,11 @@
 // helper kernels that sit beside the forward path (decode export, weight
 // quantiser).
 //
-// Combine: y[t] = sum_j w[t][j] * o[t][j]; the down projection has already
-// multiplied each pair's output by its routing weight, so this sums the k
-// rows of a token in slot order j = 0..k-1 (fixed order: deterministic) and
-// rounds once to the output type.
+// Combine: y[t] = sum_j w[t][j] * o[t][j].  The down projection stores the
+// output of pair p = t*k + j at row p, so a token's k rows form one
+// contiguous block.  Each product is rounded to float32 on its own (no fused
+// multiply-add), the k products are added in slot order j = 0..k-1 (fixed
+// order: deterministic), and the sum is rounded once to the output type.
 #include "common.hpp"
 
 namespace moe {
@@ -18,37 +19,36 @@ constexpr int kThreads = 256;
 // once, so they bypass the caches' retention).
 template <int KK>
 __global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const float* __restrict__ o,
-                                                       const int32_t* __restrict__ inverse,
+                                                       const float* __restrict__ topk_w,
                                                        void* __restrict__ out, int out_dtype) {
+#pragma clang fp contract(off)
     const int q = dm.d / 4;
     const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= (size_t)dm.T * q) return;
     const int t = (int)(gid / q), c = (int)(gid % q) * 4;
     const int k = KK > 0 ? KK : dm.k;
+    const float* ot = o + (size_t)t * k * dm.d + c;
+    const float* wt = topk_w + (size_t)t * k;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KK > 0) {
-        f32x4_t v[KK];
+        static_assert(KK % 4 == 0, "weights are read 4 at a time");
+        f32x4_t v[KK], w4[KK / 4];
 #pragma unroll
-        for (int j = 0; j < KK; ++j) {
-            const size_t row = (size_t)inverse[(size_t)t * KK + j];
-            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(o + row * dm.d + c));
-        }
+        for (int j = 0; j < KK; ++j)
+            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ot + (size_t)j * dm.d));
 #pragma unroll
-        for (int j = 0; j < KK; ++j) acc += v[j];
+        for (int j = 0; j < KK / 4; ++j) w4[j] = reinterpret_cast<const f32x4_t*>(wt)[j];
+#pragma unroll
+        for (int j = 0; j < KK; ++j) acc += w4[j / 4][j % 4] * v[j];
     } else {
-        for (int j = 0; j < k; ++j) {
-            const size_t row = (size_t)inverse[(size_t)t * k + j];
-            acc += *reinterpret_cast<const f32x4_t*>(o + row * dm.d + c);
-        }
+        for (int j = 0; j < k; ++j) acc += wt[j] * *reinterpret_cast<const f32x4_t*>(ot + (size_t)j * dm.d);
     }
     if (out_dtype == MOE_OUT_F32) {
         *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + (size_t)t * dm.d + c) = acc;
     } else {
         const uint32_t lo = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
         const uint32_t hi = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + (size_t)t * dm.d + c);
-        dst[0] = lo;
-        dst[1] = hi;
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * dm.d + c) = make_uint2(lo, hi);
     }
 }
 
@@ -165,9 +165,9 @@ hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int o
     const size_t n = (size_t)dm.T * (dm.d / 4);
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads)), block(kThreads);
     if (dm.k == 8)
-        hipLaunchKernelGGL(k_finalize<8>, grid, block, 0, s, dm, ws.o, ws.inverse, out, out_dtype);
+        hipLaunchKernelGGL(k_finalize<8>, grid, block, 0, s, dm, ws.o, ws.topk_w, out, out_dtype);
     else
-        hipLaunchKernelGGL(k_finalize<0>, grid, block, 0, s, dm, ws.o, ws.inverse, out, out_dtype);
+        hipLaunchKernelGGL(k_finalize<0>, grid, block, 0, s, dm, ws.o, ws.topk_w, out, out_dtype);
     return hipGetLastError();
 }
 

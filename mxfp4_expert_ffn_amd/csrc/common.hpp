@@ -90,8 +90,6 @@ struct Workspace {
     float* topk_w;            // [P]
     int32_t* offsets;         // [E+1]
     int32_t* sorted_pairs;    // [P]
-    float* sorted_w;          // [P]   routing weight of sorted_pairs[i]
-    int32_t* inverse;         // [P]   position of pair p in sorted_pairs
     int32_t* active;          // [E+1] active experts (count > 0) by descending count; [E] = how many
     int32_t* chunks;          // [max_chunks][4] (expert, first pair within the expert,
                               //   first chunk of the expert, number of chunks of the expert)
@@ -101,7 +99,7 @@ struct Workspace {
     uint8_t* xs;              // MXFP8 mode: [T][d/32] E8M0 scales of x
     uint8_t* h;               // [P][f] bf16 (or E4M3 codes in MXFP8 mode), rows in sorted order
     uint8_t* hs;              // MXFP8 mode: [P][f/32] E8M0 scales of h
-    float* o;                 // [P][d] weighted expert outputs, rows in sorted order
+    float* o;                 // [P][d] expert outputs, row p = pair p (token-major)
 };
 
 // Problem description passed by value to kernels.

@@ -34,8 +34,9 @@
 // Gate/up: weight rows 0..127 of a unit are W_gate rows (h columns), 128..255
 // the W_up rows of the same columns, and a wave's tiles j and j + kJ/2 meet
 // in one lane, so SwiGLU and the MXFP8 re-quantisation of h (each run of 32
-// h columns is one MX block) run in the epilogue.  Down: the epilogue
-// multiplies by the pair's routing weight and stores float32 per pair.
+// h columns is one MX block) run in the epilogue.  Down: the epilogue stores
+// each float32 result row at its pair's own row p = t*k + j (the combine
+// applies the routing weights).
 #include "common.hpp"
 
 namespace moe {
@@ -64,10 +65,9 @@ struct DenseArgs {
     const int32_t* sorted;       // [P]
     const int32_t* chunks;       // chunk records
     const int32_t* nchunks;
-    const float* sorted_w;       // [P] routing weight of each sorted pair
     uint8_t* h_out;              // gate/up: [P][f] E4M3
     uint8_t* h_scale_out;        // gate/up: [P][f/32]
-    float* o_out;                // down: [P][d]
+    float* o_out;                // down: [P][d], row = pair index
     int32_t K, N, n_tiles, k_top, ldo;
 };
 
@@ -284,15 +284,15 @@ struct Dense {
 #pragma unroll
             for (int jj = 0; jj < kJ; ++jj) acc[ms][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         uint32_t sbw[kJ];
-        // down: routing weights of this lane's output rows, loaded before the
-        // main loop so that the epilogue does not wait on them
-        float wr[kMs][4];
+        // down: pair indices (output rows) of this lane's rows, loaded
+        // before the main loop so that the epilogue does not wait on them
+        int32_t pr[kMs][4];
         if constexpr (MODE == kDown) {
 #pragma unroll
             for (int ms = 0; ms < kMs; ++ms)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    wr[ms][r] = a.sorted_w[m0 + min(c0 + wm * 64 + ms * 16 + 4 * g + r, M - 1)];
+                    pr[ms][r] = a.sorted[m0 + min(c0 + wm * 64 + ms * 16 + 4 * g + r, M - 1)];
         }
 
         // prologue: steps 0 .. STAGES-2, the first group's scales first
@@ -316,8 +316,8 @@ struct Dense {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int idx = c0 + wm * 64 + ms * 16 + 4 * g + r;
-                const size_t orow = (size_t)(m0 + idx);
                 if constexpr (MODE == kGateUp) {
+                    const size_t orow = (size_t)(m0 + idx);
                     // the wave's h columns: kJ/2 tiles of 16, MX blocks of 2 tiles
                     constexpr int h = kJ / 2;
                     const int col0 = nt * 128 + wn * h * 16;
@@ -339,10 +339,9 @@ struct Dense {
                     }
                 } else {
                     if (idx < M) {
-                        const float wgt = wr[ms][r];
-                        float* orow_p = a.o_out + orow * a.ldo + nt * 256 + wn * kJ * 16 + li;
+                        float* orow_p = a.o_out + (size_t)pr[ms][r] * a.ldo + nt * 256 + wn * kJ * 16 + li;
 #pragma unroll
-                        for (int jj = 0; jj < kJ; ++jj) __builtin_nontemporal_store(wgt * acc[ms][jj][r], orow_p + jj * 16);
+                        for (int jj = 0; jj < kJ; ++jj) __builtin_nontemporal_store(acc[ms][jj][r], orow_p + jj * 16);
                     }
                 }
             }
@@ -391,7 +390,6 @@ hipError_t launch_gateup_dense(const moe_mxfp4_weights& w, const Dims& dm, const
     a.w0 = w.w_gate; a.s0 = w.w_gate_scale;
     a.w1 = w.w_up;   a.s1 = w.w_up_scale;
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
-    a.sorted_w = ws.sorted_w;
     a.h_out = ws.h; a.h_scale_out = ws.hs; a.o_out = nullptr;
     a.K = dm.d; a.N = dm.f; a.n_tiles = dm.f / 128; a.k_top = dm.k; a.ldo = dm.f;
     return launch<kGateUp>(a, max_dense_chunks(dm) * a.n_tiles, s);
@@ -403,7 +401,6 @@ hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const W
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
-    a.sorted_w = ws.sorted_w;
     a.h_out = nullptr; a.h_scale_out = nullptr; a.o_out = ws.o;
     a.K = dm.f; a.N = dm.d; a.n_tiles = dm.d / 256; a.k_top = dm.k; a.ldo = dm.d;
     return launch<kDown>(a, max_dense_chunks(dm) * a.n_tiles, s);

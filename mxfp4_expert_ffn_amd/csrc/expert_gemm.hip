@@ -35,9 +35,10 @@
 //   Gate/up: tiles 0..RT/2-1 come from W_gate and RT/2.. from W_up, so the
 //   gate and up accumulators of a (token, column) sit in the same lane and
 //   SwiGLU h = silu(g) * u runs in the epilogue; h is stored in bf16, rows in
-//   expert-sorted order.  Down: A = those h rows; the epilogue multiplies by
-//   the pair's routing weight and stores float32 per pair (combined later in
-//   a fixed order, so the result is deterministic).
+//   expert-sorted order.  Down: A = those h rows; the epilogue stores each
+//   float32 result row at its pair's own row p = t*k + j, so that the
+//   combine (routing weights, k-slot sum in a fixed order, hence
+//   deterministic) reads every token's k rows as one contiguous block.
 //
 // Memory ordering is explicit: the loads are always issued in the same order
 // (prologue: weights of steps 0..D-2, activations of step 0, weights of step
@@ -69,9 +70,8 @@ struct GemmArgs {
     const int32_t* sorted;      // [P]
     const int32_t* chunks;      // chunk records
     const int32_t* nchunks;     // device count of chunks
-    const float* sorted_w;      // [P] routing weight of each sorted pair
     uint8_t* h_out;             // gate/up: h [P][f] bf16
-    float* o_out;               // down: [P][d]
+    float* o_out;               // down: [P][d], row = pair index
     int32_t K;                  // reduction length
     int32_t N;                  // rows per weight matrix
     int32_t n_tiles;            // column tiles per expert
@@ -236,14 +236,14 @@ struct Pipe {
             const int lchunk = swz(r, lane % kChunksPerRow);
             c.xoff[q] = (uint32_t)src_row(r) * (uint32_t)(a.K * 2) + (uint32_t)(lchunk * 16);
         }
-        // down: routing weights of this lane's output rows, loaded up front
-        // so that the epilogue does not wait on them
-        float wr[MS][4];
+        // down: pair indices (output rows) of this lane's rows, loaded up
+        // front so that the epilogue does not wait on them
+        int32_t pr[MS][4];
         if constexpr (MODE == kDown) {
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) wr[ms][r] = a.sorted_w[m0 + min(c0 + ms * 16 + 4 * g + r, M - 1)];
+                for (int r = 0; r < 4; ++r) pr[ms][r] = a.sorted[m0 + min(c0 + ms * 16 + 4 * g + r, M - 1)];
         }
 
         f32x4_t acc[MS][RT];
@@ -284,9 +284,9 @@ struct Pipe {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int idx = c0 + ms * 16 + 4 * g + r;
-                const size_t orow = (size_t)(m0 + idx);
                 if (idx < M) {
                     if constexpr (MODE == kGateUp) {
+                        const size_t orow = (size_t)(m0 + idx);
                         uint16_t* h = reinterpret_cast<uint16_t*>(a.h_out);
 #pragma unroll
                         for (int rt = 0; rt < RT / 2; ++rt) {
@@ -294,9 +294,9 @@ struct Pipe {
                             h[orow * a.ldo + col0 + rt * 16 + li] = f32_to_bf16_rne(hv);
                         }
                     } else {
+                        const size_t orow = (size_t)pr[ms][r];
 #pragma unroll
-                        for (int rt = 0; rt < RT; ++rt)
-                            a.o_out[orow * a.ldo + col0 + rt * 16 + li] = wr[ms][r] * acc[ms][rt][r];
+                        for (int rt = 0; rt < RT; ++rt) a.o_out[orow * a.ldo + col0 + rt * 16 + li] = acc[ms][rt][r];
                     }
                 }
             }
@@ -363,7 +363,6 @@ hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Di
     a.w0 = w.w_gate; a.s0 = w.w_gate_scale;
     a.w1 = w.w_up;   a.s1 = w.w_up_scale;
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
-    a.sorted_w = ws.sorted_w;
     a.h_out = ws.h; a.o_out = nullptr;
     a.K = dm.d; a.N = dm.f;
     a.k_top = dm.k; a.ldo = dm.f;
@@ -376,7 +375,6 @@ hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspa
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
     a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
-    a.sorted_w = ws.sorted_w;
     a.h_out = nullptr; a.o_out = ws.o;
     a.K = dm.f; a.N = dm.d;
     a.k_top = dm.k; a.ldo = dm.d;

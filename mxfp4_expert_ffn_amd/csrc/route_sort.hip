@@ -172,14 +172,13 @@ __device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) 
 }
 
 // Visit the pairs [p0, p1) of one wave in ascending order, kPrefetch rounds
-// of 64 at a time (their id loads overlap), and call f(q, valid, e, rank,
+// of 64 at a time (their id loads overlap), and call f(valid, e, rank,
 // peers, p) per lane and pair: rank = lanes of this round before it with the
-// same expert, peers = those lanes' mask.  keep/keepw: the round's ids and
-// weights, reused instead of reloading when `reuse` (one round per wave).
+// same expert, peers = those lanes' mask.  keep: the round's ids, reused
+// instead of reloading when `reuse` (one round per wave).
 template <typename F>
-__device__ __forceinline__ void wave_pairs(const int32_t* __restrict__ ids, const float* __restrict__ topk_w,
-                                           int p0, int p1, int nbits, int lane, bool reuse, int (&keep)[kPrefetch],
-                                           float (&keepw)[kPrefetch], F&& f) {
+__device__ __forceinline__ void wave_pairs(const int32_t* __restrict__ ids, int p0, int p1, int nbits, int lane,
+                                           bool reuse, int (&keep)[kPrefetch], F&& f) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     for (int base = p0; base < p1; base += kPrefetch * kWave) {
         if (!reuse) {
@@ -187,7 +186,6 @@ __device__ __forceinline__ void wave_pairs(const int32_t* __restrict__ ids, cons
             for (int q = 0; q < kPrefetch; ++q) {
                 const int p = base + q * kWave + lane;
                 keep[q] = p < p1 ? ids[p] : 0;
-                keepw[q] = (topk_w != nullptr && p < p1) ? topk_w[p] : 0.0f;
             }
         }
 #pragma unroll
@@ -196,7 +194,7 @@ __device__ __forceinline__ void wave_pairs(const int32_t* __restrict__ ids, cons
             const int p = base + q * kWave + lane;
             const bool valid = p < p1;
             const uint64_t peers = match_peers(keep[q], valid, nbits);
-            f(q, valid, keep[q], __popcll(peers & lt_mask), __popcll(peers), p);
+            f(valid, keep[q], __popcll(peers & lt_mask), __popcll(peers), p);
         }
     }
 }
@@ -280,9 +278,6 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
 __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ sorted,
-                                                       const float* __restrict__ topk_w,
-                                                       float* __restrict__ sorted_w,
-                                                       int32_t* __restrict__ inverse,
                                                        int32_t* __restrict__ active,
                                                        int32_t* __restrict__ chunks,
                                                        int32_t* __restrict__ nchunks, int chunk_rows) {
@@ -309,11 +304,10 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     // for the scatter instead of loading them again
     const bool one_round = per_wave <= kPrefetch * kWave;
     int keep[kPrefetch];
-    float keepw[kPrefetch];
 
     // 1) per-wave histograms
-    wave_pairs(ids, topk_w, p0, p1, nbits, lane, false, keep, keepw,
-               [&](int, bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
+    wave_pairs(ids, p0, p1, nbits, lane, false, keep,
+               [&](bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
     __syncthreads();
 
     // 2) per-expert totals; hist[w][e] becomes the count of waves before w
@@ -334,13 +328,10 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     __syncthreads();
 
     // 3) scatter in the same visiting order: stable within each expert
-    wave_pairs(ids, topk_w, p0, p1, nbits, lane, one_round, keep, keepw,
-               [&](int q, bool valid, int e, int rank, int n, int p) {
+    wave_pairs(ids, p0, p1, nbits, lane, one_round, keep,
+               [&](bool valid, int e, int rank, int n, int p) {
                    if (valid) {
-                       const int pos = my[e] + rank;
-                       sorted[pos] = p;
-                       sorted_w[pos] = keepw[q];
-                       inverse[p] = pos;
+                       sorted[my[e] + rank] = p;
                        if (rank == 0) my[e] += n;
                    }
                });
@@ -365,10 +356,9 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_sort_hist(Dims dm, const
     const int p0 = blockIdx.x * kSortTile + wave * kPrefetch * kWave;
     const int p1 = min(dm.P, p0 + kPrefetch * kWave);
     int keep[kPrefetch];
-    float keepw[kPrefetch];
     int32_t* my = sm + wave * E;
-    wave_pairs(ids, nullptr, p0, p1, id_bits(E), lane, false, keep, keepw,
-               [&](int, bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
+    wave_pairs(ids, p0, p1, id_bits(E), lane, false, keep,
+               [&](bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
     __syncthreads();
     for (int e = tid; e < E; e += kTileWaves * kWave) {
         int c = 0;
@@ -419,11 +409,8 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles,
 }
 
 __global__ __launch_bounds__(kTileWaves * kWave) void k_sort_scatter(Dims dm, const int32_t* __restrict__ ids,
-                                                                     const float* __restrict__ topk_w,
                                                                      const int32_t* __restrict__ part,
-                                                                     int32_t* __restrict__ sorted,
-                                                                     float* __restrict__ sorted_w,
-                                                                     int32_t* __restrict__ inverse) {
+                                                                     int32_t* __restrict__ sorted) {
     extern __shared__ int32_t sm[];                   // [kTileWaves][E]
     const int E = dm.E, tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     for (int i = tid; i < kTileWaves * E; i += kTileWaves * kWave) sm[i] = 0;
@@ -432,10 +419,9 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_sort_scatter(Dims dm, co
     const int p0 = blockIdx.x * kSortTile + wave * kPrefetch * kWave;
     const int p1 = min(dm.P, p0 + kPrefetch * kWave);
     int keep[kPrefetch];
-    float keepw[kPrefetch];
     int32_t* my = sm + wave * E;
-    wave_pairs(ids, topk_w, p0, p1, nbits, lane, false, keep, keepw,
-               [&](int, bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
+    wave_pairs(ids, p0, p1, nbits, lane, false, keep,
+               [&](bool valid, int e, int rank, int n, int) { if (valid && rank == 0) my[e] += n; });
     __syncthreads();
     // my[w][e] <- first position of wave w's pairs of expert e
     for (int e = tid; e < E; e += kTileWaves * kWave) {
@@ -447,13 +433,10 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_sort_scatter(Dims dm, co
         }
     }
     __syncthreads();
-    wave_pairs(ids, topk_w, p0, p1, nbits, lane, true, keep, keepw,
-               [&](int q, bool valid, int e, int rank, int n, int p) {
+    wave_pairs(ids, p0, p1, nbits, lane, true, keep,
+               [&](bool valid, int e, int rank, int n, int p) {
                    if (valid) {
-                       const int pos = my[e] + rank;
-                       sorted[pos] = p;
-                       sorted_w[pos] = keepw[q];
-                       inverse[p] = pos;
+                       sorted[my[e] + rank] = p;
                        if (rank == 0) my[e] += n;
                    }
                });
@@ -479,7 +462,7 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
     if (dm.P <= kSortSingleMax) {
         const size_t lds = sizeof(uint64_t) * E + sizeof(int32_t) * (kSortWaves * E + E4 + E + 2 * kSortWaves);
         hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
-                           ws.sorted_pairs, ws.topk_w, ws.sorted_w, ws.inverse, ws.active, ws.chunks, ws.nchunks,
+                           ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks,
                            chunk_rows);
         return hipGetLastError();
     }
@@ -492,7 +475,7 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
                        ntiles, ws.sort_part, ws.offsets, ws.active, ws.chunks, ws.nchunks, chunk_rows);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
-                       ws.topk_w, ws.sort_part, ws.sorted_pairs, ws.sorted_w, ws.inverse);
+                       ws.sort_part, ws.sorted_pairs);
     return hipGetLastError();
 }
 

@@ -83,6 +83,19 @@ def test_mxfp8_small_forward(T, E, k):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("d,f", [(8704, 512), (512, 8704), (256, 1024)])
+def test_mxfp8_k_extents(d, f):
+    moe = _moe()
+    w = synth.Workload("mx8", 24, d, f, 4, 2, "mxfp8", "none", d + f)
+    acts = synth.make_activations(w)
+    wts = problems.pack_experts(w)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, w.k, act_mode=oracle.ACT_MXFP8)
+    y32, _ = _run(w, acts, problems.to_device(wts), moe.OUT_F32)
+    err = problems.rel_max_err(y32, ref["y"])
+    print(f"mxfp8 d={d} f={f}: f32-out rel max err {err:.3e}")
+    assert err <= TOL
+
+
 def test_chunk_8192_sampled_parity():
     moe = _moe()
     w = synth.workload("chunk_8192")

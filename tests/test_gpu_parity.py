@@ -170,6 +170,18 @@ def test_edge_shapes(T, E, k):
     assert problems.rel_max_err(got["y"], ref) <= TOL
 
 
+@pytest.mark.parametrize("d,f", [(8704, 512), (512, 8704), (256, 1024)])
+def test_k_extents(d, f):
+    # 68 K steps on either projection, and the 2-step (K = 256) pipeline
+    w, acts, wts = _custom(24, d, f, 4, 2, seed=d + f)
+    got, _ = _run(w, acts, problems.to_device(wts))
+    _check_routing(w, acts, got)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, w.k)["y"]
+    err = problems.rel_max_err(got["y"], ref)
+    print(f"bf16 d={d} f={f}: f32-out rel max err {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("T,E,k,coarse", [
     (20, 100, 6, False),      # E not a multiple of 64
     (24, 128, 8, True),       # many exact ties
