@@ -22,9 +22,9 @@
 //   contiguous 1 KB buffer load per tile and step, plus one contiguous
 //   256-byte load of the dword of scales that covers the lane's 4 steps.
 //   Weights run D steps ahead in a register ring (the HBM stream);
-//   activations, which the column tiles of a chunk share through L2, run one
-//   step ahead in a two-slot LDS ring filled by direct-to-LDS loads, in a
-//   layout whose 16-byte chunks are XOR-swizzled by row so that the
+//   activations, which the column tiles of a chunk share through L2, run
+//   D - 1 steps ahead in a D-slot LDS ring filled by direct-to-LDS loads, in
+//   a layout whose 16-byte chunks are XOR-swizzled by row so that the
 //   matrix-core operand reads are free of bank conflicts.
 //
 //   The 32 nibbles of a block feed four v_mfma_f32_16x16x32_bf16 steps; the
@@ -40,12 +40,15 @@
 //   combine (routing weights, k-slot sum in a fixed order, hence
 //   deterministic) reads every token's k rows as one contiguous block.
 //
-// Memory ordering is explicit: the loads are always issued in the same order
-// (prologue: weights of steps 0..D-2, activations of step 0, weights of step
-// D-1; step s: activations of step s+1, then weights of step s+D) and pinned
-// there, so a fixed vmcnt wait before each step's barrier guarantees that
-// the step's data has landed, and the barrier makes every wave's
-// direct-to-LDS writes visible.
+// Memory ordering is explicit.  Vector-memory loads retire in issue order,
+// so waiting for one load waits for every older one; the loads are always
+// issued in the same interleaved order (W_j = weights of step j, X_j =
+// activations of step j: prologue W_0 X_0 W_1 X_1 .. W_{D-2} X_{D-2} W_{D-1};
+// step s: X_{s+D-1}, then W_{s+D}) and pinned there, so a fixed vmcnt wait
+// before each step's barrier guarantees that the step's data has landed
+// while everything issued in the D - 1 steps since stays in flight, and the
+// barrier makes every wave's direct-to-LDS writes visible (and frees the
+// slot the step's own activation load refills).
 #include "common.hpp"
 
 namespace moe {
@@ -173,24 +176,57 @@ struct Pipe {
         }
     }
 
+    // Loads issued after X_s by the time step s starts, R < 0 meaning a step
+    // before the last D and R >= 0 the R-th of them: X_{s+1} .. X_{s+D-2} and
+    // W_{s+1} .. W_{s+D-1}, cut off at the last step.
+    static constexpr int after_x(int R) {
+        const int nw = R < 0 ? D - 1 : D - 1 - R;
+        const int nx = R < 0 ? D - 2 : (D - 1 - R < D - 2 ? D - 1 - R : D - 2);
+        return nx * kNx + nw * kNw;
+    }
+
     // Step s (ring slot SLOT == s mod D, S4 == s mod 4).  R < 0: a step
-    // before the last D, which issues the activations of step s+1 and the
-    // weights of step s+D; R >= 0: one of the last D steps, R steps after it.
-    // The activations of step s were the last load issued before the weights
-    // of step s+D-1 (when those exist: all but the last D-1 steps), and its
-    // weights are older still, so waiting for at most that many outstanding
-    // loads means both have landed.
+    // before the last D, which issues the activations of step s+D-1 into the
+    // slot that step s-1 read and the weights of step s+D; R >= 0: the R-th
+    // (from 0) of the last D steps, of which only the first still has
+    // activations to issue.  X_s is older than the after_x(R) loads issued
+    // since, and W_s older still, so waiting for at most that many
+    // outstanding loads means both have landed.
     template <int SLOT, int S4, int R>
     __device__ static void step(const Ctx& c, f32x4_t (&acc)[MS][RT], u32x4_t (&w)[RT], uint32_t (&sg)[RT], int s,
                                 int li, int g) {
-        step_barrier<(R < 0 || R == D - 1) ? kNw : 0>();
+        step_barrier<after_x(R)>();
         pin();
-        if (R < 0 || R >= 1) issue_x<(S4 + 1) & 1>(c, s + 1);
+        if (R <= 0) issue_x<(SLOT + D - 1) % D>(c, s + D - 1);
         pin();
-        compute<S4>(acc, w, sg, c.lds + (S4 & 1) * kSlot, li, g);
+        compute<S4>(acc, w, sg, c.lds + SLOT * kSlot, li, g);
         pin();
         if (R < 0) issue_w(c, w, sg, s + D);
         pin();
+    }
+
+    // Prologue loads W_J X_J .. W_{D-2} X_{D-2} (compile-time slots).
+    template <int J>
+    __device__ static void prologue(const Ctx& c, u32x4_t (&w)[D][RT], uint32_t (&sg)[D][RT]) {
+        if constexpr (J < D - 1) {
+            issue_w(c, w[J], sg[J], J);
+            pin();
+            issue_x<J>(c, J);
+            pin();
+            prologue<J + 1>(c, w, sg);
+        }
+    }
+
+    // Steps s+J .. s+D-1 of one ring turn (s a multiple of D, and D a
+    // multiple of 4 or D == 2 == n, so s+J == J mod 4); TAIL: the last D
+    // steps of the pass.
+    template <int J, bool TAIL>
+    __device__ static void steps(const Ctx& c, f32x4_t (&acc)[MS][RT], u32x4_t (&w)[D][RT], uint32_t (&sg)[D][RT],
+                                 int s, int li, int g) {
+        if constexpr (J < D) {
+            step<J, J % 4, TAIL ? J : -1>(c, acc, w[J], sg[J], s + J, li, g);
+            steps<J + 1, TAIL>(c, acc, w, sg, s, li, g);
+        }
     }
 
     __device__ static void run(const GemmArgs& a, uint8_t* lds, int e, int nt, int m0, int c0, int M) {
@@ -256,27 +292,13 @@ struct Pipe {
         u32x4_t w[D][RT];
         uint32_t sg[D][RT];
         pin();
-#pragma unroll
-        for (int j = 0; j < D - 1; ++j) {
-            issue_w(c, w[j], sg[j], j);
-            pin();
-        }
-        issue_x<0>(c, 0);
-        pin();
+        prologue<0>(c, w, sg);
         issue_w(c, w[D - 1], sg[D - 1], D - 1);
         pin();
 
         int s = 0;
-        for (; s < n - D; s += D) {
-            step<0, 0, -1>(c, acc, w[0], sg[0], s + 0, li, g);
-            if constexpr (D > 1) step<1 % D, 1, -1>(c, acc, w[1 % D], sg[1 % D], s + 1, li, g);
-            if constexpr (D > 2) step<2 % D, 2, -1>(c, acc, w[2 % D], sg[2 % D], s + 2, li, g);
-            if constexpr (D > 3) step<3 % D, 3, -1>(c, acc, w[3 % D], sg[3 % D], s + 3, li, g);
-        }
-        step<0, 0, D - 1>(c, acc, w[0], sg[0], s + 0, li, g);
-        if constexpr (D > 1) step<1 % D, 1, D - 2>(c, acc, w[1 % D], sg[1 % D], s + 1, li, g);
-        if constexpr (D > 2) step<2 % D, 2, D - 3>(c, acc, w[2 % D], sg[2 % D], s + 2, li, g);
-        if constexpr (D > 3) step<3 % D, 3, D - 4>(c, acc, w[3 % D], sg[3 % D], s + 3, li, g);
+        for (; s < n - D; s += D) steps<0, false>(c, acc, w, sg, s, li, g);
+        steps<0, true>(c, acc, w, sg, s, li, g);
 
         // Epilogue.  Lane holds D[token 4g + r][column li] of every (ms, rt).
 #pragma unroll
@@ -307,7 +329,7 @@ struct Pipe {
 // RT = 4 fits two workgroups per CU (registers), RT = 2 three.
 template <int MODE, int RT, int D>
 __global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kSlot];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[D * kSlot];
     // Work unit = (chunk, column tile), chunk-major: the column tiles of a
     // chunk (same activation rows) are adjacent.  Chunks are listed expert
     // by expert, hottest expert first.  Workgroup-uniform values are kept in
