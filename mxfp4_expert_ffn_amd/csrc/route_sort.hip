@@ -207,12 +207,13 @@ __device__ __forceinline__ int id_bits(int E) {
 
 // From the per-expert pair counts (LDS counts[E4], zero past E) of all P
 // pairs, with every thread of a kSortThreads workgroup: expert offsets
-// [E+1], the active experts by descending count (ties to the lower index)
-// with their number at active[E], and the chunk records, expert by expert in
-// that order, with their number.  Returns the exclusive offset of expert
-// `threadIdx.x` (0 past E).  LDS: act[E] + 32 ints of scratch.
-__device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act, int32_t* wsum, int E, int P,
-                            int chunk_rows,
+// [E+1] (also left in LDS exoff[E]), the active experts by descending count
+// (ties to the lower index) with their number at active[E], and the chunk
+// records, expert by expert in that order, with their number.  Returns the
+// exclusive offset of expert `threadIdx.x` (0 past E).  LDS: keys[E] +
+// act[E] + rnk[E] + exoff[E] + 32 ints of scratch.
+__device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act, int32_t* rnk, int32_t* exoff,
+                            int32_t* wsum, int E, int P, int chunk_rows,
                             int32_t* __restrict__ offsets, int32_t* __restrict__ active,
                             int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -220,7 +221,10 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
     // exclusive scan of counts over experts (E <= 512 <= 1024 threads), and
     // each expert's unique ranking key: pair count, then lower index first
     const int c = tid < E ? counts[tid] : 0;
-    if (tid < E) keys[tid] = ((uint64_t)(uint32_t)c << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)tid);
+    if (tid < E) {
+        keys[tid] = ((uint64_t)(uint32_t)c << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)tid);
+        rnk[tid] = 0;
+    }
     const int incl = wave_inclusive_scan(c, lane);
     if (lane == kWave - 1) wsum[wave] = incl;
     __syncthreads();
@@ -229,14 +233,23 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
     const int excl = before + incl - c;
     if (tid < E) {
         offsets[tid] = excl;
-        if (c > 0) {
-            // rank = number of experts whose key is larger
-            const uint64_t mine = keys[tid];
+        exoff[tid] = excl;
+    }
+    // rank of an active expert = number of experts whose key is larger,
+    // counted in slices: thread (slice j, expert e) compares key e with the
+    // keys of slice j and adds what it finds to rnk[e] (integer adds: the
+    // total does not depend on their order)
+    {
+        const int ep = (E + kWave - 1) / kWave * kWave;    // experts rounded up to whole waves
+        const int nsl = kSortThreads / ep;                  // slices, >= 2 (E <= 512)
+        const int e = tid % ep, j = tid / ep;
+        if (e < E && j < nsl && counts[e] > 0) {
+            const uint64_t mine = keys[e];
+            const int len = (E + nsl - 1) / nsl;
+            const int hi = min(E, (j + 1) * len);
             int r = 0;
-#pragma unroll 8
-            for (int e2 = 0; e2 < E; ++e2) r += keys[e2] > mine;
-            active[r] = tid;
-            act[r] = tid;
+            for (int e2 = j * len; e2 < hi; ++e2) r += keys[e2] > mine;
+            if (r > 0) atomicAdd(&rnk[e], r);
         }
     }
     // number of active experts = number of nonzero counts
@@ -249,10 +262,15 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
         offsets[E] = P;
         active[E] = na;
     }
+    if (tid < E && c > 0) {
+        const int r = rnk[tid];
+        active[r] = tid;
+        act[r] = tid;
+    }
+    __syncthreads();                                   // act[] complete (and wsum's reads done)
     // work chunks of <= chunk_rows pairs, expert by expert in rank order
     const int nch = tid < na ? (counts[act[tid]] + chunk_rows - 1) / chunk_rows : 0;
     const int nincl = wave_inclusive_scan(nch, lane);
-    __syncthreads();                                   // wsum is reused below
     if (lane == kWave - 1) wsum[wave] = nincl;
     __syncthreads();
     int cbefore = 0;
@@ -273,8 +291,9 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
     return tid < E ? excl : 0;
 }
 
-// Single workgroup, up to kSortSingleMax pairs.  LDS: hist[kSortWaves][E] +
-// counts[E rounded up to 4] + act[E] + 32 ints.
+// Single workgroup, up to kSortSingleMax pairs.  LDS: keys[E] (8 bytes) +
+// hist[kSortWaves][E] + counts[E rounded up to 4] + act[E] + rnk[E] +
+// exoff[E] + 32 ints.
 __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ sorted,
@@ -289,7 +308,9 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
     int32_t* hist = sm;                               // [kSortWaves][E]
     int32_t* counts = sm + kSortWaves * E;            // [E4], zero past E
     int32_t* act = counts + E4;                       // [E] active experts in rank order
-    int32_t* wsum = act + E;                          // [32]
+    int32_t* rnk = act + E;                           // [E] their ranks
+    int32_t* exoff = rnk + E;                         // [E] expert offsets
+    int32_t* wsum = exoff + E;                        // [32]
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
     for (int i = tid; i < kSortWaves * E; i += kSortThreads) hist[i] = 0;
@@ -312,26 +333,27 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
 
     // 2) per-expert totals; hist[w][e] becomes the count of waves before w
     for (int e = tid; e < E; e += kSortThreads) {
+        int v[kSortWaves];
+#pragma unroll
+        for (int w = 0; w < kSortWaves; ++w) v[w] = hist[w * E + e];
         int run = 0;
+#pragma unroll
         for (int w = 0; w < kSortWaves; ++w) {
-            const int c = hist[w * E + e];
             hist[w * E + e] = run;
-            run += c;
+            run += v[w];
         }
         counts[e] = run;
     }
     if (tid >= E && tid < E4) counts[tid] = 0;
     __syncthreads();
-    const int excl = expert_lists(counts, keys, act, wsum, E, P, chunk_rows, offsets, active, chunks, nchunks);
-    if (tid < E)
-        for (int w = 0; w < kSortWaves; ++w) hist[w * E + tid] += excl;
-    __syncthreads();
+    expert_lists(counts, keys, act, rnk, exoff, wsum, E, P, chunk_rows, offsets, active, chunks, nchunks);
 
     // 3) scatter in the same visiting order: stable within each expert
+    //    (position = expert offset + pairs of earlier waves and rounds + rank)
     wave_pairs(ids, p0, p1, nbits, lane, one_round, keep,
                [&](bool valid, int e, int rank, int n, int p) {
                    if (valid) {
-                       sorted[my[e] + rank] = p;
+                       sorted[exoff[e] + my[e] + rank] = p;
                        if (rank == 0) my[e] += n;
                    }
                });
@@ -378,7 +400,9 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles,
     int32_t* sm = reinterpret_cast<int32_t*>(sm64 + E);
     int32_t* counts = sm;                             // [E4]
     int32_t* act = counts + E4;                       // [E]
-    int32_t* wsum = act + E;                          // [32]
+    int32_t* rnk = act + E;                           // [E]
+    int32_t* exoff = rnk + E;                         // [E]
+    int32_t* wsum = exoff + E;                        // [32]
     // per expert: exclusive prefix over tiles (tile-major part[b][e])
     if (tid < E) {
         int run = 0;
@@ -403,7 +427,8 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles,
         counts[tid] = 0;
     }
     __syncthreads();
-    const int excl = expert_lists(counts, keys, act, wsum, E, dm.P, chunk_rows, offsets, active, chunks, nchunks);
+    const int excl = expert_lists(counts, keys, act, rnk, exoff, wsum, E, dm.P, chunk_rows, offsets, active, chunks,
+                                  nchunks);
     if (tid < E)
         for (int b = 0; b < ntiles; ++b) part[(size_t)b * E + tid] += excl;
 }
@@ -460,7 +485,7 @@ hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s) {
     const size_t E = dm.E, E4 = (E + 3) & ~3;
     if (dm.P <= kSortSingleMax) {
-        const size_t lds = sizeof(uint64_t) * E + sizeof(int32_t) * (kSortWaves * E + E4 + E + 2 * kSortWaves);
+        const size_t lds = sizeof(uint64_t) * E + sizeof(int32_t) * (kSortWaves * E + E4 + 3 * E + 2 * kSortWaves);
         hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
                            ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks,
                            chunk_rows);
@@ -471,7 +496,7 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
     hipLaunchKernelGGL(k_sort_hist, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
                        ws.sort_part);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortThreads), sizeof(uint64_t) * E + sizeof(int32_t) * (E4 + E + 2 * kSortWaves), s, dm,
+    hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortThreads), sizeof(uint64_t) * E + sizeof(int32_t) * (E4 + 3 * E + 2 * kSortWaves), s, dm,
                        ntiles, ws.sort_part, ws.offsets, ws.active, ws.chunks, ws.nchunks, chunk_rows);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
