@@ -471,8 +471,9 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_sort_scatter(Dims dm, co
 
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s) {
     const int grid = (dm.T + kRouteWaves - 1) / kRouteWaves;
-    // ranking costs E compares per logit: it wins for one logit per lane;
-    // with more, the k argmax rounds are cheaper
+    // ranking costs E compares per logit (each a 4-cycle wave64 VALU op):
+    // it wins for one logit per lane; with two (E <= 128) it already takes
+    // 1.3-1.4x as long as the k argmax rounds
     if (dm.E <= kWave)
         hipLaunchKernelGGL(k_route_rank<1>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
                            ws.topk_ids, ws.topk_w);
