@@ -20,7 +20,6 @@ namespace moe {
 namespace {
 
 constexpr int kRouteWaves = 4;          // tokens per routing workgroup
-constexpr int kMaxPerLane = 8;          // E <= 512
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kPrefetch = 8;            // rounds of pair ids loaded ahead per wave
@@ -95,7 +94,58 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_rank(const float*
     }
 }
 
-// One wavefront per token, any E <= 512.  Lane l holds logits l, l+64, ...
+// (value, expert) order of the routing: larger value first, then the lower
+// expert index; INT_MAX marks an empty candidate, which comes last.
+__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
+    if (oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(float& bv, int& bi) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
+    take_better(bv, bi, ov, oi);
+}
+
+// Every lane ends with the wave-wide best candidate.  Within each row of 16
+// lanes, DPP moves pair lanes 1 apart, then 2 apart (quad permutes), then
+// the two halves of each 8 (half-mirror) and of the row (mirror): after each
+// step both partners hold the better of two groups.  The four row results
+// are then read from lanes 0, 16, 32, 48 and folded in that order.
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+    dpp_step<0xB1>(bv, bi);      // quad_perm [1, 0, 3, 2]
+    dpp_step<0x4E>(bv, bi);      // quad_perm [2, 3, 0, 1]
+    dpp_step<0x141>(bv, bi);     // row_half_mirror
+    dpp_step<0x140>(bv, bi);     // row_mirror
+    float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int ri = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+        take_better(rv, ri, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r)),
+                    __builtin_amdgcn_readlane(bi, 16 * r));
+    bv = rv;
+    bi = ri;
+}
+
+// Wave-wide sum with the same pairing (every lane gets the same bits: each
+// step adds the partner's value, and a + b == b + a).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// One wavefront per token, E <= 64 * NV.  Lane l holds logits l, l+64, ...
+template <int NV>
 __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __restrict__ logits,
                                                                Dims dm, int32_t* __restrict__ ids,
                                                                float* __restrict__ wts) {
@@ -103,13 +153,14 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __re
     const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
     if (t >= dm.T) return;                       // whole wave exits together
     const float* l = logits + (size_t)t * dm.E;
-    float v[kMaxPerLane];
+    float v[NV];
+    uint32_t taken = 0;                          // slots already selected, or past E
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
+    for (int i = 0; i < NV; ++i) {
         const int e = lane + kWave * i;
         v[i] = e < dm.E ? l[e] : 0.0f;
+        if (e >= dm.E) taken |= 1u << i;
     }
-    uint32_t taken = 0;
     int my_id = 0;
     float my_val = 0.0f, top_val = 0.0f;
     for (int j = 0; j < dm.k; ++j) {
@@ -117,23 +168,13 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __re
         float bv = -FLT_MAX;
         int bi = INT_MAX;
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; ++i) {
-            const int e = lane + kWave * i;
-            if (e < dm.E && !((taken >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
+        for (int i = 0; i < NV; ++i) {
+            if (!((taken >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
                 bv = v[i];
-                bi = e;
+                bi = lane + kWave * i;
             }
         }
-        // butterfly: every lane ends with the wave-wide best (value desc, index asc)
-#pragma unroll
-        for (int off = kWave / 2; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
+        wave_best(bv, bi);
         if (bi % kWave == lane) taken |= 1u << (bi / kWave);
         if (lane == j) {
             my_id = bi;
@@ -142,9 +183,7 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __re
         if (j == 0) top_val = bv;
     }
     const float ex = lane < dm.k ? expf(my_val - top_val) : 0.0f;
-    float sum = ex;
-#pragma unroll
-    for (int off = kWave / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    const float sum = wave_sum(ex);
     if (lane < dm.k) {
         ids[(size_t)t * dm.k + lane] = my_id;
         wts[(size_t)t * dm.k + lane] = ex / sum;
@@ -477,8 +516,14 @@ hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws
     if (dm.E <= kWave)
         hipLaunchKernelGGL(k_route_rank<1>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
                            ws.topk_ids, ws.topk_w);
+    else if (dm.E <= 2 * kWave)
+        hipLaunchKernelGGL(k_route<2>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
+                           ws.topk_ids, ws.topk_w);
+    else if (dm.E <= 4 * kWave)
+        hipLaunchKernelGGL(k_route<4>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
+                           ws.topk_ids, ws.topk_w);
     else
-        hipLaunchKernelGGL(k_route, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
+        hipLaunchKernelGGL(k_route<8>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
                            ws.topk_ids, ws.topk_w);
     return hipGetLastError();
 }
