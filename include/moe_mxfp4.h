@@ -221,8 +221,8 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
  * gaps between operators matter (techllm.github.io "Xiaomi MiMo x TileRT",
  * section "3. TileRT"), so the stages are timed one by one.  The stages, in
  * launch order: 0 routing, 1 permutation, 2 MXFP8 quantisation of the
- * activations (empty in bf16 mode), 3 gate/up + SwiGLU, 4 down + routing
- * weight, 5 combine.
+ * activations (empty in bf16 mode), 3 gate/up + SwiGLU, 4 down, 5 combine
+ * (routing weights and the sum over the k slots).
  *
  * moe_mxfp4_stage_timing(ctx, capacity): capacity > 0 creates capacity *
  * (MOE_MXFP4_NUM_STAGES + 1) HIP events (host call, never inside forward)

@@ -1,0 +1,117 @@
+"""GPU behaviour of the C ABI beyond the numbers: streams, stage timing,
+several contexts over one weight set, and workspaces sized for fewer tokens
+than the context allows.  Results are compared bit for bit between runs (the
+path is deterministic) and, once, against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import problems
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _moe():
+    import mxfp4_expert_ffn_amd as moe
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    return moe
+
+
+@pytest.fixture(scope="module")
+def small():
+    w = synth.Workload("api", 40, 512, 1024, 8, 2, "bf16", "none", 404)
+    acts = synth.make_activations(w)
+    wts = problems.pack_experts(w)
+    return w, acts, wts, problems.to_device(wts)
+
+
+def _inputs(acts, T):
+    x = torch.from_numpy(acts["x_bf16"][:T].view(np.int16)).cuda().view(torch.bfloat16)
+    lg = torch.from_numpy(acts["logits"][:T]).cuda()
+    return x, lg
+
+
+def test_forward_on_a_side_stream_matches_the_default_stream(small):
+    moe = _moe()
+    w, acts, wts, dev = small
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T, out_dtype=moe.OUT_F32)
+    x, lg = _inputs(acts, w.T)
+    y0 = layer(x, lg).clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()                     # default priority
+    with torch.cuda.stream(side):
+        # queue unrelated work first so the call really runs behind it
+        busy = torch.randn(2048, 2048, device="cuda")
+        for _ in range(4):
+            busy = busy @ busy.T * 1e-3
+        y1 = layer(x, lg, stream=side)
+    side.synchronize()
+    assert torch.equal(y0, y1)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, w.k)["y"]
+    assert problems.rel_max_err(y1.cpu().numpy(), ref) <= TOL
+
+
+def test_two_contexts_over_one_weight_set(small):
+    moe = _moe()
+    w, acts, wts, dev = small
+    a = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T, out_dtype=moe.OUT_F32)
+    b = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T, out_dtype=moe.OUT_BF16)
+    x, lg = _inputs(acts, w.T)
+    ya = a(x, lg)
+    yb = b(x, lg)
+    torch.cuda.synchronize()
+    # the bf16 output is the float32 one rounded once
+    assert torch.equal(yb, ya.bfloat16())
+    a.close()
+    yb2 = b(x, lg)                                  # b still works after a is destroyed
+    torch.cuda.synchronize()
+    assert torch.equal(yb, yb2)
+
+
+def test_workspace_for_fewer_tokens_than_the_context_allows(small):
+    moe = _moe()
+    w, acts, wts, dev = small
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T, out_dtype=moe.OUT_F32)
+    for T in (1, 7, 17):
+        ws = torch.empty(layer.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+        x, lg = _inputs(acts, T)
+        y = layer(x, lg, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.moe_forward(acts["x_bf16"][:T], acts["logits"][:T], wts, w.k)["y"]
+        assert problems.rel_max_err(y.cpu().numpy(), ref) <= TOL, T
+        # the first T rows of a full-batch call are the same tokens
+        yfull = layer(*_inputs(acts, w.T))
+        torch.cuda.synchronize()
+        assert torch.equal(y, yfull[:T])
+
+
+def test_stage_timing_records_every_stage(small):
+    moe = _moe()
+    w, acts, wts, dev = small
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T)
+    x, lg = _inputs(acts, w.T)
+    y0 = layer(x, lg).clone()
+    layer.stage_timing(4)
+    for _ in range(3):
+        y = layer(x, lg)
+    torch.cuda.synchronize()
+    times, n = layer.stage_times()
+    assert n == 3
+    assert set(times) == set(moe.STAGES)
+    for name, ms in times.items():
+        assert ms >= 0.0, name
+        if name != "quant":                        # no activation quantisation in bf16 mode
+            assert ms > 0.0, name
+    assert torch.equal(y, y0)                       # timing does not change the result
+    layer.stage_timing(0)                            # stop recording: nothing left to read
+    y = layer(x, lg)
+    torch.cuda.synchronize()
+    with pytest.raises(moe.MoeError):
+        layer.stage_times()
+    assert torch.equal(y, y0)
