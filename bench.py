@@ -118,7 +118,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="verify_32seq")
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated across steps")
-    ap.add_argument("--cpu-tokens", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=128)       # about 10 s of oracle time on 16 cores
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the measurements, run a plain device copy (torch.neg, float32) of this many "
