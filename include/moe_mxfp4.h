@@ -34,9 +34,10 @@
  *     frees or copies caller memory; it only reads inputs and writes outputs
  *     and the caller-provided workspace.
  *   - `hip_stream` is a hipStream_t passed as void* (NULL = default stream).
- *     Work is queued on it asynchronously; no call synchronises the device or
- *     copies device data to the host, so forward calls can be captured into
- *     a HIP graph.
+ *     Work is queued on it asynchronously; apart from moe_mxfp4_stage_times
+ *     (which waits for its last timing event) no call synchronises the
+ *     device or copies device data to the host, so forward calls can be
+ *     captured into a HIP graph.
  *   - Every call returns a moe_status.  Argument errors are detected on the
  *     host before anything is queued and leave all state unchanged.  A
  *     failed kernel launch returns MOE_ERR_HIP; faults inside kernels surface
