@@ -115,3 +115,33 @@ def test_stage_timing_records_every_stage(small):
     with pytest.raises(moe.MoeError):
         layer.stage_times()
     assert torch.equal(y, y0)
+
+
+def test_forward_replays_from_a_hip_graph(small):
+    moe = _moe()
+    w, acts, wts, dev = small
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T, out_dtype=moe.OUT_F32)
+    x, lg = _inputs(acts, w.T)
+    ws = torch.empty(layer.workspace_bytes(w.T), dtype=torch.uint8, device="cuda")
+    y_graph = torch.empty((w.T, w.d), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()                     # warm-up off the default stream, as capture expects
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer(x, lg, out=y_graph, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x, lg, out=y_graph, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    for i in range(3):
+        # new inputs in the captured buffers, a replay, then the eager call
+        xi = synth.bf16_bits_from_f32(rng.standard_normal((w.T, w.d)).astype(np.float32))
+        x.copy_(torch.from_numpy(xi.view(np.int16)).cuda().view(torch.bfloat16))
+        lg.copy_(torch.from_numpy(rng.standard_normal((w.T, w.E)).astype(np.float32)).cuda())
+        g.replay()
+        torch.cuda.synchronize()
+        y_eager = layer(x, lg)
+        torch.cuda.synchronize()
+        assert torch.equal(y_graph, y_eager), i
