@@ -60,6 +60,11 @@ constexpr int kMaxMs = kChunk / 16;            // token sub-tiles of 16 per chun
 constexpr int kRow = kKStep * 2;               // bf16 activation bytes per row and step
 constexpr int kSlot = kMaxMs * 16 * kRow;      // one LDS activation slot
 constexpr int kRsrcWord3 = 0x00020000;         // gfx9 raw buffer descriptor, dword 3
+// Cache policy of the weight loads: nt (non-temporal).  Each weight byte is
+// streamed once per chunk, so it should not displace the activation rows
+// the column tiles share; measured 3-14% faster than the default policy
+// (and setting it on the small scale loads as well was slower).
+constexpr int kWeightAux = 2;
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -140,7 +145,7 @@ struct Pipe {
             const int mat = (MODE == kGateUp && rt >= kHalf) ? 1 : 0;
             const int tile = c.tile0 + rt % kHalf;
             w[rt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    c.rw[mat], c.lane16, (tile * c.ns + step) * 1024, 0));
+                                                    c.rw[mat], c.lane16, (tile * c.ns + step) * 1024, kWeightAux));
             sg[rt] = __builtin_amdgcn_raw_buffer_load_b32(c.rs[mat], c.lane4, (tile * c.ng + step / 4) * 256, 0);
         }
     }
