@@ -135,7 +135,7 @@ struct Pipe {
         int32_t ns, ng;                   // K steps, scale groups
         const uint8_t* xbase;             // activation rows (bytes)
         uint32_t xoff[kNx];               // this lane's direct-to-LDS source offsets
-        uint8_t* lds;                     // activation ring (2 slots)
+        uint8_t* lds;                     // activation ring (D slots)
         int wave;
     };
 
