@@ -223,7 +223,9 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
  * section "3. TileRT"), so the stages are timed one by one.  The stages, in
  * launch order: 0 routing, 1 permutation, 2 MXFP8 quantisation of the
  * activations (empty in bf16 mode), 3 gate/up + SwiGLU, 4 down, 5 combine
- * (routing weights and the sum over the k slots).
+ * (routing weights and the sum over the k slots).  Batches of at most 64
+ * tokens with at most 64 experts route and permute in one launch, timed as
+ * stage 0 (stage 1 is then empty).
  *
  * moe_mxfp4_stage_timing(ctx, capacity): capacity > 0 creates capacity *
  * (MOE_MXFP4_NUM_STAGES + 1) HIP events (host call, never inside forward)

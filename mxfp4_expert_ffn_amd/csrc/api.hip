@@ -224,9 +224,16 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
 
     const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_sort(dm, ws, mx8 ? moe::kDenseChunk : moe::kChunk, s) != hipSuccess || mark(2) != hipSuccess)
-        return MOE_ERR_HIP;
+    const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
+    if (moe::route_sort_fused(dm)) {
+        // one launch; its time is recorded as the routing stage
+        if (moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s) != hipSuccess || mark(1) != hipSuccess ||
+            mark(2) != hipSuccess)
+            return MOE_ERR_HIP;
+    } else {
+        if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess) return MOE_ERR_HIP;
+        if (moe::launch_sort(dm, ws, chunk_rows, s) != hipSuccess || mark(2) != hipSuccess) return MOE_ERR_HIP;
+    }
     if (mx8 && moe::launch_quant_x8(x, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
     if (mark(3) != hipSuccess) return MOE_ERR_HIP;
     const hipError_t gu = mx8 ? moe::launch_gateup_dense(ctx->w, dm, ws, s)

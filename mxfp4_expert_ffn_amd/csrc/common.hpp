@@ -122,6 +122,10 @@ inline int max_chunks(const Dims& dm) {
 // Kernel launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s);
+// Small batches: routing and permutation in one launch (when route_sort_fused).
+bool route_sort_fused(const Dims& dm);
+hipError_t launch_route_sort(const float* logits, const Dims& dm, const Workspace& ws, int chunk_rows,
+                             hipStream_t s);
 hipError_t launch_quant_x8(const uint16_t* x, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_quant_act8(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);

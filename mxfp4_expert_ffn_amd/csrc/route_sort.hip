@@ -24,21 +24,30 @@ constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kPrefetch = 8;            // rounds of pair ids loaded ahead per wave
 
-// One wavefront per token, E <= 64 * NV.  Lane l holds logits l and l + 64.
-// The rank of logit e is the number of logits that come before it in the
-// order (value descending, expert index ascending); the experts of ranks
-// 0..k-1 are the selection, already in order.
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per-wave LDS scratch of the ranking router.
 template <int NV>
-__global__ __launch_bounds__(kRouteWaves * kWave) void k_route_rank(const float* __restrict__ logits,
-                                                                    Dims dm, int32_t* __restrict__ ids,
-                                                                    float* __restrict__ wts) {
-    __shared__ float sv[kRouteWaves][NV * kWave];
-    __shared__ int32_t sid[kRouteWaves][kMaxTopK];
-    __shared__ float sval[kRouteWaves][kMaxTopK];
-    __shared__ float sex[kRouteWaves][kMaxTopK];
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int t = blockIdx.x * kRouteWaves + wave;
-    if (t >= dm.T) return;                       // whole wave exits; waves share no LDS
+struct alignas(16) RankScratch {                 // sv is read as float4
+    float sv[NV * kWave];
+    int32_t sid[kMaxTopK];
+    float sval[kMaxTopK];
+    float sex[kMaxTopK];
+};
+
+// Routing of token t by one wavefront, E <= 64 * NV.  Lane l holds logits l
+// and l + 64.  The rank of logit e is the number of logits that come before
+// it in the order (value descending, expert index ascending); the experts of
+// ranks 0..k-1 are the selection, already in order.  Writes ids/weights of
+// the token's k slots (and the ids to ids_lds when given).
+template <int NV>
+__device__ __forceinline__ void route_token_rank(const float* __restrict__ logits, const Dims& dm, int t, int lane,
+                                 RankScratch<NV>& sc, int32_t* __restrict__ ids, float* __restrict__ wts,
+                                 int32_t* ids_lds) {
     const float* l = logits + (size_t)t * dm.E;
     float v[NV];
 #pragma unroll
@@ -46,15 +55,13 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_rank(const float*
         const int e = lane + kWave * i;
         // padding sorts after every logit: it never beats one (-inf included)
         v[i] = e < dm.E ? l[e] : -INFINITY;
-        sv[wave][e] = v[i];
+        sc.sv[e] = v[i];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
     int rank[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) rank[i] = 0;
-    const float4* row = reinterpret_cast<const float4*>(sv[wave]);
+    const float4* row = reinterpret_cast<const float4*>(sc.sv);
 #pragma unroll 4
     for (int q = 0; q < NV * kWave / 4; ++q) {
         const float4 u4 = row[q];
@@ -71,27 +78,38 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_rank(const float*
     for (int i = 0; i < NV; ++i) {
         const int e = lane + kWave * i;
         if (e < dm.E && rank[i] < dm.k) {
-            sid[wave][rank[i]] = e;
-            sval[wave][rank[i]] = v[i];
+            sc.sid[rank[i]] = e;
+            sc.sval[rank[i]] = v[i];
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
     float ex = 0.0f;
     if (lane < dm.k) {
-        ex = expf(sval[wave][lane] - sval[wave][0]);
-        sex[wave][lane] = ex;
+        ex = expf(sc.sval[lane] - sc.sval[0]);
+        sc.sex[lane] = ex;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync_lds();
     if (lane < dm.k) {
         float sum = 0.0f;
-        for (int j = 0; j < dm.k; ++j) sum += sex[wave][j];
-        ids[(size_t)t * dm.k + lane] = sid[wave][lane];
+        for (int j = 0; j < dm.k; ++j) sum += sc.sex[j];
+        const int id = sc.sid[lane];
+        ids[(size_t)t * dm.k + lane] = id;
         wts[(size_t)t * dm.k + lane] = ex / sum;
+        if (ids_lds) ids_lds[t * dm.k + lane] = id;
     }
+    wave_sync_lds();                             // the scratch may be reused for the next token
+}
+
+// One wavefront per token, E <= 64 * NV.
+template <int NV>
+__global__ __launch_bounds__(kRouteWaves * kWave) void k_route_rank(const float* __restrict__ logits,
+                                                                    Dims dm, int32_t* __restrict__ ids,
+                                                                    float* __restrict__ wts) {
+    __shared__ RankScratch<NV> sc[kRouteWaves];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int t = blockIdx.x * kRouteWaves + wave;
+    if (t >= dm.T) return;                       // whole wave exits; waves share no LDS
+    route_token_rank<NV>(logits, dm, t, lane, sc[wave], ids, wts, nullptr);
 }
 
 // (value, expert) order of the routing: larger value first, then the lower
@@ -330,16 +348,21 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
     return tid < E ? excl : 0;
 }
 
-// Single workgroup, up to kSortSingleMax pairs.  LDS: keys[E] (8 bytes) +
-// hist[kSortWaves][E] + counts[E rounded up to 4] + act[E] + rnk[E] +
-// exoff[E] + 32 ints.
-__global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
-                                                       int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ sorted,
-                                                       int32_t* __restrict__ active,
-                                                       int32_t* __restrict__ chunks,
-                                                       int32_t* __restrict__ nchunks, int chunk_rows) {
-    extern __shared__ uint64_t sm64[];
+// LDS of the single-workgroup sort: keys[E] (8 bytes) + hist[kSortWaves][E]
+// + counts[E rounded up to 4] + act[E] + rnk[E] + exoff[E] + 32 ints,
+// rounded up to 16 bytes.
+__host__ __device__ inline size_t sort_lds_bytes(int E) {
+    const size_t E4 = (size_t)(E + 3) & ~(size_t)3;
+    const size_t b = sizeof(uint64_t) * E + sizeof(int32_t) * (kSortWaves * (size_t)E + E4 + 3 * (size_t)E + 2 * kSortWaves);
+    return (b + 15) & ~(size_t)15;
+}
+
+// The permutation by one kSortThreads workgroup, up to kSortSingleMax pairs,
+// ids read from `ids` (global or LDS); sm64: the LDS of sort_lds_bytes(E).
+__device__ __forceinline__ void sort_single(const Dims& dm, const int32_t* __restrict__ ids, uint64_t* sm64,
+                            int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
+                            int32_t* __restrict__ active, int32_t* __restrict__ chunks,
+                            int32_t* __restrict__ nchunks, int chunk_rows) {
     const int E = dm.E, P = dm.P;
     const int E4 = (E + 3) & ~3;
     uint64_t* keys = sm64;                            // [E]
@@ -396,6 +419,40 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
                        if (rank == 0) my[e] += n;
                    }
                });
+}
+
+__global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* __restrict__ ids,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted,
+                                                       int32_t* __restrict__ active,
+                                                       int32_t* __restrict__ chunks,
+                                                       int32_t* __restrict__ nchunks, int chunk_rows) {
+    extern __shared__ uint64_t sm64[];
+    sort_single(dm, ids, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows);
+}
+
+// Small batches (T <= kFusedMaxTokens, E <= 64): routing and the permutation
+// in one workgroup.  Wave w routes tokens w, w + 16, ... and keeps their ids
+// in LDS, where the sort then reads them: one launch instead of two, and no
+// round trip of the ids through memory between them.  LDS after the sort's:
+// ids[P] (rounded to 16 bytes), then one ranking scratch per wave.
+constexpr int kFusedMaxTokens = 4 * kSortWaves;
+
+__global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __restrict__ logits, Dims dm,
+                                                             int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted,
+                                                             int32_t* __restrict__ active,
+                                                             int32_t* __restrict__ chunks,
+                                                             int32_t* __restrict__ nchunks, int chunk_rows) {
+    extern __shared__ uint64_t sm64[];
+    uint8_t* extra = reinterpret_cast<uint8_t*>(sm64) + sort_lds_bytes(dm.E);
+    int32_t* ids_lds = reinterpret_cast<int32_t*>(extra);
+    RankScratch<1>* sc = reinterpret_cast<RankScratch<1>*>(extra + (((size_t)dm.P * sizeof(int32_t) + 15) & ~(size_t)15));
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    for (int t = wave; t < dm.T; t += kSortWaves) route_token_rank<1>(logits, dm, t, lane, sc[wave], ids, wts, ids_lds);
+    __syncthreads();
+    sort_single(dm, ids_lds, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows);
 }
 
 // Many pairs: tiles of kSortTile pairs, one 256-thread workgroup each (the
@@ -528,11 +585,23 @@ hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws
     return hipGetLastError();
 }
 
+bool route_sort_fused(const Dims& dm) {
+    return dm.E <= kWave && dm.T <= kFusedMaxTokens && dm.P <= kSortSingleMax;
+}
+
+hipError_t launch_route_sort(const float* logits, const Dims& dm, const Workspace& ws, int chunk_rows,
+                             hipStream_t s) {
+    const size_t lds = sort_lds_bytes(dm.E) + (((size_t)dm.P * sizeof(int32_t) + 15) & ~(size_t)15) +
+                       kSortWaves * sizeof(RankScratch<1>);
+    hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(kSortThreads), lds, s, logits, dm, ws.topk_ids, ws.topk_w,
+                       ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks, chunk_rows);
+    return hipGetLastError();
+}
+
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s) {
     const size_t E = dm.E, E4 = (E + 3) & ~3;
     if (dm.P <= kSortSingleMax) {
-        const size_t lds = sizeof(uint64_t) * E + sizeof(int32_t) * (kSortWaves * E + E4 + 3 * E + 2 * kSortWaves);
-        hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), lds, s, dm, ws.topk_ids, ws.offsets,
+        hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), sort_lds_bytes(dm.E), s, dm, ws.topk_ids, ws.offsets,
                            ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks,
                            chunk_rows);
         return hipGetLastError();
