@@ -106,7 +106,9 @@ def test_stage_timing_records_every_stage(small):
     assert set(times) == set(moe.STAGES)
     for name, ms in times.items():
         assert ms >= 0.0, name
-        if name != "quant":                        # no activation quantisation in bf16 mode
+        # no activation quantisation in bf16 mode; 40 tokens over 8 experts
+        # route and permute in one launch, timed as the routing stage
+        if name not in ("quant", "sort"):
             assert ms > 0.0, name
     assert torch.equal(y, y0)                       # timing does not change the result
     layer.stage_timing(0)                            # stop recording: nothing left to read
