@@ -91,8 +91,8 @@ struct Workspace {
     int32_t* offsets;         // [E+1]
     int32_t* sorted_pairs;    // [P]
     int32_t* active;          // [E+1] active experts (count > 0) by descending count; [E] = how many
-    int32_t* chunks;          // [max_chunks][4] (expert, first pair within the expert,
-                              //   first chunk of the expert, number of chunks of the expert)
+    int32_t* chunks;          // [max_chunks][4] (expert, position of the chunk's first pair in
+                              //   sorted_pairs, pairs in the chunk, 0)
     int32_t* nchunks;         // [1] number of chunks
     int32_t* sort_part;       // [sort_tiles(P)][E] per-tile expert histograms / first positions
     uint8_t* xq;              // MXFP8 mode: [T][d] E4M3 codes of x

@@ -61,7 +61,6 @@ struct DenseArgs {
     const uint8_t* s0;
     const uint8_t* w1;           // up (gate/up only)
     const uint8_t* s1;
-    const int32_t* offsets;      // [E+1]
     const int32_t* sorted;       // [P]
     const int32_t* chunks;       // chunk records
     const int32_t* nchunks;
@@ -358,13 +357,16 @@ __global__ __launch_bounds__((Shape<WN, STAGES>::kT), (Shape<WN, STAGES>::kPerCu
     const int unit = blockIdx.x;
     const int chunk = unit / a.n_tiles;
     const int nt = unit % a.n_tiles;
-    if (chunk >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;
+    // the record (inside the chunk list for every unit of the grid) is read
+    // together with the count, so the first loads wait on one round trip
     const int* rec = a.chunks + kChunkRec * chunk;
     const int e = __builtin_amdgcn_readfirstlane(rec[0]);
-    const int c0 = __builtin_amdgcn_readfirstlane(rec[1]);
-    const int m0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
-    const int M = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - m0;
-    Dense<MODE, WN, STAGES>::run(a, smem, e, nt, m0, c0, M);
+    const int start = __builtin_amdgcn_readfirstlane(rec[1]);
+    const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
+    if (chunk >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;
+    // run() takes (first sorted position m0, chunk offset c0, pairs M) with
+    // the chunk's pairs at m0 + c0 .. m0 + M - 1
+    Dense<MODE, WN, STAGES>::run(a, smem, e, nt, start, 0, rows);
 }
 
 // Upper bound of the chunk list at kDenseChunk pairs per chunk.
@@ -389,7 +391,7 @@ hipError_t launch_gateup_dense(const moe_mxfp4_weights& w, const Dims& dm, const
     a.act = ws.xq; a.act_scale = ws.xs; a.act_rows = (uint32_t)dm.T;
     a.w0 = w.w_gate; a.s0 = w.w_gate_scale;
     a.w1 = w.w_up;   a.s1 = w.w_up_scale;
-    a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.h_out = ws.h; a.h_scale_out = ws.hs; a.o_out = nullptr;
     a.K = dm.d; a.N = dm.f; a.n_tiles = dm.f / 128; a.k_top = dm.k; a.ldo = dm.f;
     return launch<kGateUp>(a, max_dense_chunks(dm) * a.n_tiles, s);
@@ -400,7 +402,7 @@ hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const W
     a.act = ws.h; a.act_scale = ws.hs; a.act_rows = (uint32_t)dm.P;
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
-    a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.h_out = nullptr; a.h_scale_out = nullptr; a.o_out = ws.o;
     a.K = dm.f; a.N = dm.d; a.n_tiles = dm.d / 256; a.k_top = dm.k; a.ldo = dm.d;
     return launch<kDown>(a, max_dense_chunks(dm) * a.n_tiles, s);

@@ -74,7 +74,6 @@ struct GemmArgs {
     const uint8_t* s0;
     const uint8_t* w1;          // up tiled packed (gate/up only)
     const uint8_t* s1;
-    const int32_t* offsets;     // [E+1]
     const int32_t* sorted;      // [P]
     const int32_t* chunks;      // chunk records
     const int32_t* nchunks;     // device count of chunks
@@ -343,17 +342,20 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a
     const int unit = blockIdx.x;
     const int chunk = unit / a.n_tiles;
     const int nt = unit % a.n_tiles;
-    if (chunk >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;     // uniform per workgroup
+    // the record (inside the chunk list for every unit of the grid) is read
+    // together with the count, so the weight loads wait on one round trip
     const int* rec = a.chunks + kChunkRec * chunk;
     const int e = __builtin_amdgcn_readfirstlane(rec[0]);
-    const int c0 = __builtin_amdgcn_readfirstlane(rec[1]);
-    const int m0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
-    const int M = __builtin_amdgcn_readfirstlane(a.offsets[e + 1]) - m0;
-    switch (min(kMaxMs, (M - c0 + 15) / 16)) {
-        case 1: Pipe<MODE, RT, 1, D>::run(a, lds, e, nt, m0, c0, M); break;
-        case 2: Pipe<MODE, RT, 2, D>::run(a, lds, e, nt, m0, c0, M); break;
-        case 3: Pipe<MODE, RT, 3, D>::run(a, lds, e, nt, m0, c0, M); break;
-        default: Pipe<MODE, RT, 4, D>::run(a, lds, e, nt, m0, c0, M); break;
+    const int start = __builtin_amdgcn_readfirstlane(rec[1]);
+    const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
+    if (chunk >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;     // uniform per workgroup
+    // run() takes (first sorted position m0, chunk offset c0, pairs M) with
+    // the chunk's pairs at m0 + c0 .. m0 + M - 1
+    switch (min(kMaxMs, (rows + 15) / 16)) {
+        case 1: Pipe<MODE, RT, 1, D>::run(a, lds, e, nt, start, 0, rows); break;
+        case 2: Pipe<MODE, RT, 2, D>::run(a, lds, e, nt, start, 0, rows); break;
+        case 3: Pipe<MODE, RT, 3, D>::run(a, lds, e, nt, start, 0, rows); break;
+        default: Pipe<MODE, RT, 4, D>::run(a, lds, e, nt, start, 0, rows); break;
     }
 }
 
@@ -389,7 +391,7 @@ hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Di
     a.act = reinterpret_cast<const uint8_t*>(x);
     a.w0 = w.w_gate; a.s0 = w.w_gate_scale;
     a.w1 = w.w_up;   a.s1 = w.w_up_scale;
-    a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.h_out = ws.h; a.o_out = nullptr;
     a.K = dm.d; a.N = dm.f;
     a.k_top = dm.k; a.ldo = dm.f;
@@ -401,7 +403,7 @@ hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspa
     a.act = ws.h;
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
-    a.offsets = ws.offsets; a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
     a.h_out = nullptr; a.o_out = ws.o;
     a.K = dm.f; a.N = dm.d;
     a.k_top = dm.k; a.ldo = dm.d;

@@ -333,14 +333,16 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
     int cbefore = 0;
     for (int w = 0; w < wave; ++w) cbefore += wsum[w];
     if (tid < na) {
-        // record: expert, first pair of the chunk, first chunk of the expert, chunks of the expert
+        // record: expert, position of the chunk's first pair in sorted_pairs,
+        // pairs in the chunk, 0
         const int first = cbefore + nincl - nch;
+        const int e = act[tid], n = counts[e], base = exoff[e];
         for (int q = 0; q < nch; ++q) {
             int32_t* rec = chunks + kChunkRec * (first + q);
-            rec[0] = act[tid];
-            rec[1] = q * chunk_rows;
-            rec[2] = first;
-            rec[3] = nch;
+            rec[0] = e;
+            rec[1] = base + q * chunk_rows;
+            rec[2] = min(chunk_rows, n - q * chunk_rows);
+            rec[3] = 0;
         }
     }
     if (tid == kSortThreads - 1) *nchunks = cbefore + nincl;
