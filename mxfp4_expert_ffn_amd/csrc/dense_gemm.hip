@@ -153,10 +153,13 @@ struct Dense {
         if (lane < kTM / kW) lds_dma16(c.ras, c.lAs + gs * kAsSlot + c.wave * (kTM / kW) * 16, c.asoff, grp * 16);
     }
 
-    // The A operands of the step are read first (they serve every MFMA), then
-    // the weight tiles one ahead of the MFMAs that use them.  FULL: every
-    // sub-tile of the wave holds pairs (otherwise only the first nms are
-    // multiplied).
+    // LDS reads of a step: the operands of the first MFMA (A sub-tile 0 and
+    // weight tile 0) first, then the other A sub-tiles, each MFMA waiting
+    // only for its own operands (LDS reads return in order).  Gate/up also
+    // reads all its weight tiles up front, into registers of their own;
+    // down lacks the registers and reads each tile one ahead of its MFMAs.
+    // FULL: every sub-tile of the wave holds pairs (otherwise only the first
+    // nms are multiplied).
     template <int S4, bool FULL>
     __device__ static void compute(const Ctx& c, f32x4_t (&acc)[kMs][kJ], const uint32_t (&sbw)[kJ], int slot,
                                    int gs, int nms, int wm, int wn, int lane) {
@@ -166,27 +169,49 @@ struct Dense {
         const uint8_t* As = c.lAs + gs * kAsSlot;
         i32x8_t a[kMs];
         int sa[kMs];
-#pragma unroll
-        for (int ms = 0; ms < kMs; ++ms) {
+        auto load_a = [&](int ms) {
             const int r = wm * 64 + ms * 16 + li;
             const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(A + r * kKStep + swz(r, g) * 16);
             const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(A + r * kKStep + swz(r, 4 + g) * 16);
             a[ms] = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             sa[ms] = As[r * 16 + S4 * 4 + g];
-        }
+        };
+        load_a(0);
         u32x4_t b = *reinterpret_cast<const u32x4_t*>(B + wslot(wn, 0) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int jj = 0; jj < kJ; ++jj) {
-            u32x4_t bn = b;
-            if (jj + 1 < kJ) bn = *reinterpret_cast<const u32x4_t*>(B + wslot(wn, jj + 1) * 1024);
-            // FP4 B operand: only the low 4 registers are read
-            const i32x8_t bb = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3));
+        for (int ms = 1; ms < kMs; ++ms) load_a(ms);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MODE == kGateUp) {
+            u32x4_t bt[kJ];
+            bt[0] = b;
 #pragma unroll
-            for (int ms = 0; ms < kMs; ++ms)
-                if (FULL || ms < nms)
-                    acc[ms][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        a[ms], bb, acc[ms][jj], 0 /* A: E4M3 */, 4 /* B: E2M1 */, 0, sa[ms], S4, (int)sbw[jj]);
-            b = bn;
+            for (int jj = 1; jj < kJ; ++jj) bt[jj] = *reinterpret_cast<const u32x4_t*>(B + wslot(wn, jj) * 1024);
+            __builtin_amdgcn_sched_barrier(0);             // keeps the reads ahead of the MFMAs
+#pragma unroll
+            for (int jj = 0; jj < kJ; ++jj) {
+                // FP4 B operand: only the low 4 registers are read
+                const i32x8_t bb =
+                    __builtin_bit_cast(i32x8_t, __builtin_shufflevector(bt[jj], bt[jj], 0, 1, 2, 3, 0, 1, 2, 3));
+#pragma unroll
+                for (int ms = 0; ms < kMs; ++ms)
+                    if (FULL || ms < nms)
+                        acc[ms][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a[ms], bb, acc[ms][jj], 0 /* A: E4M3 */, 4 /* B: E2M1 */, 0, sa[ms], S4, (int)sbw[jj]);
+            }
+        } else {
+#pragma unroll
+            for (int jj = 0; jj < kJ; ++jj) {
+                u32x4_t bn = b;
+                if (jj + 1 < kJ) bn = *reinterpret_cast<const u32x4_t*>(B + wslot(wn, jj + 1) * 1024);
+                const i32x8_t bb = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3));
+#pragma unroll
+                for (int ms = 0; ms < kMs; ++ms)
+                    if (FULL || ms < nms)
+                        acc[ms][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a[ms], bb, acc[ms][jj], 0 /* A: E4M3 */, 4 /* B: E2M1 */, 0, sa[ms], S4, (int)sbw[jj]);
+                b = bn;
+            }
         }
     }
 
