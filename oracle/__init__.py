@@ -31,6 +31,8 @@ PINS = {
     "orc_e4m3_round": "torch float8_e4m3fn round-to-nearest-even below saturation",
     "orc_quant_mxfp4": "exact round trip of codebook x 2^e blocks; second quantiser",
     "orc_quant_mxfp8": "torch E4M3 rounding with the OCP scale rule; round trips",
+    "orc_router_logits": "pure-Python brute force on small shapes; one-hot rows pick "
+                         "weight entries; sign flip; split-support additivity",
     "orc_route": "brute-force sort on (-logit, index); forced ties; 1-ulp gaps",
     "orc_permute": "stable sort of pair ids by expert; invariants",
     "orc_moe_forward": "dense numpy evaluation over all experts; E=1 matmul "
@@ -67,6 +69,7 @@ def bind(L):
     for name in ("orc_quant_mxfp4", "orc_quant_mxfp8"):
         getattr(L, name).argtypes = [P, i64, i64, P, P]
         getattr(L, name).restype = None
+    L.orc_router_logits.argtypes = [P, P, i32, i32, i32, P, P]; L.orc_router_logits.restype = None
     L.orc_route.argtypes = [P, i32, i32, i32, P, P]; L.orc_route.restype = None
     L.orc_permute.argtypes = [P, i32, i32, i32, P, P, P, P]; L.orc_permute.restype = None
     L.orc_moe_forward.argtypes = [i32] * 6 + [P] * 8 + [P, P, P, P, i32]
@@ -147,6 +150,18 @@ def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     out = np.empty((rows, K), np.float64)
     lib().orc_dequant_mxfp8(_p(codes), _p(scales), rows, K, _p(out))
     return out
+
+
+def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray):
+    """bf16 bits x [T, d], W [E, d] -> (logits float64 [T, E], absdot float64 [T, E])."""
+    x_bf16, w_bf16 = _c(x_bf16, np.uint16), _c(w_bf16, np.uint16)
+    T, d = x_bf16.shape
+    E = w_bf16.shape[0]
+    assert w_bf16.shape == (E, d)
+    logits = np.empty((T, E), np.float64)
+    absdot = np.empty((T, E), np.float64)
+    lib().orc_router_logits(_p(x_bf16), _p(w_bf16), T, d, E, _p(logits), _p(absdot))
+    return logits, absdot
 
 
 def route(logits: np.ndarray, k: int):

@@ -246,6 +246,32 @@ static double bf16_value(uint16_t bits) {
     return (double)f;
 }
 
+/* Router projection that produces the routing logits from the hidden
+ * states.  The pages keep every module outside the experts in FP8 or its
+ * original precision (techllm.github.io "Xiaomi MiMo x TileRT", section
+ * "1. MXFP4 — MoE에만 걸린 양자화") and route each token to its experts
+ * (same page, section "3. TileRT"), but give no router form; the reading
+ * taken is the plain linear map logits = x W^T with bf16 x and W and no
+ * bias.  Every product of two bf16 values is exact in double; the sum is
+ * taken in index order. */
+void orc_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int32_t T, int32_t d,
+                       int32_t E, double* logits, double* absdot) {
+    for (int32_t t = 0; t < T; ++t) {
+        const uint16_t* xt = x_bf16 + (int64_t)t * d;
+        for (int32_t e = 0; e < E; ++e) {
+            const uint16_t* we = w_bf16 + (int64_t)e * d;
+            double s = 0.0, a = 0.0;
+            for (int32_t i = 0; i < d; ++i) {
+                const double p = bf16_value(xt[i]) * bf16_value(we[i]);
+                s += p;
+                a += fabs(p);
+            }
+            logits[(int64_t)t * E + e] = s;
+            if (absdot) absdot[(int64_t)t * E + e] = a;
+        }
+    }
+}
+
 /* Element [r][kk] of an MXFP4 matrix with K columns. */
 static double w_elem(const uint8_t* packed, const uint8_t* scales, int64_t K,
                      int64_t r, int64_t kk) {

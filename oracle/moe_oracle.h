@@ -53,6 +53,13 @@ void orc_quant_mxfp8(const double* v, int64_t rows, int64_t K,
 void orc_dequant_mxfp8(const uint8_t* codes, const uint8_t* scales,
                        int64_t rows, int64_t K, double* out);
 
+/* ---- router projection (in front of the routing) ---- */
+/* logits[T][E] = x[T][d] . W[E][d]^T in double from bf16 bit patterns; the
+ * optional absdot[T][E] (NULL to skip) gets sum_i |x[t][i] * W[e][i]|, the
+ * scale of any rounding error in a lower-precision evaluation. */
+void orc_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int32_t T, int32_t d,
+                       int32_t E, double* logits, double* absdot);
+
 /* ---- routing and permutation ---- */
 void orc_route(const float* logits, int32_t T, int32_t E, int32_t k,
                int32_t* topk_ids, double* topk_w);

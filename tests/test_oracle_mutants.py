@@ -28,6 +28,9 @@ MUTANTS = {
     "scale_emax": ("block_scale_exp(amax, 2);", "block_scale_exp(amax, 1);"),
     "scale_floor": ("int se = (ex - 1) - emax_elem;", "int se = ex - emax_elem;"),
     "e4m3_subnormal": ("ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)"),
+    "router_transposed": ("const uint16_t* we = w_bf16 + (int64_t)e * d;",
+                          "const uint16_t* we = w_bf16 + (int64_t)e;"),
+    "router_abs_of_sum": ("a += fabs(p);", "a += p;"),
     "route_tie_high": ("(best < 0 || l[e] > l[best])", "(best < 0 || l[e] >= l[best])"),
     "softmax_sign": ("sum += exp((double)l[ids[j]] - l0);",
                      "sum += exp(l0 - (double)l[ids[j]]);"),

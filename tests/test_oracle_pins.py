@@ -213,6 +213,61 @@ def _route_cases():
     yield rng.standard_normal((16, 128)).astype(np.float32), 8
 
 
+# ---------------------------------------------------------- router logits
+
+def _bf16(a):
+    return synth.bf16_bits_from_f32(np.asarray(a, np.float32))
+
+
+def test_router_logits_match_pure_python_bruteforce():
+    rng = np.random.default_rng(41)
+    for T, d, E in ((3, 64, 5), (1, 32, 1), (4, 96, 3)):
+        x = _bf16(rng.standard_normal((T, d)))
+        w = _bf16(rng.standard_normal((E, d)) * 0.02)
+        got, absdot = oracle.router_logits(x, w)
+        xv = synth.bf16_bits_to_f32(x).astype(np.float64).tolist()
+        wv = synth.bf16_bits_to_f32(w).astype(np.float64).tolist()
+        for t in range(T):
+            for e in range(E):
+                s = a = 0.0
+                for i in range(d):
+                    s += xv[t][i] * wv[e][i]
+                    a += abs(xv[t][i] * wv[e][i])
+                assert got[t, e] == s and absdot[t, e] == a, (t, e)
+
+
+def test_router_one_hot_rows_pick_weight_entries():
+    rng = np.random.default_rng(42)
+    d, E = 256, 7
+    w = _bf16(rng.standard_normal((E, d)))
+    picks = [0, 1, 31, 32, 200, 255]
+    x = np.zeros((len(picks), d), np.float32)
+    for t, i in enumerate(picks):
+        x[t, i] = 1.0 if t % 2 == 0 else -2.0
+    logits, _ = oracle.router_logits(_bf16(x), w)
+    wv = synth.bf16_bits_to_f32(w).astype(np.float64)
+    for t, i in enumerate(picks):
+        assert np.array_equal(logits[t], (1.0 if t % 2 == 0 else -2.0) * wv[:, i])
+
+
+def test_router_sign_flip_and_split_support_additivity():
+    rng = np.random.default_rng(43)
+    T, d, E = 5, 512, 9
+    x = _bf16(rng.standard_normal((T, d)))
+    w = rng.standard_normal((E, d)).astype(np.float32)
+    w_lo, w_hi = w.copy(), w.copy()
+    w_lo[:, d // 2:] = 0.0                            # disjoint supports: w = w_lo + w_hi exactly
+    w_hi[:, :d // 2] = 0.0
+    full, absdot = oracle.router_logits(x, _bf16(w))
+    lo, a_lo = oracle.router_logits(x, _bf16(w_lo))
+    hi, a_hi = oracle.router_logits(x, _bf16(w_hi))
+    np.testing.assert_allclose(full, lo + hi, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(absdot, a_lo + a_hi, rtol=1e-12)
+    neg, _ = oracle.router_logits(x ^ np.uint16(0x8000), _bf16(w))
+    assert np.array_equal(neg, -full)
+    assert np.all(absdot >= np.abs(full))
+
+
 def test_route_matches_bruteforce():
     for logits, k in _route_cases():
         ids, w = oracle.route(logits, k)
