@@ -60,14 +60,21 @@ def pack_on_gpu(w, copies, moe, torch):
     return out
 
 
-def cpu_baseline(w, acts, ntok):
-    """The oracle, as it stands, on the first `ntok` tokens (oracle-packed weights)."""
+def cpu_baseline(w, acts, ntok, router_bits=None):
+    """The oracle, as it stands, on the first `ntok` tokens (oracle-packed weights);
+    with `router_bits` (bf16 [E, d]) the logits come from the oracle's router
+    projection, timed with the layer."""
     import numpy as np
     import oracle
     import synth
     from concurrent.futures import ThreadPoolExecutor
     threads = min(16, os.cpu_count() or 1)
     x, lg = acts["x_bf16"][:ntok], acts["logits"][:ntok]
+    t_router = 0.0
+    if router_bits is not None:
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(x, router_bits)[0].astype(np.float32)
+        t_router = time.perf_counter() - t0
     ids, _ = oracle.route(lg, w.k)
     need = [int(e) for e in np.unique(ids)]
     wts = {n: np.zeros(s, np.uint8) for n, s in weight_shapes(w).items()}
@@ -83,9 +90,10 @@ def cpu_baseline(w, acts, ntok):
         list(ex.map(job, need))
     t0 = time.perf_counter()
     r = oracle.moe_forward(x, lg, wts, w.k, nthreads=threads)
-    dt = time.perf_counter() - t0
+    dt = time.perf_counter() - t0 + t_router
     return {"value": ntok / dt, "unit": "tokens/s", "cores": int(r["threads"]), "kind": "oracle",
-            "sample": f"first {ntok} of {w.T} tokens of {w.name}, all {w.k} experts each; "
+            "sample": f"first {ntok} of {w.T} tokens of {w.name}, all {w.k} experts each"
+                      f"{', router projection included' if router_bits is not None else ''}; "
                       f"fp64 C oracle, OpenMP over tokens; {dt:.2f} s wall"}
 
 
@@ -120,6 +128,9 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated across steps")
     ap.add_argument("--cpu-tokens", type=int, default=128)       # about 10 s of oracle time on 16 cores
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--with-router", action="store_true",
+                    help="time the forward call with the router projection in front (logits = x W_router^T "
+                         "computed inside the call) instead of taking the logits as input")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the measurements, run a plain device copy (torch.neg, float32) of this many "
                          "MiB: the reference dispatch for scaling HBM byte counters")
@@ -145,6 +156,10 @@ def main():
 
     x = torch.from_numpy(acts["x_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
     lg = torch.from_numpy(acts["logits"]).cuda()
+    wr = None
+    if args.with_router:
+        wr = torch.from_numpy(synth.router_weights_bf16(w).view(np.int16)).cuda().view(torch.bfloat16)
+        lg = None
     out = torch.empty((w.T, w.d), dtype=torch.bfloat16, device="cuda")
     act_mode = moe.ACT_MXFP8_E4M3 if mx8 else moe.ACT_BF16
     layers = [moe.MoeMxfp4(c, w.E, w.d, w.f, w.k, max_tokens=w.T, act_mode=act_mode) for c in wcopies]
@@ -152,23 +167,25 @@ def main():
 
     # routing of this batch, from the library itself, for the byte counts
     offs = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
-    layers[0](x, lg, out=out, workspace=ws, routing={"expert_offsets": offs})
+    layers[0](x, lg, out=out, workspace=ws, routing={"expert_offsets": offs}, w_router=wr)
     torch.cuda.synchronize()
     counts = np.diff(offs.cpu().numpy())
     touched = int((counts > 0).sum())
     per_expert = 3 * w.d * w.f * (1 / 2 + 1 / 32)
     layer_bytes = touched * per_expert + w.T * w.d * 2 + w.T * w.E * 4 + w.T * w.d * 2
+    if wr is not None:
+        layer_bytes += w.E * w.d * 2                  # router weights
     gateup_bytes = touched * 2 * w.f * w.d * (1 / 2 + 1 / 32) + w.T * w.d * 2
     flops = 2.0 * w.P * 3 * w.d * w.f
 
     for i in range(args.warmup):
-        layers[i % args.copies](x, lg, out=out, workspace=ws)
+        layers[i % args.copies](x, lg, out=out, workspace=ws, w_router=wr)
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` forward calls
     t0 = time.perf_counter()
     for i in range(args.steps):
-        layers[i % args.copies](x, lg, out=out, workspace=ws)
+        layers[i % args.copies](x, lg, out=out, workspace=ws, w_router=wr)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt * 1e3 / args.steps
@@ -177,7 +194,7 @@ def main():
     for L in layers:
         L.stage_timing(args.steps)
     for i in range(args.steps):
-        layers[i % args.copies](x, lg, out=out, workspace=ws)
+        layers[i % args.copies](x, lg, out=out, workspace=ws, w_router=wr)
     torch.cuda.synchronize()
     stage_ms, ncalls = {}, 0
     for L in layers:
@@ -219,7 +236,8 @@ def main():
         "config": {"workload": f"{w.name}: {w.T} tokens ({w.T // 8} sequences x DFlash block 8), "
                                f"d_model {w.d}, d_ff {w.f}, {w.E} experts, top-{w.k}, "
                                f"bias {w.bias}, MXFP4 weights (E2M1 + E8M0 per 32), "
-                               f"{'MXFP8 (E4M3 + E8M0 per 32)' if mx8 else 'bf16'} activations, bf16 out",
+                               f"{'MXFP8 (E4M3 + E8M0 per 32)' if mx8 else 'bf16'} activations, bf16 out"
+                               f"{', router projection in the call (bf16 W_router [E][d])' if wr is not None else ''}",
                    "T": w.T, "d_model": w.d, "d_ff": w.f, "experts": w.E, "top_k": w.k,
                    "touched_experts": touched, "weight_copies": args.copies},
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -229,6 +247,18 @@ def main():
         "stage_us": stage_avg_us,
         "roofline": roofline,
     }
+    if wr is not None:
+        # the projection alone, on torch's current stream, timed with its events
+        lgo = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+        for _ in range(5):
+            layers[0].router_logits(x, wr, out=lgo)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            layers[0].router_logits(x, wr, out=lgo)
+        e1.record()
+        torch.cuda.synchronize()
+        result["router_projection_us"] = e0.elapsed_time(e1) * 1e3 / args.steps
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 18                   # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -239,7 +269,8 @@ def main():
         log(f"calibration copy: {args.copy_calibration_mib} MiB read + written, 3 dispatches")
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
-        result["cpu_baseline"] = cpu_baseline(w, acts, args.cpu_tokens)
+        rb = synth.router_weights_bf16(w) if wr is not None else None
+        result["cpu_baseline"] = cpu_baseline(w, acts, args.cpu_tokens, rb)
     print(json.dumps(result), flush=True)
 
 

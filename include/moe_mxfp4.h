@@ -205,6 +205,39 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden,
                              void* hip_stream, const moe_mxfp4_routing* debug_out);
 
 /*
+ * Router projection, the step in front of the routing:
+ *   logits[t][e] = sum_i hidden[t][i] * w_router[e][i]
+ * with bf16 inputs and float32 accumulation on the matrix cores, in an order
+ * that does not depend on timing (deterministic).  The pages keep every
+ * module outside the experts in FP8 or its original precision
+ * (techllm.github.io "Xiaomi MiMo x TileRT", section "1. MXFP4 — MoE에만 걸린
+ * 양자화") and route every token to its experts (same page, section
+ * "3. TileRT"); they give no router form, and this is the plain linear map
+ * (no bias).  All buffers are device memory:
+ *   hidden    bf16  [T][d_model] (uint16 bit patterns)
+ *   w_router  bf16  [E][d_model]: row e is expert e's router vector
+ *   logits    float [T][E], fully overwritten
+ * T = 0 is a no-op returning MOE_OK.
+ * Errors: INVALID_ARG, CAPACITY (T > max_tokens), ALIGNMENT, HIP.
+ */
+moe_status moe_mxfp4_router_logits(const moe_mxfp4_ctx* ctx, const void* hidden,
+                                   const void* w_router, int32_t num_tokens,
+                                   float* logits, void* hip_stream);
+
+/*
+ * moe_mxfp4_forward with the router projection in front: the logits are
+ * computed from hidden and w_router (as moe_mxfp4_router_logits) into the
+ * workspace, which moe_mxfp4_workspace_bytes already covers, and the call
+ * continues as moe_mxfp4_forward with them.  Stage timing counts the
+ * projection in the routing stage.
+ * Errors: as moe_mxfp4_forward (INVALID_ARG for a NULL w_router).
+ */
+moe_status moe_mxfp4_forward_hidden(moe_mxfp4_ctx* ctx, const void* hidden,
+                                    const void* w_router, int32_t num_tokens,
+                                    void* out, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream, const moe_mxfp4_routing* debug_out);
+
+/*
  * Decode rows [row0, row0 + nrows) of one expert matrix (0 gate, 1 up,
  * 2 down) from the context's TILED weights with the forward path's own
  * in-register FP4 decode, widened to float: out (device) float [nrows][K]

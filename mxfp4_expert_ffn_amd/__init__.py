@@ -29,7 +29,7 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create
            "moe_mxfp4_destroy", "moe_mxfp4_workspace_bytes", "moe_mxfp4_forward",
            "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights", "moe_mxfp4_stage_timing",
            "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights",
-           "moe_mxfp4_quantize_act_mxfp8")
+           "moe_mxfp4_quantize_act_mxfp8", "moe_mxfp4_router_logits", "moe_mxfp4_forward_hidden")
 NUM_STAGES = 6
 STAGES = ("route", "sort", "quant", "gateup", "down", "combine")
 
@@ -82,6 +82,10 @@ def lib():
         L.moe_mxfp4_workspace_bytes.restype = sz
         L.moe_mxfp4_forward.argtypes = [P, P, P, i32, P, P, sz, P, ctypes.POINTER(Routing)]
         L.moe_mxfp4_forward.restype = ctypes.c_int
+        L.moe_mxfp4_forward_hidden.argtypes = [P, P, P, i32, P, P, sz, P, ctypes.POINTER(Routing)]
+        L.moe_mxfp4_forward_hidden.restype = ctypes.c_int
+        L.moe_mxfp4_router_logits.argtypes = [P, P, P, i32, P, P]
+        L.moe_mxfp4_router_logits.restype = ctypes.c_int
         L.moe_mxfp4_debug_dequant.argtypes = [P, i32, i32, i32, i32, P, P]
         L.moe_mxfp4_debug_dequant.restype = ctypes.c_int
         L.moe_mxfp4_quantize_weights.argtypes = [P, i64, i64, P, P, P]
@@ -171,9 +175,15 @@ class MoeMxfp4:
         return self._ws
 
     def forward(self, hidden, logits, out=None, workspace=None, routing: dict | None = None,
-                stream=None):
-        """hidden: bf16 [T, d] CUDA; logits: float32 [T, E] CUDA -> out [T, d]."""
+                stream=None, w_router=None):
+        """hidden: bf16 [T, d] CUDA; logits: float32 [T, E] CUDA -> out [T, d].
+
+        With ``w_router`` (bf16 [E, d] CUDA) and ``logits=None`` the logits are
+        projected from ``hidden`` inside the call (moe_mxfp4_forward_hidden).
+        """
         import torch
+        if (logits is None) == (w_router is None):
+            raise ValueError("pass exactly one of logits and w_router")
         T = hidden.shape[0]
         if out is None:
             dt = torch.bfloat16 if self.out_dtype == OUT_BF16 else torch.float32
@@ -183,13 +193,25 @@ class MoeMxfp4:
         if routing is not None:
             r = Routing(*[_ptr(routing.get(n)) for n in ("topk_ids", "topk_w", "expert_offsets",
                                                          "sorted_pairs")])
-        st = lib().moe_mxfp4_forward(self._ctx, _ptr(hidden), _ptr(logits), T, _ptr(out), _ptr(ws),
-                                     ws.numel() if ws is not None else 0, _stream(stream),
-                                     ctypes.byref(r) if r is not None else None)
-        _check(st, "moe_mxfp4_forward")
+        fn, name = ((lib().moe_mxfp4_forward, "moe_mxfp4_forward") if w_router is None else
+                    (lib().moe_mxfp4_forward_hidden, "moe_mxfp4_forward_hidden"))
+        st = fn(self._ctx, _ptr(hidden), _ptr(logits if w_router is None else w_router), T, _ptr(out),
+                _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream),
+                ctypes.byref(r) if r is not None else None)
+        _check(st, name)
         return out
 
     __call__ = forward
+
+    def router_logits(self, hidden, w_router, out=None, stream=None):
+        """hidden: bf16 [T, d]; w_router: bf16 [E, d] -> float32 logits [T, E]."""
+        import torch
+        T = hidden.shape[0]
+        if out is None:
+            out = torch.empty((T, self.cfg.num_experts), dtype=torch.float32, device=hidden.device)
+        _check(lib().moe_mxfp4_router_logits(self._ctx, _ptr(hidden), _ptr(w_router), T, _ptr(out),
+                                             _stream(stream)), "moe_mxfp4_router_logits")
+        return out
 
     def stage_timing(self, capacity: int):
         """Record HIP events around each stage of the next forward calls."""

@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["api.hip", "route_sort.hip", "expert_gemm.hip", "dense_gemm.hip", "combine.hip", "quant_act.hip"]
+SOURCES = ["api.hip", "router.hip", "route_sort.hip", "expert_gemm.hip", "dense_gemm.hip", "combine.hip",
+           "quant_act.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU forms are disabled for all device code (see DESIGN notes on

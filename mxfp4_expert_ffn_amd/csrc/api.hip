@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/moe_mxfp4.h: argument checks,
 // workspace carve-up and the launch sequence of one forward call.
 //
-// A forward call is five launches on the caller's stream and nothing else
+// A forward call is five to eight launches on the caller's stream and nothing else
 // (no allocation, no host synchronisation, no device-to-host copy), so it can
 // be captured into a HIP graph: the pages stress that at microsecond
 // operator times the gaps between operators matter (techllm.github.io
@@ -32,13 +32,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t ids, w, offsets, sorted, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, total;
+    size_t logits, ids, w, offsets, sorted, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     const size_t P = (size_t)T * c.top_k;
     Layout L{};
     size_t at = 0;
+    L.logits = at;  at += round256((size_t)T * c.num_experts * sizeof(float));   // router projection output
     L.ids = at;     at += round256(P * sizeof(int32_t));
     L.w = at;       at += round256(P * sizeof(float));
     L.offsets = at; at += round256((size_t)(c.num_experts + 1) * sizeof(int32_t));
@@ -178,15 +179,22 @@ size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_ctx* ctx, int32_t num_tokens) {
     return make_layout(ctx->cfg, num_tokens).total;
 }
 
-moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float* router_logits,
-                             int32_t num_tokens, void* out, void* workspace, size_t workspace_bytes,
-                             void* hip_stream, const moe_mxfp4_routing* debug_out) {
+}  // extern "C"
+
+namespace {
+
+// One forward call: router logits given (w_router == NULL) or projected from
+// the hidden states with w_router into the workspace first.
+moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* router_logits, const void* w_router,
+                        int32_t num_tokens, void* out, void* workspace, size_t workspace_bytes,
+                        void* hip_stream, const moe_mxfp4_routing* debug_out) {
     if (!ctx || num_tokens < 0) return MOE_ERR_INVALID_ARG;
     const moe_mxfp4_config& c = ctx->cfg;
     if (num_tokens > c.max_tokens) return MOE_ERR_CAPACITY;
     if (num_tokens == 0) return MOE_OK;
-    if (!hidden || !router_logits || !out) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(hidden) || !aligned16(router_logits) || !aligned16(out)) return MOE_ERR_ALIGNMENT;
+    if (!hidden || !(router_logits || w_router) || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(router_logits ? (const void*)router_logits : w_router) || !aligned16(out))
+        return MOE_ERR_ALIGNMENT;
     const Layout L = make_layout(c, num_tokens);
     if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MOE_ERR_ALIGNMENT;
@@ -198,6 +206,7 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     }
 
     char* base = static_cast<char*>(workspace);
+    float* ws_logits = reinterpret_cast<float*>(base + L.logits);
     moe::Workspace ws;
     ws.topk_ids = reinterpret_cast<int32_t*>(base + L.ids);
     ws.topk_w = reinterpret_cast<float*>(base + L.w);
@@ -224,6 +233,12 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
 
     const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
+    if (w_router) {
+        // the projection is timed with the routing stage
+        if (moe::launch_router(x, static_cast<const uint16_t*>(w_router), ws_logits, dm, s) != hipSuccess)
+            return MOE_ERR_HIP;
+        router_logits = ws_logits;
+    }
     const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
     if (moe::route_sort_fused(dm)) {
         // one launch; its time is recorded as the routing stage
@@ -255,6 +270,41 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
             if (k.dst && hipMemcpyAsync(k.dst, k.src, k.n, hipMemcpyDeviceToDevice, s) != hipSuccess)
                 return MOE_ERR_HIP;
     }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float* router_logits,
+                             int32_t num_tokens, void* out, void* workspace, size_t workspace_bytes,
+                             void* hip_stream, const moe_mxfp4_routing* debug_out) {
+    if (!router_logits && num_tokens > 0) return MOE_ERR_INVALID_ARG;
+    return forward_impl(ctx, hidden, router_logits, nullptr, num_tokens, out, workspace, workspace_bytes,
+                        hip_stream, debug_out);
+}
+
+moe_status moe_mxfp4_forward_hidden(moe_mxfp4_ctx* ctx, const void* hidden, const void* w_router,
+                                    int32_t num_tokens, void* out, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream, const moe_mxfp4_routing* debug_out) {
+    if (!w_router && num_tokens > 0) return MOE_ERR_INVALID_ARG;
+    return forward_impl(ctx, hidden, nullptr, w_router, num_tokens, out, workspace, workspace_bytes, hip_stream,
+                        debug_out);
+}
+
+moe_status moe_mxfp4_router_logits(const moe_mxfp4_ctx* ctx, const void* hidden, const void* w_router,
+                                   int32_t num_tokens, float* logits, void* hip_stream) {
+    if (!ctx || num_tokens < 0) return MOE_ERR_INVALID_ARG;
+    const moe_mxfp4_config& c = ctx->cfg;
+    if (num_tokens > c.max_tokens) return MOE_ERR_CAPACITY;
+    if (num_tokens == 0) return MOE_OK;
+    if (!hidden || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(hidden) || !aligned16(w_router) || !aligned16(logits)) return MOE_ERR_ALIGNMENT;
+    moe::Dims dm{num_tokens, c.d_model, c.d_ff, c.num_experts, c.top_k, num_tokens * c.top_k};
+    if (moe::launch_router(static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(w_router), logits, dm,
+                           static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -120,6 +120,8 @@ inline int max_chunks(const Dims& dm) {
 }
 
 // Kernel launchers (each returns hipGetLastError() of its launch).
+// Router projection: logits [T][E] = x [T][d] . w [E][d]^T (bf16 in, float32 out).
+hipError_t launch_router(const uint16_t* x, const uint16_t* w, float* logits, const Dims& dm, hipStream_t s);
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s);
 // Small batches: routing and permutation in one launch (when route_sort_fused).

@@ -116,6 +116,15 @@ def make_activations(w: Workload, seed: int | None = None) -> dict:
     return {"x_bf16": xb, "x": bf16_bits_to_f32(xb), "logits": logits, "bias": bias}
 
 
+def router_weights_bf16(w: Workload, seed: int | None = None) -> np.ndarray:
+    """Router projection weights, bf16 bit patterns [E, d]: N(0, 0.02) rounded
+    to bf16, so x W^T of the N(0, 1) hidden states has standard deviation
+    0.02 * sqrt(d) (1.28 at d = 4096), the scale of the synthetic logits."""
+    rng = np.random.default_rng([w.seed if seed is None else seed, 2])
+    wr = rng.standard_normal((w.E, w.d), dtype=np.float32) * np.float32(0.02)
+    return bf16_bits_from_f32(wr)
+
+
 def expert_weights_f32(w: Workload, e: int, seed: int | None = None):
     """(W_gate [f, d], W_up [f, d], W_down [d, f]) of expert e, float32 N(0, 0.02)."""
     rng = np.random.default_rng([w.seed if seed is None else seed, 1, e])

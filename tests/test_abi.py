@@ -132,6 +132,33 @@ def test_forward_validation_happens_before_any_launch():
         L.moe_mxfp4_destroy(h)
 
 
+def test_router_entry_points_validate_before_any_launch():
+    st, h = _create()
+    L = moe.lib()
+    need = L.moe_mxfp4_workspace_bytes(h, 8)
+    rl, fh = L.moe_mxfp4_router_logits, L.moe_mxfp4_forward_hidden
+    try:
+        assert rl(None, FAKE, FAKE, 1, FAKE, None) == 1
+        assert rl(h, FAKE, FAKE, -1, FAKE, None) == 1
+        assert rl(h, FAKE, FAKE, 9, FAKE, None) == 3                # > max_tokens
+        assert rl(h, None, None, 0, None, None) == 0                # T = 0 no-op
+        assert rl(h, None, FAKE, 8, FAKE, None) == 1
+        assert rl(h, FAKE, None, 8, FAKE, None) == 1
+        assert rl(h, FAKE, FAKE, 8, None, None) == 1
+        assert rl(h, FAKE + 2, FAKE, 8, FAKE, None) == 4
+        assert rl(h, FAKE, FAKE + 8, 8, FAKE, None) == 4
+        assert rl(h, FAKE, FAKE, 8, FAKE + 4, None) == 4
+        assert fh(h, FAKE, None, 8, FAKE, FAKE, need, None, None) == 1     # no router weights
+        assert fh(h, FAKE, FAKE, 9, FAKE, FAKE, 10**9, None, None) == 3
+        assert fh(h, None, None, 0, None, None, 0, None, None) == 0
+        assert fh(h, FAKE, FAKE + 4, 8, FAKE, FAKE, need, None, None) == 4
+        assert fh(h, FAKE, FAKE, 8, FAKE, FAKE, need - 1, None, None) == 5
+        # the forward path with logits still rejects missing logits
+        assert L.moe_mxfp4_forward(h, FAKE, None, 8, FAKE, FAKE, need, None, None) == 1
+    finally:
+        L.moe_mxfp4_destroy(h)
+
+
 def test_debug_dequant_and_quantize_validation():
     st, h = _create()
     L = moe.lib()
