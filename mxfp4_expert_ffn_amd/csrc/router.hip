@@ -7,21 +7,21 @@
 // section "3. TileRT"); they give no router form, so this is the plain
 // linear map with bf16 x and W and no bias.
 //
-// Workgroup = one tile of 16 tokens x 16 experts, KS wavefronts along K
-// (contiguous ranges, KS up to 16), so that even a small batch spreads over
-// many CUs.  Lane (li, g) of a v_mfma_f32_16x16x32_bf16 step over K [k0,
-// k0 + 32) holds x[token li][k0 + 8g ..] and W[expert li][k0 + 8g ..] --
-// one 16-byte load each, straight from global memory (a K range is read by
-// one wave only, so there is nothing to share through LDS).  The KS partial
-// tiles are added through LDS in split order, so the result does not depend
-// on timing.
+// Workgroup = one tile of 16 TW tokens x 16 EW experts, KS wavefronts along
+// K (contiguous ranges).  Each wave keeps TW x EW accumulator tiles, so a
+// loaded x fragment feeds EW MFMAs and a W fragment TW of them: TW = EW = 1
+// for small batches (many small workgroups: latency), 4 x 4 for large ones
+// (4x less operand traffic per MFMA).  Lane (li, g) of a
+// v_mfma_f32_16x16x32_bf16 step over K [k0, k0 + 32) holds x[token li][k0 +
+// 8g ..] and W[expert li][k0 + 8g ..] -- 16-byte loads straight from global
+// memory (a K range is read by one wave only).  The KS partial tiles are
+// added through LDS in split order, so the result does not depend on timing.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
 constexpr int kRouterWaves = 16;
-constexpr int kUnroll = 8;                  // MFMA steps (32 K each) per loop turn
 
 struct RouterArgs {
     const uint16_t* x;      // [T][d]
@@ -31,41 +31,77 @@ struct RouterArgs {
     int32_t ks;             // waves along K
 };
 
-__global__ __launch_bounds__(kRouterWaves * kWave) void k_router(RouterArgs a) {
-    __shared__ f32x4_t part[kRouterWaves][kWave];
+template <int TW, int EW, int KSMAX, int UNROLL>
+__global__ __launch_bounds__(KSMAX * kWave) void k_router(RouterArgs a) {
+    __shared__ f32x4_t part[KSMAX][TW * EW][kWave];
     const int lane = threadIdx.x % kWave;
     const int ks = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int li = lane % 16, g = lane / 16;
-    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int t0 = blockIdx.x * 16 * TW, e0 = blockIdx.y * 16 * EW;
     const int kr = a.d / a.ks;                               // K range of one split (multiple of 256)
     const int kbeg = ks * kr;
     // rows past T / experts past E repeat the last one; never stored
-    const uint16_t* xrow = a.x + (size_t)min(t0 + li, a.T - 1) * a.d + kbeg + 8 * g;
-    const uint16_t* wrow = a.w + (size_t)min(e0 + li, a.E - 1) * a.d + kbeg + 8 * g;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < kr; k += 32 * kUnroll) {
-        bf16x8_t xa[kUnroll], wb[kUnroll];
+    const uint16_t* xrow[TW];
+    const uint16_t* wrow[EW];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            xa[u] = *reinterpret_cast<const bf16x8_t*>(xrow + k + 32 * u);
-            wb[u] = *reinterpret_cast<const bf16x8_t*>(wrow + k + 32 * u);
+    for (int i = 0; i < TW; ++i) xrow[i] = a.x + (size_t)min(t0 + 16 * i + li, a.T - 1) * a.d + kbeg + 8 * g;
+#pragma unroll
+    for (int j = 0; j < EW; ++j) wrow[j] = a.w + (size_t)min(e0 + 16 * j + li, a.E - 1) * a.d + kbeg + 8 * g;
+    f32x4_t acc[TW][EW];
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int j = 0; j < EW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < kr; k += 32 * UNROLL) {
+        bf16x8_t xa[UNROLL][TW], wb[UNROLL][EW];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+            for (int i = 0; i < TW; ++i) xa[u][i] = *reinterpret_cast<const bf16x8_t*>(xrow[i] + k + 32 * u);
+#pragma unroll
+            for (int j = 0; j < EW; ++j) wb[u][j] = *reinterpret_cast<const bf16x8_t*>(wrow[j] + k + 32 * u);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u], wb[u], acc, 0, 0, 0);
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+#pragma unroll
+                for (int j = 0; j < EW; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[u][i], wb[u][j], acc[i][j], 0, 0, 0);
     }
-    part[ks][lane] = acc;
+#pragma unroll
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int j = 0; j < EW; ++j) part[ks][i * EW + j][lane] = acc[i][j];
     __syncthreads();
     if (ks != 0) return;
-    // lane holds D[token 4g + r][expert li]
-    for (int q = 1; q < a.ks; ++q) acc += part[q][lane];
-    const int e = e0 + li;
-    if (e < a.E) {
+    // lane holds D[token 16 i + 4g + r][expert 16 j + li] of tile (i, j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = t0 + 4 * g + r;
-            if (t < a.T) a.logits[(size_t)t * a.E + e] = acc[r];
+    for (int i = 0; i < TW; ++i)
+#pragma unroll
+        for (int j = 0; j < EW; ++j) {
+            f32x4_t s = acc[i][j];
+            for (int q = 1; q < a.ks; ++q) s += part[q][i * EW + j][lane];
+            const int e = e0 + 16 * j + li;
+            if (e < a.E) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = t0 + 16 * i + 4 * g + r;
+                    if (t < a.T) a.logits[(size_t)t * a.E + e] = s[r];
+                }
+            }
         }
-    }
+}
+
+template <int TW, int EW, int KSMAX, int UNROLL>
+hipError_t launch_tiles(RouterArgs a, hipStream_t s) {
+    // K splits: a power of two up to KSMAX whose K range is a multiple of 256
+    int ks = KSMAX;
+    while (ks > 1 && (a.d % (256 * ks)) != 0) ks /= 2;
+    a.ks = ks;
+    const dim3 grid((a.T + 16 * TW - 1) / (16 * TW), (a.E + 16 * EW - 1) / (16 * EW)), block(ks * kWave);
+    hipLaunchKernelGGL((k_router<TW, EW, KSMAX, UNROLL>), grid, block, 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -74,13 +110,10 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w, float* logits, co
     RouterArgs a{};
     a.x = x; a.w = w; a.logits = logits;
     a.T = dm.T; a.d = dm.d; a.E = dm.E;
-    // K splits: a power of two up to 16 whose K range is a multiple of 256
-    int ks = kRouterWaves;
-    while (ks > 1 && (dm.d % (256 * ks)) != 0) ks /= 2;
-    a.ks = ks;
-    const dim3 grid((dm.T + 15) / 16, (dm.E + 15) / 16), block(ks * kWave);
-    hipLaunchKernelGGL(k_router, grid, block, 0, s, a);
-    return hipGetLastError();
+    // 64 x 64 tiles once they alone fill the GPU, 16 x 16 tiles below that
+    const long big_tiles = (long)((dm.T + 63) / 64) * ((dm.E + 63) / 64);
+    if (big_tiles >= 128) return launch_tiles<4, 4, 8, 2>(a, s);
+    return launch_tiles<1, 1, kRouterWaves, 8>(a, s);
 }
 
 }  // namespace moe

@@ -81,6 +81,29 @@ def test_router_logits_within_rounding_bound(T, d, E):
     print(f"router T={T} d={d} E={E}: max err / bound {float((err / bound).max()):.3e}")
 
 
+@pytest.mark.parametrize("T,d,E,nsample", [
+    (2000, 512, 250, None),                        # 64 x 64 tiles, ragged in tokens and experts
+    (8192, 6144, 128, 48),                         # the 8192-token chunk's shape, sampled rows
+])
+def test_router_logits_large_batches(T, d, E, nsample):
+    moe = _moe()
+    w = synth.Workload("router", T, d, 512, E, 1, "bf16", "none", 650 + E)
+    acts = synth.make_activations(w)
+    wr = synth.router_weights_bf16(w)
+    layer = moe.MoeMxfp4(_unused_weights(), E, d, 512, 1, max_tokens=T)
+    got = layer.router_logits(_dev_bf16(acts["x_bf16"]), _dev_bf16(wr))
+    torch.cuda.synchronize()
+    rows = np.arange(T)
+    if nsample is not None:
+        rng = np.random.default_rng(3)
+        rows = np.unique(np.concatenate([rng.choice(T, size=nsample, replace=False), [0, 63, 64, T - 1]]))
+    ref, absdot = oracle.router_logits(acts["x_bf16"][rows], wr)
+    err = np.abs(got.cpu().numpy()[rows].astype(np.float64) - ref)
+    bound = _bound(d, absdot)
+    assert np.all(err <= bound), float((err / bound).max())
+    print(f"router T={T} d={d} E={E}: max err / bound {float((err / bound).max()):.3e} over {rows.size} rows")
+
+
 def _check_routing(ids_gpu, w_gpu, exact, bound, k):
     """Exact on unambiguous tokens, valid top-k on the rest; returns the mask
     of unambiguous tokens."""
