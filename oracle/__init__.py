@@ -33,6 +33,10 @@ PINS = {
     "orc_quant_mxfp8": "torch E4M3 rounding with the OCP scale rule; round trips",
     "orc_router_logits": "pure-Python brute force on small shapes; one-hot rows pick "
                          "weight entries; sign flip; split-support additivity",
+    "orc_dflash_accept": "losslessness: Monte Carlo distribution of the first emitted token "
+                         "against p_target (chi-square) and acceptance rate against "
+                         "sum min(p_draft, p_target); identical distributions accept all; "
+                         "one-hot targets; draws against an independent searchsorted",
     "orc_route": "brute-force sort on (-logit, index); forced ties; 1-ulp gaps",
     "orc_permute": "stable sort of pair ids by expert; invariants",
     "orc_moe_forward": "dense numpy evaluation over all experts; E=1 matmul "
@@ -70,6 +74,8 @@ def bind(L):
         getattr(L, name).argtypes = [P, i64, i64, P, P]
         getattr(L, name).restype = None
     L.orc_router_logits.argtypes = [P, P, i32, i32, i32, P, P]; L.orc_router_logits.restype = None
+    L.orc_dflash_accept.argtypes = [i32, i32, i32, P, P, P, P, P, P, P]
+    L.orc_dflash_accept.restype = None
     L.orc_route.argtypes = [P, i32, i32, i32, P, P]; L.orc_route.restype = None
     L.orc_permute.argtypes = [P, i32, i32, i32, P, P, P, P]; L.orc_permute.restype = None
     L.orc_moe_forward.argtypes = [i32] * 6 + [P] * 8 + [P, P, P, P, i32]
@@ -162,6 +168,21 @@ def router_logits(x_bf16: np.ndarray, w_bf16: np.ndarray):
     absdot = np.empty((T, E), np.float64)
     lib().orc_router_logits(_p(x_bf16), _p(w_bf16), T, d, E, _p(logits), _p(absdot))
     return logits, absdot
+
+
+def dflash_accept(draft, p_draft, p_target, u, r):
+    """draft int32 [B, G], p_draft float32 [B, G, V], p_target float32 [B, G+1, V],
+    u float32 [B, G], r float32 [B] -> (n_accepted int32 [B], next_token int32 [B])."""
+    draft, u, r = _c(draft, np.int32), _c(u, np.float32), _c(r, np.float32)
+    p_draft, p_target = _c(p_draft, np.float32), _c(p_target, np.float32)
+    B, G = draft.shape
+    V = p_draft.shape[2]
+    assert p_draft.shape == (B, G, V) and p_target.shape == (B, G + 1, V)
+    assert u.shape == (B, G) and r.shape == (B,)
+    n_acc = np.empty(B, np.int32)
+    tok = np.empty(B, np.int32)
+    lib().orc_dflash_accept(B, G, V, _p(draft), _p(p_draft), _p(p_target), _p(u), _p(r), _p(n_acc), _p(tok))
+    return n_acc, tok
 
 
 def route(logits: np.ndarray, k: int):

@@ -236,6 +236,68 @@ void orc_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
 }
 
 /* ------------------------------------------------------------------------ */
+/* DFlash verify acceptance                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Index drawn from weights w[0..V) with the uniform r: integer weights
+ * q_i = rint(2^32 w_i) (w_i in [0, 1]), S = sum q_i, threshold =
+ * floor(S * floor(2^24 r) / 2^24), result = the first i whose inclusive
+ * prefix sum of q exceeds the threshold.  Integer sums make the draw
+ * independent of summation order.  Returns -1 when S == 0. */
+static int32_t draw_index(const float* w, int32_t V, float r) {
+    uint64_t S = 0;
+    for (int32_t i = 0; i < V; ++i) S += (uint64_t)rint((double)w[i] * 4294967296.0);
+    if (S == 0) return -1;
+    const uint64_t r24 = (uint64_t)floor((double)r * 16777216.0);
+    const uint64_t thr = (uint64_t)(((unsigned __int128)S * r24) >> 24);
+    uint64_t run = 0;
+    for (int32_t i = 0; i < V; ++i) {
+        run += (uint64_t)rint((double)w[i] * 4294967296.0);
+        if (run > thr) return i;
+    }
+    return V - 1;                                   /* not reached: run ends at S > thr */
+}
+
+/* The pages make the verification of a drafted block lossless with a final
+ * rejection-sampling pass (techllm.github.io "Xiaomi MiMo x TileRT", section
+ * "2. DFlash") without printing the rule; the reading is standard
+ * speculative sampling.  Position j's draft token x is accepted when
+ * u_j * p_draft[j][x] < p_target[j][x] (u_j < p_target / p_draft, decided
+ * in float32); the first rejection ends the block and the next token is
+ * drawn from max(0, p_target[j] - p_draft[j]) (float32 per element), or from
+ * p_target[j] if that residual rounds to nothing; after G acceptances it is
+ * drawn from p_target[G]. */
+void orc_dflash_accept(int32_t B, int32_t G, int32_t V, const int32_t* draft, const float* p_draft,
+                       const float* p_target, const float* u, const float* r, int32_t* n_accepted,
+                       int32_t* next_token) {
+    float* res = (float*)malloc(sizeof(float) * (size_t)(V > 0 ? V : 1));
+    for (int32_t b = 0; b < B; ++b) {
+        int32_t j = 0;
+        for (; j < G; ++j) {
+            const int32_t x = draft[(int64_t)b * G + j];
+            const float pd = p_draft[((int64_t)b * G + j) * V + x];
+            const float pt = p_target[((int64_t)b * (G + 1) + j) * V + x];
+            const float up = u[(int64_t)b * G + j] * pd;
+            if (!(up < pt)) break;
+        }
+        n_accepted[b] = j;
+        const float* pt_row = p_target + ((int64_t)b * (G + 1) + j) * V;
+        int32_t tok = -1;
+        if (j < G) {
+            const float* pd_row = p_draft + ((int64_t)b * G + j) * V;
+            for (int32_t i = 0; i < V; ++i) {
+                const float dlt = pt_row[i] - pd_row[i];
+                res[i] = dlt > 0.0f ? dlt : 0.0f;
+            }
+            tok = draw_index(res, V, r[b]);
+        }
+        if (tok < 0) tok = draw_index(pt_row, V, r[b]);
+        next_token[b] = tok;
+    }
+    free(res);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Expert layer                                                               */
 /* ------------------------------------------------------------------------ */
 

@@ -60,6 +60,14 @@ void orc_dequant_mxfp8(const uint8_t* codes, const uint8_t* scales,
 void orc_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int32_t T, int32_t d,
                        int32_t E, double* logits, double* absdot);
 
+/* ---- DFlash verify acceptance (rejection sampling over a block) ---- */
+/* B sequences, blocks of G draft tokens, vocabulary V.  draft [B][G],
+ * p_draft [B][G][V], p_target [B][G+1][V], u [B][G], r [B] (uniforms in
+ * [0, 1)).  Out: n_accepted [B] (0..G) and next_token [B]. */
+void orc_dflash_accept(int32_t B, int32_t G, int32_t V, const int32_t* draft, const float* p_draft,
+                       const float* p_target, const float* u, const float* r, int32_t* n_accepted,
+                       int32_t* next_token);
+
 /* ---- routing and permutation ---- */
 void orc_route(const float* logits, int32_t T, int32_t E, int32_t k,
                int32_t* topk_ids, double* topk_w);

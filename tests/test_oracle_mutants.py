@@ -31,6 +31,10 @@ MUTANTS = {
     "router_transposed": ("const uint16_t* we = w_bf16 + (int64_t)e * d;",
                           "const uint16_t* we = w_bf16 + (int64_t)e;"),
     "router_abs_of_sum": ("a += fabs(p);", "a += p;"),
+    "dflash_accept_reversed": ("if (!(up < pt)) break;", "if (up < pt) break;"),
+    "dflash_residual_sign": ("const float dlt = pt_row[i] - pd_row[i];", "const float dlt = pd_row[i] - pt_row[i];"),
+    "dflash_prefix_ge": ("if (run > thr) return i;", "if (run >= thr) return i;"),
+    "dflash_no_residual": ("tok = draw_index(res, V, r[b]);", "tok = draw_index(pt_row, V, r[b]);"),
     "route_tie_high": ("(best < 0 || l[e] > l[best])", "(best < 0 || l[e] >= l[best])"),
     "softmax_sign": ("sum += exp((double)l[ids[j]] - l0);",
                      "sum += exp(l0 - (double)l[ids[j]]);"),

@@ -268,6 +268,110 @@ def test_router_sign_flip_and_split_support_additivity():
     assert np.all(absdot >= np.abs(full))
 
 
+# ------------------------------------------------------- dflash acceptance
+
+def _dirichlet(rng, shape, V, alpha=0.5):
+    p = rng.gamma(alpha, size=shape + (V,))
+    return (p / p.sum(axis=-1, keepdims=True)).astype(np.float32)
+
+
+def _draw_searchsorted(w, r):
+    """Independent integer inverse CDF: numpy cumulative sum and searchsorted."""
+    q = np.rint(np.asarray(w, np.float64) * 2.0 ** 32).astype(np.uint64)
+    cum = np.cumsum(q, dtype=np.uint64)
+    S = int(cum[-1])
+    thr = (S * int(np.floor(np.float64(r) * 2.0 ** 24))) >> 24
+    return int(np.searchsorted(cum, np.uint64(thr), side="right"))
+
+
+def test_dflash_first_token_is_distributed_as_the_target():
+    # losslessness: whatever the drafter proposes, the first emitted token
+    # (the accepted draft, or the draw after a rejection) follows p_target
+    rng = np.random.default_rng(51)
+    V, G, N = 6, 3, 200000
+    pt1 = _dirichlet(rng, (G + 1,), V)
+    pd1 = _dirichlet(rng, (G,), V)
+    p64 = pd1.astype(np.float64)
+    p64 /= p64.sum(axis=1, keepdims=True)
+    draft = np.stack([rng.choice(V, size=N, p=p64[j]) for j in range(G)], 1)
+    u = rng.random((N, G), dtype=np.float32)
+    r = rng.random(N, dtype=np.float32)
+    n_acc, tok = oracle.dflash_accept(draft, np.broadcast_to(pd1, (N, G, V)), np.broadcast_to(pt1, (N, G + 1, V)), u, r)
+    first = np.where(n_acc >= 1, draft[:, 0], tok)
+    counts = np.bincount(first, minlength=V)
+    expect = pt1[0].astype(np.float64) / pt1[0].sum() * N
+    chi2 = float(((counts - expect) ** 2 / expect).sum())
+    assert chi2 < 35.0, chi2                        # 5 degrees of freedom: p < 2e-6 to fail
+    # acceptance rate of position 0: sum_x min(p_draft(x), p_target(x))
+    acc = float(np.minimum(pd1[0], pt1[0]).sum())
+    sd = math.sqrt(acc * (1 - acc) / N)
+    assert abs((n_acc >= 1).mean() - acc) < 6 * sd
+
+
+def test_dflash_identical_distributions_accept_the_whole_block():
+    rng = np.random.default_rng(52)
+    B, G, V = 20, 8, 50
+    pt = _dirichlet(rng, (B, G + 1), V)
+    draft = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    pt[np.arange(B)[:, None], np.arange(G)[None, :], draft] += 0.01   # every draft token has p > 0
+    u = rng.random((B, G), dtype=np.float32)
+    r = rng.random(B, dtype=np.float32)
+    n_acc, tok = oracle.dflash_accept(draft, pt[:, :G], pt, u, r)
+    assert np.all(n_acc == G)
+    for b in range(B):
+        assert tok[b] == _draw_searchsorted(pt[b, G], r[b]), b
+
+
+def test_dflash_one_hot_target_rejects_and_draws_its_token():
+    rng = np.random.default_rng(53)
+    B, G, V = 16, 4, 32
+    pd = _dirichlet(rng, (B, G), V)
+    pt = np.zeros((B, G + 1, V), np.float32)
+    want = rng.integers(0, V, size=B)
+    draft = (want[:, None] + 1 + rng.integers(0, V - 1, size=(B, G))) % V   # never the target's token
+    pt[np.arange(B), 0, want] = 1.0
+    u = rng.random((B, G), dtype=np.float32)
+    r = rng.random(B, dtype=np.float32)
+    n_acc, tok = oracle.dflash_accept(draft.astype(np.int32), pd, pt, u, r)
+    assert np.all(n_acc == 0)
+    assert np.array_equal(tok, want)
+
+
+def test_dflash_draw_skips_zero_weights():
+    # a draw never lands on a zero-weight token, at either end of r's range
+    G, V = 2, 8
+    pt = np.zeros((4, G + 1, V), np.float32)
+    pt[:, :G, 1] = 1.0                               # the drafts (token 1) are accepted
+    pt[:, G, 2:4] = 0.5                              # the bonus draw: tokens 2 and 3 only
+    draft = np.ones((4, G), np.int32)
+    u = np.zeros((4, G), np.float32)
+    r = np.array([0.0, 0.4999, 0.5, np.float32(1.0) - np.float32(2.0 ** -24)], np.float32)
+    n_acc, tok = oracle.dflash_accept(draft, pt[:, :G], pt, u, r)
+    assert np.all(n_acc == G)
+    assert tok.tolist() == [2, 2, 3, 3]
+
+
+def test_dflash_draws_match_independent_searchsorted():
+    rng = np.random.default_rng(54)
+    B, G, V = 64, 2, 1000
+    pt = _dirichlet(rng, (B, G + 1), V, alpha=0.2)
+    pd = _dirichlet(rng, (B, G), V, alpha=0.2)
+    draft = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    u = rng.random((B, G), dtype=np.float32)
+    r = rng.random(B, dtype=np.float32)
+    r[:4] = [0.0, np.float32(1.0) - np.float32(2.0 ** -24), 0.5, 2.0 ** -20]
+    n_acc, tok = oracle.dflash_accept(draft, pd, pt, u, r)
+    for b in range(B):
+        j = n_acc[b]
+        if j < G:
+            w = np.maximum(pt[b, j] - pd[b, j], np.float32(0.0))
+            assert not (u[b, j] * pd[b, j, draft[b, j]] < pt[b, j, draft[b, j]]), b
+        else:
+            w = pt[b, G]
+        assert tok[b] == _draw_searchsorted(w, r[b]), b
+        assert all(u[b, i] * pd[b, i, draft[b, i]] < pt[b, i, draft[b, i]] for i in range(j)), b
+
+
 def test_route_matches_bruteforce():
     for logits, k in _route_cases():
         ids, w = oracle.route(logits, k)
