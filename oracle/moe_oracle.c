@@ -239,23 +239,34 @@ void orc_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
 /* DFlash verify acceptance                                                   */
 /* ------------------------------------------------------------------------ */
 
+/* Integer weight of one entry: rint(2^32 w) for w > 0; zero for w <= 0 and
+ * for NaN (entries outside a probability's range carry no mass). */
+static uint64_t int_weight(float w) {
+    return w > 0.0f ? (uint64_t)rint((double)w * 4294967296.0) : 0;
+}
+
 /* Index drawn from weights w[0..V) with the uniform r: integer weights
- * q_i = rint(2^32 w_i) (w_i in [0, 1]), S = sum q_i, threshold =
- * floor(S * floor(2^24 r) / 2^24), result = the first i whose inclusive
- * prefix sum of q exceeds the threshold.  Integer sums make the draw
- * independent of summation order.  Returns -1 when S == 0. */
+ * q_i = int_weight(w_i), S = sum q_i, threshold = floor(S * r24 / 2^24) with
+ * r24 = floor(2^24 r) clamped to [0, 2^24 - 1] (r below 0 or NaN counts as
+ * 0, r at or above 1 as the largest float below 1), result = the first i
+ * whose inclusive prefix sum of q exceeds the threshold.  Integer sums make
+ * the draw independent of summation order.  Returns -1 when S == 0. */
 static int32_t draw_index(const float* w, int32_t V, float r) {
     uint64_t S = 0;
-    for (int32_t i = 0; i < V; ++i) S += (uint64_t)rint((double)w[i] * 4294967296.0);
+    for (int32_t i = 0; i < V; ++i) S += int_weight(w[i]);
     if (S == 0) return -1;
-    const uint64_t r24 = (uint64_t)floor((double)r * 16777216.0);
+    uint64_t r24 = 0;
+    if (r > 0.0f) {
+        const double f = floor((double)r * 16777216.0);
+        r24 = f >= 16777215.0 ? 16777215u : (uint64_t)f;
+    }
     const uint64_t thr = (uint64_t)(((unsigned __int128)S * r24) >> 24);
     uint64_t run = 0;
     for (int32_t i = 0; i < V; ++i) {
-        run += (uint64_t)rint((double)w[i] * 4294967296.0);
+        run += int_weight(w[i]);
         if (run > thr) return i;
     }
-    return V - 1;                                   /* not reached: run ends at S > thr */
+    return -1;                                      /* not reached: thr < S */
 }
 
 /* The pages make the verification of a drafted block lossless with a final
@@ -266,7 +277,8 @@ static int32_t draw_index(const float* w, int32_t V, float r) {
  * in float32); the first rejection ends the block and the next token is
  * drawn from max(0, p_target[j] - p_draft[j]) (float32 per element), or from
  * p_target[j] if that residual rounds to nothing; after G acceptances it is
- * drawn from p_target[G]. */
+ * drawn from p_target[G].  A draft token outside [0, V) is rejected (it has
+ * no probability to compare). */
 void orc_dflash_accept(int32_t B, int32_t G, int32_t V, const int32_t* draft, const float* p_draft,
                        const float* p_target, const float* u, const float* r, int32_t* n_accepted,
                        int32_t* next_token) {
@@ -275,6 +287,7 @@ void orc_dflash_accept(int32_t B, int32_t G, int32_t V, const int32_t* draft, co
         int32_t j = 0;
         for (; j < G; ++j) {
             const int32_t x = draft[(int64_t)b * G + j];
+            if (x < 0 || x >= V) break;
             const float pd = p_draft[((int64_t)b * G + j) * V + x];
             const float pt = p_target[((int64_t)b * (G + 1) + j) * V + x];
             const float up = u[(int64_t)b * G + j] * pd;

@@ -63,7 +63,10 @@ void orc_router_logits(const uint16_t* x_bf16, const uint16_t* w_bf16, int32_t T
 /* ---- DFlash verify acceptance (rejection sampling over a block) ---- */
 /* B sequences, blocks of G draft tokens, vocabulary V.  draft [B][G],
  * p_draft [B][G][V], p_target [B][G+1][V], u [B][G], r [B] (uniforms in
- * [0, 1)).  Out: n_accepted [B] (0..G) and next_token [B]. */
+ * [0, 1)).  Out: n_accepted [B] (0..G) and next_token [B] (-1 if the row
+ * drawn from has no positive entry).  Readings for inputs outside the
+ * method's domain: a draft token outside [0, V) is rejected; entries that
+ * are not positive (NaN included) weigh nothing; r is clamped into [0, 1). */
 void orc_dflash_accept(int32_t B, int32_t G, int32_t V, const int32_t* draft, const float* p_draft,
                        const float* p_target, const float* u, const float* r, int32_t* n_accepted,
                        int32_t* next_token);

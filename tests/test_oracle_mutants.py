@@ -35,6 +35,8 @@ MUTANTS = {
     "dflash_residual_sign": ("const float dlt = pt_row[i] - pd_row[i];", "const float dlt = pd_row[i] - pt_row[i];"),
     "dflash_prefix_ge": ("if (run > thr) return i;", "if (run >= thr) return i;"),
     "dflash_no_residual": ("tok = draw_index(res, V, r[b]);", "tok = draw_index(pt_row, V, r[b]);"),
+    "dflash_no_fallback": ("if (tok < 0) tok = draw_index(pt_row, V, r[b]);", ""),
+    "dflash_r_unclamped": ("r24 = f >= 16777215.0 ? 16777215u : (uint64_t)f;", "r24 = (uint64_t)f;"),
     "route_tie_high": ("(best < 0 || l[e] > l[best])", "(best < 0 || l[e] >= l[best])"),
     "softmax_sign": ("sum += exp((double)l[ids[j]] - l0);",
                      "sum += exp(l0 - (double)l[ids[j]]);"),

@@ -372,6 +372,78 @@ def test_dflash_draws_match_independent_searchsorted():
         assert all(u[b, i] * pd[b, i, draft[b, i]] < pt[b, i, draft[b, i]] for i in range(j)), b
 
 
+def test_dflash_zero_residual_falls_back_to_the_target_row():
+    # p_target = p_draft / 2 (not normalised): max(0, p_target - p_draft) is
+    # zero everywhere, so a rejection draws from p_target itself
+    rng = np.random.default_rng(55)
+    B, G, V = 24, 3, 40
+    pd = _dirichlet(rng, (B, G), V)
+    pt = np.concatenate([pd * np.float32(0.5), _dirichlet(rng, (B, 1), V)], axis=1)
+    draft = rng.integers(0, V, size=(B, G)).astype(np.int32)
+    u = np.full((B, G), 0.75, np.float32)           # 0.75 p_draft >= p_draft / 2: rejected at once
+    r = rng.random(B, dtype=np.float32)
+    n_acc, tok = oracle.dflash_accept(draft, pd, pt, u, r)
+    assert np.all(n_acc == 0)
+    for b in range(B):
+        assert tok[b] == _draw_searchsorted(pt[b, 0], r[b]), b
+
+
+def test_dflash_out_of_range_draft_is_rejected():
+    # a token outside [0, V) ends the block like one the target gives no mass
+    rng = np.random.default_rng(56)
+    B, G, V = 12, 4, 30
+    pd = _dirichlet(rng, (B, G), V)
+    pt = _dirichlet(rng, (B, G + 1), V)
+    draft = rng.integers(1, V, size=(B, G)).astype(np.int32)
+    pt[np.arange(B)[:, None], np.arange(G)[None, :], draft] += 0.05   # the in-range drafts are likely kept
+    u = np.zeros((B, G), np.float32)                # u = 0: every token with p_target > 0 is accepted
+    r = rng.random(B, dtype=np.float32)
+    jbad = np.arange(B) % G
+    bad = draft.copy()
+    bad[np.arange(B), jbad] = np.where(np.arange(B) % 2 == 0, -1, V)
+    zero = draft.copy()
+    zero[np.arange(B), jbad] = 0
+    pt0 = pt.copy()
+    pt0[np.arange(B), jbad, 0] = 0.0                 # token 0 has no target mass at the bad position
+    n_bad, tok_bad = oracle.dflash_accept(bad, pd, pt0, u, r)
+    n_zero, tok_zero = oracle.dflash_accept(zero, pd, pt0, u, r)
+    assert np.array_equal(n_bad, jbad)
+    assert np.array_equal(n_bad, n_zero) and np.array_equal(tok_bad, tok_zero)
+
+
+def test_dflash_non_positive_weights_count_as_zero():
+    # negative and NaN entries of the row drawn from carry no mass
+    rng = np.random.default_rng(57)
+    B, V = 16, 64
+    pt = _dirichlet(rng, (B, 1), V)
+    junk = pt.copy()
+    mask = rng.random((B, 1, V)) < 0.3
+    vals = np.where(rng.random((B, 1, V)) < 0.5, np.float32(-0.25), np.float32(np.nan))
+    junk[mask] = vals[mask]
+    clean = np.where(mask, np.float32(0.0), pt)
+    draft = np.zeros((B, 0), np.int32)
+    pd = np.zeros((B, 0, V), np.float32)
+    r = rng.random(B, dtype=np.float32)
+    _, tok_junk = oracle.dflash_accept(draft, pd, junk, np.zeros((B, 0), np.float32), r)
+    _, tok_clean = oracle.dflash_accept(draft, pd, clean, np.zeros((B, 0), np.float32), r)
+    assert np.array_equal(tok_junk, tok_clean)
+    assert not np.any(mask[np.arange(B), 0, tok_junk])
+
+
+def test_dflash_r_outside_the_unit_interval_is_clamped():
+    rng = np.random.default_rng(58)
+    V = 20
+    pt = _dirichlet(rng, (1, 1), V)
+    pt[0, 0, [0, 1, V - 1]] = 0.0                    # first and last positive weights at 2 and V - 2
+    one_minus = np.float32(1.0) - np.float32(2.0 ** -24)
+    rs = np.array([-0.5, np.nan, 0.0, 1.0, 2.0, np.inf, one_minus], np.float32)
+    n = rs.size
+    _, tok = oracle.dflash_accept(np.zeros((n, 0), np.int32), np.zeros((n, 0, V), np.float32),
+                                  np.broadcast_to(pt, (n, 1, V)), np.zeros((n, 0), np.float32), rs)
+    assert tok[:3].tolist() == [2, 2, 2]            # at or below 0: the first positive weight
+    assert tok[3:].tolist() == [V - 2] * 4           # at or above 1: as the largest float below 1
+
+
 def test_route_matches_bruteforce():
     for logits, k in _route_cases():
         ids, w = oracle.route(logits, k)
