@@ -97,6 +97,20 @@ def cpu_baseline(w, acts, ntok, router_bits=None):
                       f"fp64 C oracle, OpenMP over tokens; {dt:.2f} s wall"}
 
 
+def cpu_baseline_accept(inp):
+    """The oracle's acceptance pass over the same batch (one thread)."""
+    import oracle
+    args = [inp[k] for k in ("draft", "p_draft", "p_target", "u", "r")]
+    reps, t0 = 0, time.perf_counter()
+    while reps < 3 or time.perf_counter() - t0 < 1.0:
+        oracle.dflash_accept(*args)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    B = inp["draft"].shape[0]
+    return {"value": B / dt, "unit": "sequences/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole batch ({B} sequences), {reps} calls; {dt * 1e3:.2f} ms per call"}
+
+
 def measured_traffic(workload, mx8):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy
@@ -119,6 +133,36 @@ def measured_traffic(workload, mx8):
     return float(fields["traffic bytes per launch"])
 
 
+def time_accept(w, args, moe, torch, np, synth):
+    """The acceptance pass over the batch's sequences: every row it reads is
+    an HBM stream (4 bytes per vocabulary entry), so it is priced against HBM."""
+    B, G, V = w.T // 8, 8, synth.DFLASH_VOCAB
+    inp = synth.dflash_batch(B, G, V, seed=w.seed + 7)
+    dev = [torch.from_numpy(inp[k]).cuda() for k in ("draft", "p_draft", "p_target", "u", "r")]
+    n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    wsa = torch.empty(moe.dflash_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        moe.dflash_accept(*dev, n_accepted=n_acc, next_token=tok, workspace=wsa)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        moe.dflash_accept(*dev, n_accepted=n_acc, next_token=tok, workspace=wsa)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    n = n_acc.cpu().numpy()
+    # rows streamed: p_target and p_draft at the rejected position, or p_target[G]
+    rows = int(np.where(n < G, 2, 1).sum())
+    nbytes = rows * V * 4 + B * G * (4 + 4 + 2 * 64) + B * (4 + 4 + 4 + 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"dflash acceptance: {us:.1f} us per call, {gbs:.0f} GB/s, mean accepted {n.mean():.2f}")
+    return {"workload": f"{B} sequences x block {G}, vocabulary {V}, float32 distributions",
+            "us_per_call": us, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes, "mean_accepted": float(n.mean()),
+            "whole_block_accepted": float((n == G).mean())}, inp
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +175,9 @@ def main():
     ap.add_argument("--with-router", action="store_true",
                     help="time the forward call with the router projection in front (logits = x W_router^T "
                          "computed inside the call) instead of taking the logits as input")
+    ap.add_argument("--with-accept", action="store_true",
+                    help="also time the DFlash verify acceptance (rejection sampling) of the batch's "
+                         "sequences over a full vocabulary, as its own figure")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the measurements, run a plain device copy (torch.neg, float32) of this many "
                          "MiB: the reference dispatch for scaling HBM byte counters")
@@ -259,6 +306,8 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         result["router_projection_us"] = e0.elapsed_time(e1) * 1e3 / args.steps
+    if args.with_accept:
+        result["dflash_accept"], accept_inputs = time_accept(w, args, moe, torch, np, synth)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 18                   # float32 elements
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -271,6 +320,8 @@ def main():
         log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
         rb = synth.router_weights_bf16(w) if wr is not None else None
         result["cpu_baseline"] = cpu_baseline(w, acts, args.cpu_tokens, rb)
+        if args.with_accept:
+            result["dflash_accept"]["cpu_baseline"] = cpu_baseline_accept(accept_inputs)
     print(json.dumps(result), flush=True)
 
 

@@ -238,6 +238,49 @@ moe_status moe_mxfp4_forward_hidden(moe_mxfp4_ctx* ctx, const void* hidden,
                                     void* hip_stream, const moe_mxfp4_routing* debug_out);
 
 /*
+ * DFlash verify acceptance: the rejection-sampling pass that ends a verify
+ * step and makes block drafting lossless (techllm.github.io "Xiaomi MiMo x
+ * TileRT", section "2. DFlash"; blocks of at most 8 drafted tokens).  The
+ * pages do not print the rule; this is standard speculative sampling, per
+ * sequence b:
+ *   - position j = 0, 1, ... of the block: the draft token x = draft[b][j]
+ *     is accepted when u[b][j] * p_draft[b][j][x] < p_target[b][j][x]
+ *     (float32); a token outside [0, V) is rejected; the first rejection
+ *     ends the block.  n_accepted[b] = the number accepted (0..G).
+ *   - next_token[b] is drawn with r[b] from max(0, p_target[b][j] -
+ *     p_draft[b][j]) (float32 per entry) after a rejection at j, or from
+ *     p_target[b][j] if that residual has no positive entry, or from
+ *     p_target[b][G] when the whole block is accepted.
+ *   - a draw: integer weights q_i = rint(2^32 w_i) (0 for w_i <= 0 or NaN),
+ *     S = sum_i q_i, threshold = floor(S * r24 / 2^24) with r24 = floor(2^24
+ *     r) clamped to [0, 2^24 - 1], result = the first i whose inclusive
+ *     prefix sum of q exceeds the threshold; -1 if S = 0.  Integer sums make
+ *     the result exact and independent of how the row is split over threads.
+ * All arrays are device memory, row-major:
+ *   draft      int32 [B][G]          drafted tokens
+ *   p_draft    float [B][G][V]       drafter distributions at the G positions
+ *   p_target   float [B][G+1][V]     target distributions at the G+1 positions
+ *   u          float [B][G]          uniforms of the acceptance tests
+ *   r          float [B]             uniforms of the draws
+ *   n_accepted int32 [B], next_token int32 [B]   outputs
+ *   workspace  >= moe_mxfp4_dflash_workspace_bytes(B, V) bytes, caller-owned,
+ *              no initial contents needed; calls that overlap in time need
+ *              distinct workspaces.
+ * Limits: 0 <= G <= 64, 1 <= V <= 2^30, 0 <= B <= 65535 (B = 0 is a no-op).
+ * Entries are probabilities: rows need not be normalised, but every row's
+ * sum must stay below 2^31.  Not context-bound: no moe_mxfp4_ctx.
+ * Errors: INVALID_ARG (null pointer, size out of range), ALIGNMENT,
+ * WORKSPACE (too small), HIP.
+ */
+size_t moe_mxfp4_dflash_workspace_bytes(int32_t batch, int32_t vocab);
+moe_status moe_mxfp4_dflash_accept(int32_t batch, int32_t block, int32_t vocab,
+                                   const int32_t* draft, const float* p_draft,
+                                   const float* p_target, const float* u,
+                                   const float* r, int32_t* n_accepted,
+                                   int32_t* next_token, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream);
+
+/*
  * Decode rows [row0, row0 + nrows) of one expert matrix (0 gate, 1 up,
  * 2 down) from the context's TILED weights with the forward path's own
  * in-register FP4 decode, widened to float: out (device) float [nrows][K]

@@ -7,7 +7,8 @@ and there is no CPU fallback -- if the library is missing, loading fails.
 
 Names follow the C ABI: ``MoeMxfp4`` wraps ``moe_mxfp4_create / _forward /
 _destroy / _workspace_bytes / _debug_dequant``; ``quantize_weights`` wraps
-``moe_mxfp4_quantize_weights``.
+``moe_mxfp4_quantize_weights``; ``dflash_accept`` wraps
+``moe_mxfp4_dflash_accept`` (the rejection-sampling pass of a verify step).
 """
 from __future__ import annotations
 
@@ -29,7 +30,8 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create
            "moe_mxfp4_destroy", "moe_mxfp4_workspace_bytes", "moe_mxfp4_forward",
            "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights", "moe_mxfp4_stage_timing",
            "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights",
-           "moe_mxfp4_quantize_act_mxfp8", "moe_mxfp4_router_logits", "moe_mxfp4_forward_hidden")
+           "moe_mxfp4_quantize_act_mxfp8", "moe_mxfp4_router_logits", "moe_mxfp4_forward_hidden",
+           "moe_mxfp4_dflash_workspace_bytes", "moe_mxfp4_dflash_accept")
 NUM_STAGES = 6
 STAGES = ("route", "sort", "quant", "gateup", "down", "combine")
 
@@ -96,6 +98,10 @@ def lib():
         L.moe_mxfp4_tiled_scale_bytes.restype = sz
         L.moe_mxfp4_tile_weights.argtypes = [P, P, i64, i64, P, P, P]
         L.moe_mxfp4_tile_weights.restype = ctypes.c_int
+        L.moe_mxfp4_dflash_workspace_bytes.argtypes = [i32, i32]
+        L.moe_mxfp4_dflash_workspace_bytes.restype = sz
+        L.moe_mxfp4_dflash_accept.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
+        L.moe_mxfp4_dflash_accept.restype = ctypes.c_int
         L.moe_mxfp4_stage_timing.argtypes = [P, i32]
         L.moe_mxfp4_stage_timing.restype = ctypes.c_int
         L.moe_mxfp4_stage_times.argtypes = [P, ctypes.POINTER(ctypes.c_float),
@@ -286,3 +292,36 @@ def quantize_act_mxfp8(x, codes=None, scales=None, stream=None):
     _check(lib().moe_mxfp4_quantize_act_mxfp8(_ptr(x), rows, K, _ptr(codes), _ptr(scales),
                                               _stream(stream)), "moe_mxfp4_quantize_act_mxfp8")
     return codes, scales
+
+
+def dflash_workspace_bytes(batch: int, vocab: int) -> int:
+    return lib().moe_mxfp4_dflash_workspace_bytes(batch, vocab)
+
+
+def dflash_accept(draft, p_draft, p_target, u, r, n_accepted=None, next_token=None, workspace=None,
+                  stream=None):
+    """Rejection-sampling acceptance of drafted blocks (moe_mxfp4_dflash_accept).
+
+    draft int32 [B, G], p_draft float32 [B, G, V], p_target float32 [B, G+1, V],
+    u float32 [B, G], r float32 [B], all contiguous CUDA tensors ->
+    (n_accepted int32 [B], next_token int32 [B]).
+    """
+    import torch
+    B, G = draft.shape
+    V = p_target.shape[2]
+    if p_target.shape != (B, G + 1, V) or p_draft.shape != (B, G, V) or u.shape != (B, G) or r.shape != (B,):
+        raise ValueError("dflash_accept: inconsistent shapes")
+    for t in (draft, p_draft, p_target, u, r):
+        if not t.is_contiguous():
+            raise ValueError("dflash_accept: inputs must be contiguous")
+    if n_accepted is None:
+        n_accepted = torch.empty(B, dtype=torch.int32, device=p_target.device)
+    if next_token is None:
+        next_token = torch.empty(B, dtype=torch.int32, device=p_target.device)
+    if workspace is None:
+        workspace = torch.empty(max(dflash_workspace_bytes(B, V), 256), dtype=torch.uint8,
+                                device=p_target.device)
+    _check(lib().moe_mxfp4_dflash_accept(B, G, V, _ptr(draft), _ptr(p_draft), _ptr(p_target), _ptr(u),
+                                         _ptr(r), _ptr(n_accepted), _ptr(next_token), _ptr(workspace),
+                                         workspace.numel(), _stream(stream)), "moe_mxfp4_dflash_accept")
+    return n_accepted, next_token

@@ -308,6 +308,31 @@ moe_status moe_mxfp4_router_logits(const moe_mxfp4_ctx* ctx, const void* hidden,
     return MOE_OK;
 }
 
+size_t moe_mxfp4_dflash_workspace_bytes(int32_t batch, int32_t vocab) {
+    if (batch < 0 || batch > 65535 || vocab < 1 || vocab > (1 << 30)) return 0;
+    return moe::dflash_workspace_bytes(batch, vocab);
+}
+
+moe_status moe_mxfp4_dflash_accept(int32_t batch, int32_t block, int32_t vocab, const int32_t* draft,
+                                   const float* p_draft, const float* p_target, const float* u, const float* r,
+                                   int32_t* n_accepted, int32_t* next_token, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
+    if (batch < 0 || batch > 65535 || block < 0 || block > 64 || vocab < 1 || vocab > (1 << 30))
+        return MOE_ERR_INVALID_ARG;
+    if (batch == 0) return MOE_OK;
+    if (!p_target || !r || !n_accepted || !next_token || (block > 0 && (!draft || !p_draft || !u)))
+        return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {draft, p_draft, p_target, u, r, n_accepted, next_token};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_ERR_ALIGNMENT;
+    if (!workspace || workspace_bytes < moe::dflash_workspace_bytes(batch, vocab)) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_ERR_ALIGNMENT;
+    if (moe::launch_dflash_accept(batch, block, vocab, draft, p_draft, p_target, u, r, n_accepted, next_token,
+                                  workspace, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert, int32_t matrix,
                                    int32_t row0, int32_t nrows, float* out, void* hip_stream) {
     if (!ctx || !out) return MOE_ERR_INVALID_ARG;

@@ -122,6 +122,12 @@ inline int max_chunks(const Dims& dm) {
 // Kernel launchers (each returns hipGetLastError() of its launch).
 // Router projection: logits [T][E] = x [T][d] . w [E][d]^T (bf16 in, float32 out).
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, float* logits, const Dims& dm, hipStream_t s);
+// DFlash verify acceptance over B sequences (two launches); the workspace
+// holds dflash_workspace_bytes(B, V) bytes.
+size_t dflash_workspace_bytes(int32_t B, int32_t V);
+hipError_t launch_dflash_accept(int32_t B, int32_t G, int32_t V, const int32_t* draft, const float* p_draft,
+                                const float* p_target, const float* u, const float* r, int32_t* n_accepted,
+                                int32_t* next_token, void* workspace, hipStream_t s);
 hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s);
 // Small batches: routing and permutation in one launch (when route_sort_fused).

@@ -17,6 +17,15 @@ Recipe (one workload = one ``Workload`` below):
   N(0, 0.02) float32, drawn from a stream of their own per expert so that any
   subset of experts can be regenerated alone and in parallel.
 
+* DFlash verify batches (``dflash_batch``): per sequence and position,
+  target logits N(0, sigma^2) over the vocabulary (sigma = 4: about 4.8
+  nats of entropy) and drafter logits = target logits + N(0, eps^2) (eps =
+  0.15), each turned into a distribution by a float64 softmax rounded to
+  float32; draft tokens are drawn from the drafter distributions, u and r
+  are uniform float32 in [0, 1).  With these values the drafter's tokens
+  are accepted about 95% of the time, 6.4 of a block of 8 on average -- the
+  acceptance length the pages report for coding (6.30).
+
 Streams: ``numpy.random.default_rng([seed, 0])`` for x then logits then bias;
 ``numpy.random.default_rng([seed, 1, e])`` for expert e's three matrices in
 the order gate, up, down.  The default seed of a named workload is
@@ -32,7 +41,7 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "make_activations",
            "expert_weights_f32", "all_expert_weights_f32", "bf16_bits_from_f32",
-           "bf16_bits_to_f32"]
+           "bf16_bits_to_f32", "router_weights_bf16", "dflash_batch", "DFLASH_VOCAB"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -158,3 +167,39 @@ def all_expert_weights_f32(w: Workload, experts=None, seed: int | None = None,
             if nxt is not None:
                 pending.append((nxt, ex.submit(expert_weights_f32, w, nxt, seed)))
             yield (e, *fut.result())
+
+
+# The pages give no vocabulary size; 152064 entries is the size class of
+# current open LLM tokenisers (a multiple of 256).
+DFLASH_VOCAB = 152064
+
+
+def _softmax_f32(z: np.ndarray) -> np.ndarray:
+    z = z - z.max(axis=-1, keepdims=True)
+    np.exp(z, out=z)
+    z /= z.sum(axis=-1, keepdims=True)
+    return z.astype(np.float32)
+
+
+def dflash_batch(B: int, G: int, V: int, seed: int, sigma: float = 4.0, eps: float = 0.15) -> dict:
+    """One verify step's inputs for the acceptance pass: ``draft`` int32 [B, G],
+    ``p_draft`` float32 [B, G, V], ``p_target`` float32 [B, G+1, V], ``u``
+    float32 [B, G], ``r`` float32 [B].  Stream ``default_rng([seed, 3])``."""
+    rng = np.random.default_rng([seed, 3])
+    zt = rng.standard_normal((B, G + 1, V)) * sigma
+    zd = zt[:, :G] + rng.standard_normal((B, G, V)) * eps
+    p_target = _softmax_f32(zt)
+    del zt
+    p_draft = _softmax_f32(zd)
+    del zd
+    # draft tokens: inverse CDF of the drafter distribution (float64 cumulative sums)
+    c = np.cumsum(p_draft, axis=-1, dtype=np.float64)
+    v = rng.random((B, G)) * c[..., -1]
+    draft = np.empty((B, G), np.int32)
+    for b in range(B):
+        for j in range(G):
+            draft[b, j] = min(int(np.searchsorted(c[b, j], v[b, j], side="right")), V - 1)
+    del c
+    u = rng.random((B, G), dtype=np.float32)
+    r = rng.random(B, dtype=np.float32)
+    return {"draft": draft, "p_draft": p_draft, "p_target": p_target, "u": u, "r": r}

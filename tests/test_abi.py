@@ -159,6 +159,41 @@ def test_router_entry_points_validate_before_any_launch():
         L.moe_mxfp4_destroy(h)
 
 
+def test_dflash_accept_validates_before_any_launch():
+    L = moe.lib()
+    wb, acc = L.moe_mxfp4_dflash_workspace_bytes, L.moe_mxfp4_dflash_accept
+    B, G, V = 32, 8, 152064
+    need = wb(B, V)
+    # one int32 per sequence (rounded to 256 bytes) and one uint64 per 256 vocabulary entries
+    assert need == 256 + B * ((V + 255) // 256) * 8
+    assert wb(1, 1) == 256 + 8
+    assert wb(0, 5) == 0
+    assert wb(-1, 5) == 0 and wb(1, 0) == 0 and wb(1, (1 << 30) + 1) == 0 and wb(65536, 5) == 0
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None)
+    assert acc(0, G, V, None, None, None, None, None, None, None, None, 0, None) == 0   # B = 0 no-op
+    assert acc(-1, G, V, *ok) == 1
+    assert acc(65536, G, V, *ok) == 1
+    assert acc(B, -1, V, *ok) == 1
+    assert acc(B, 65, V, *ok) == 1
+    assert acc(B, G, 0, *ok) == 1
+    assert acc(B, G, (1 << 30) + 1, *ok) == 1
+    for i in range(7):                                  # each pointer argument missing in turn
+        args = list(ok)
+        args[i] = None
+        assert acc(B, G, V, *args) == 1, i
+    # G = 0: draft, p_draft and u are never read and may be NULL
+    need0 = wb(B, V)
+    st = acc(B, 0, V, None, None, FAKE, None, FAKE + 16, FAKE, FAKE, FAKE + 1, need0, None)
+    assert st == 4                                      # reaches the checks after the NULL ones
+    for i in range(7):                                  # each pointer misaligned in turn
+        args = list(ok)
+        args[i] = FAKE + 4
+        assert acc(B, G, V, *args) == 4, i
+    assert acc(B, G, V, *ok[:7], None, need, None) == 5
+    assert acc(B, G, V, *ok[:8], need - 1, None) == 5
+    assert acc(B, G, V, *ok[:7], FAKE + 8, need, None) == 4
+
+
 def test_debug_dequant_and_quantize_validation():
     st, h = _create()
     L = moe.lib()
