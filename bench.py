@@ -138,19 +138,30 @@ def time_accept(w, args, moe, torch, np, synth):
     an HBM stream (4 bytes per vocabulary entry), so it is priced against HBM."""
     B, G, V = w.T // 8, 8, synth.DFLASH_VOCAB
     inp = synth.dflash_batch(B, G, V, seed=w.seed + 7)
-    dev = [torch.from_numpy(inp[k]).cuda() for k in ("draft", "p_draft", "p_target", "u", "r")]
+    dev0 = [torch.from_numpy(inp[k]).cuda() for k in ("draft", "p_draft", "p_target", "u", "r")]
+    # copies at distinct addresses, rotated so that the rows a call reads
+    # (about 30 MB) are not still in the 256 MB last-level cache from the
+    # previous calls: 12 copies cycle 360 MB of rows
+    copies = [dev0] + [[t.clone() for t in dev0] for _ in range(args.accept_copies - 1)]
     n_acc = torch.empty(B, dtype=torch.int32, device="cuda")
     tok = torch.empty(B, dtype=torch.int32, device="cuda")
     wsa = torch.empty(moe.dflash_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")
-    for _ in range(args.warmup):
-        moe.dflash_accept(*dev, n_accepted=n_acc, next_token=tok, workspace=wsa)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        moe.dflash_accept(*dev, n_accepted=n_acc, next_token=tok, workspace=wsa)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    def timed(rotate):
+        for i in range(args.warmup):
+            moe.dflash_accept(*copies[i % len(copies) if rotate else 0], n_accepted=n_acc, next_token=tok,
+                              workspace=wsa)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            moe.dflash_accept(*copies[i % len(copies) if rotate else 0], n_accepted=n_acc, next_token=tok,
+                              workspace=wsa)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    us = timed(True)
     n = n_acc.cpu().numpy()
     # rows streamed: p_target and p_draft at the rejected position, or p_target[G]
     rows = int(np.where(n < G, 2, 1).sum())
@@ -158,7 +169,7 @@ def time_accept(w, args, moe, torch, np, synth):
     gbs = nbytes / (us * 1e-6) / 1e9
     log(f"dflash acceptance: {us:.1f} us per call, {gbs:.0f} GB/s, mean accepted {n.mean():.2f}")
     return {"workload": f"{B} sequences x block {G}, vocabulary {V}, float32 distributions",
-            "us_per_call": us, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "us_per_call": us, "input_copies": len(copies), "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes, "mean_accepted": float(n.mean()),
             "whole_block_accepted": float((n == G).mean())}, inp
 
@@ -178,6 +189,8 @@ def main():
     ap.add_argument("--with-accept", action="store_true",
                     help="also time the DFlash verify acceptance (rejection sampling) of the batch's "
                          "sequences over a full vocabulary, as its own figure")
+    ap.add_argument("--accept-copies", type=int, default=12,
+                    help="input copies rotated across acceptance calls")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the measurements, run a plain device copy (torch.neg, float32) of this many "
                          "MiB: the reference dispatch for scaling HBM byte counters")
