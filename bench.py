@@ -26,6 +26,7 @@ import time
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense FP4/FP6 matrix peak
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 matrix peak (the rate of FP8 x FP4 scaled MFMA)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 WNAMES = ("w_gate", "w_gate_scale", "w_up", "w_up_scale", "w_down", "w_down_scale")
 
 
@@ -94,7 +95,60 @@ def cpu_baseline(w, acts, ntok, router_bits=None):
     return {"value": ntok / dt, "unit": "tokens/s", "cores": int(r["threads"]), "kind": "oracle",
             "sample": f"first {ntok} of {w.T} tokens of {w.name}, all {w.k} experts each"
                       f"{', router projection included' if router_bits is not None else ''}; "
-                      f"fp64 C oracle, OpenMP over tokens; {dt:.2f} s wall"}
+                      f"fp64 C oracle, OpenMP over tokens; {dt:.2f} s wall; {cpu_model()}, "
+                      f"{os.cpu_count()} logical CPUs visible"}
+
+
+def measure_peaks(moe, torch):
+    """What this GPU sustains: a 4 GiB streaming read and the MFMA issue
+    rates of the three instructions the path uses (the library's probes),
+    each timed over 5 launches with HIP events on the launch stream."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    src = torch.ones(4 << 30, dtype=torch.uint8, device="cuda")
+
+    def rate(kind, reps, src=None):
+        moe.probe(kind, src=src, reps=reps, sink=sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            work = moe.probe(kind, src=src, reps=reps, sink=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        return work / (e0.elapsed_time(e1) / 5 * 1e-3)
+
+    out = {"stream_read_GBps": rate(moe.PROBE_STREAM, 0, src) / 1e9}
+    del src
+    for kind, name, reps, nominal in ((moe.PROBE_MFMA_BF16, "mfma_bf16_16x16x32", 250, BF16_PEAK_TFLOPS),
+                                      (moe.PROBE_MFMA_FP8_FP4, "mfma_fp8xfp4_16x16x128", 125, FP8_PEAK_TFLOPS),
+                                      (moe.PROBE_MFMA_FP4_FP4, "mfma_fp4xfp4_16x16x128", 250, MXFP4_PEAK_TFLOPS)):
+        tf = rate(kind, reps) / 1e12
+        out[name] = {"TFLOPs": tf, "nominal_TFLOPs": nominal, "frac_of_nominal": tf / nominal}
+    log("measured peaks: " + ", ".join(f"{k} {v if isinstance(v, float) else v['TFLOPs']:.0f}" for k, v in out.items()))
+    return out
+
+
+def per_call_percentiles(call, steps, torch):
+    """p10 / p50 / p90 of single calls, each between its own HIP events."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        call(i)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    pick = lambda q: ms[min(len(ms) - 1, int(q * len(ms)))]
+    return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def cpu_baseline_accept(inp):
@@ -189,6 +243,9 @@ def main():
     ap.add_argument("--with-accept", action="store_true",
                     help="also time the DFlash verify acceptance (rejection sampling) of the batch's "
                          "sequences over a full vocabulary, as its own figure")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also measure this GPU's streaming-read rate and MFMA issue rates (library probes) and "
+                         "report the roofline fraction against them too")
     ap.add_argument("--accept-copies", type=int, default=12,
                     help="input copies rotated across acceptance calls")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -264,6 +321,8 @@ def main():
             stage_ms[k] = stage_ms.get(k, 0.0) + v
         L.stage_timing(0)
     stage_avg_us = {k: 1e3 * v / ncalls for k, v in stage_ms.items()}
+    pct = per_call_percentiles(lambda i: layers[i % args.copies](x, lg, out=out, workspace=ws, w_router=wr),
+                               args.steps, torch)
     log(f"stage averages (us): " + ", ".join(f"{k} {v:.1f}" for k, v in stage_avg_us.items()))
 
     gateup_s = stage_avg_us["gateup"] * 1e-6
@@ -305,6 +364,7 @@ def main():
         "layer_algorithmic_bytes": layer_bytes,
         "layer_tflops": flops / (ms_per_step * 1e-3) / 1e12,
         "stage_us": stage_avg_us,
+        "per_call_ms": pct,
         "roofline": roofline,
     }
     if wr is not None:
@@ -319,6 +379,14 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         result["router_projection_us"] = e0.elapsed_time(e1) * 1e3 / args.steps
+    if args.peaks:
+        peaks = measure_peaks(moe, torch)
+        result["measured_peaks"] = peaks
+        if roofline["unit"] == "GB/s":
+            roofline["measured_peak"] = peaks["stream_read_GBps"]
+        else:
+            roofline["measured_peak"] = peaks["mfma_fp8xfp4_16x16x128"]["TFLOPs"]
+        roofline["frac_of_measured"] = roofline["achieved"] / roofline["measured_peak"]
     if args.with_accept:
         result["dflash_accept"], accept_inputs = time_accept(w, args, moe, torch, np, synth)
     if args.copy_calibration_mib > 0:

@@ -281,6 +281,25 @@ moe_status moe_mxfp4_dflash_accept(int32_t batch, int32_t block, int32_t vocab,
                                    size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Measurement probes, for reading roofline fractions against what this GPU
+ * sustains as well as against its nominal peaks (not part of the forward
+ * path).  One launch on hip_stream; *work (host) receives the algorithmic
+ * amount it does, so rate = *work / the caller's timing of the launch.
+ *   kind 0  read `bytes` (> 0, multiple of 16) from src (device) once with
+ *           16-byte non-temporal loads; *work = bytes.
+ *   kind 1  v_mfma_f32_16x16x32_bf16 loop       (*work = flops)
+ *   kind 2  v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E2M1 (flops)
+ *   kind 3  the same, E2M1 x E2M1 (flops)
+ * MFMA kinds run 2048 workgroups x 4 waves x 32 `reps` (reps 1 .. 2^20)
+ * rounds of 8 independent MFMAs per wave, operands in registers; src and bytes are
+ * ignored.  sink (device, 4 bytes) is written only with a value the probes
+ * never produce (it keeps the work from being optimised away).
+ * Errors: INVALID_ARG (kind, bytes, reps, null sink or src), ALIGNMENT, HIP.
+ */
+moe_status moe_mxfp4_probe(int32_t kind, const void* src, size_t bytes, int32_t reps,
+                           uint32_t* sink, double* work, void* hip_stream);
+
+/*
  * Decode rows [row0, row0 + nrows) of one expert matrix (0 gate, 1 up,
  * 2 down) from the context's TILED weights with the forward path's own
  * in-register FP4 decode, widened to float: out (device) float [nrows][K]

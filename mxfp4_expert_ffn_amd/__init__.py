@@ -31,7 +31,7 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create
            "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights", "moe_mxfp4_stage_timing",
            "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights",
            "moe_mxfp4_quantize_act_mxfp8", "moe_mxfp4_router_logits", "moe_mxfp4_forward_hidden",
-           "moe_mxfp4_dflash_workspace_bytes", "moe_mxfp4_dflash_accept")
+           "moe_mxfp4_dflash_workspace_bytes", "moe_mxfp4_dflash_accept", "moe_mxfp4_probe")
 NUM_STAGES = 6
 STAGES = ("route", "sort", "quant", "gateup", "down", "combine")
 
@@ -102,6 +102,8 @@ def lib():
         L.moe_mxfp4_dflash_workspace_bytes.restype = sz
         L.moe_mxfp4_dflash_accept.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, sz, P]
         L.moe_mxfp4_dflash_accept.restype = ctypes.c_int
+        L.moe_mxfp4_probe.argtypes = [i32, P, sz, i32, P, ctypes.POINTER(ctypes.c_double), P]
+        L.moe_mxfp4_probe.restype = ctypes.c_int
         L.moe_mxfp4_stage_timing.argtypes = [P, i32]
         L.moe_mxfp4_stage_timing.restype = ctypes.c_int
         L.moe_mxfp4_stage_times.argtypes = [P, ctypes.POINTER(ctypes.c_float),
@@ -325,3 +327,19 @@ def dflash_accept(draft, p_draft, p_target, u, r, n_accepted=None, next_token=No
                                          _ptr(r), _ptr(n_accepted), _ptr(next_token), _ptr(workspace),
                                          workspace.numel(), _stream(stream)), "moe_mxfp4_dflash_accept")
     return n_accepted, next_token
+
+
+PROBE_STREAM, PROBE_MFMA_BF16, PROBE_MFMA_FP8_FP4, PROBE_MFMA_FP4_FP4 = 0, 1, 2, 3
+
+
+def probe(kind: int, src=None, reps: int = 0, sink=None, stream=None) -> float:
+    """Launch one measurement probe (moe_mxfp4_probe); returns the bytes or
+    flops it does.  ``src``: a CUDA tensor to read (kind 0)."""
+    import torch
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    work = ctypes.c_double()
+    nbytes = 0 if src is None else src.numel() * src.element_size()
+    _check(lib().moe_mxfp4_probe(kind, _ptr(src), nbytes, reps, _ptr(sink), ctypes.byref(work), _stream(stream)),
+           "moe_mxfp4_probe")
+    return work.value

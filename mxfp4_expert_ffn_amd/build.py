@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["api.hip", "router.hip", "dflash.hip", "route_sort.hip", "expert_gemm.hip", "dense_gemm.hip", "combine.hip",
+SOURCES = ["api.hip", "router.hip", "dflash.hip", "probes.hip", "route_sort.hip", "expert_gemm.hip", "dense_gemm.hip", "combine.hip",
            "quant_act.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

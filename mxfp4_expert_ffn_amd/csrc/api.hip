@@ -308,6 +308,17 @@ moe_status moe_mxfp4_router_logits(const moe_mxfp4_ctx* ctx, const void* hidden,
     return MOE_OK;
 }
 
+moe_status moe_mxfp4_probe(int32_t kind, const void* src, size_t bytes, int32_t reps, uint32_t* sink, double* work,
+                           void* hip_stream) {
+    if (kind < 0 || kind > 3 || !sink || !work) return MOE_ERR_INVALID_ARG;
+    if (kind == 0 && (!src || bytes == 0 || bytes % 16 != 0)) return MOE_ERR_INVALID_ARG;
+    if (kind != 0 && (reps < 1 || reps > (1 << 20))) return MOE_ERR_INVALID_ARG;
+    if ((kind == 0 && !aligned16(src)) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return MOE_ERR_ALIGNMENT;
+    if (moe::launch_probe(kind, src, bytes, reps, sink, work, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 size_t moe_mxfp4_dflash_workspace_bytes(int32_t batch, int32_t vocab) {
     if (batch < 0 || batch > 65535 || vocab < 1 || vocab > (1 << 30)) return 0;
     return moe::dflash_workspace_bytes(batch, vocab);

@@ -122,6 +122,10 @@ inline int max_chunks(const Dims& dm) {
 // Kernel launchers (each returns hipGetLastError() of its launch).
 // Router projection: logits [T][E] = x [T][d] . w [E][d]^T (bf16 in, float32 out).
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, float* logits, const Dims& dm, hipStream_t s);
+// Measurement probes (not on the forward path): kind 0 streaming read of
+// `bytes`, kinds 1-3 MFMA issue loops; *work = bytes read or flops done.
+hipError_t launch_probe(int kind, const void* src, size_t bytes, int reps, uint32_t* sink, double* work,
+                        hipStream_t s);
 // DFlash verify acceptance over B sequences (two launches); the workspace
 // holds dflash_workspace_bytes(B, V) bytes.
 size_t dflash_workspace_bytes(int32_t B, int32_t V);

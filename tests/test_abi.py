@@ -194,6 +194,24 @@ def test_dflash_accept_validates_before_any_launch():
     assert acc(B, G, V, *ok[:7], FAKE + 8, need, None) == 4
 
 
+def test_probe_validates_before_any_launch():
+    L = moe.lib()
+    pr = L.moe_mxfp4_probe
+    w = ctypes.c_double()
+    W = ctypes.byref(w)
+    assert pr(-1, FAKE, 16, 1, FAKE, W, None) == 1
+    assert pr(4, FAKE, 16, 1, FAKE, W, None) == 1
+    assert pr(0, None, 16, 1, FAKE, W, None) == 1                  # stream needs a source
+    assert pr(0, FAKE, 0, 1, FAKE, W, None) == 1
+    assert pr(0, FAKE, 24, 1, FAKE, W, None) == 1                  # not a multiple of 16
+    assert pr(0, FAKE + 8, 32, 1, FAKE, W, None) == 4
+    assert pr(1, None, 0, 0, FAKE, W, None) == 1                   # reps out of range
+    assert pr(2, None, 0, (1 << 20) + 1, FAKE, W, None) == 1
+    assert pr(3, None, 0, 1, None, W, None) == 1                   # no sink
+    assert pr(3, None, 0, 1, FAKE, None, None) == 1                # no work out-pointer
+    assert pr(1, None, 0, 1, FAKE + 2, W, None) == 4
+
+
 def test_debug_dequant_and_quantize_validation():
     st, h = _create()
     L = moe.lib()
