@@ -99,6 +99,34 @@ def cpu_baseline(w, acts, ntok, router_bits=None):
                       f"{os.cpu_count()} logical CPUs visible"}
 
 
+def time_graph_replay(layers, x, lg, out, ws, wr, args, torch):
+    """The timed loop again, each call replayed from a HIP graph captured
+    once per weight copy (same buffers, so the replays do the same work)."""
+    side = torch.cuda.Stream()                      # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for L in layers:
+            L(x, lg, out=out, workspace=ws, w_router=wr)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for L in layers:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            L(x, lg, out=out, workspace=ws, w_router=wr)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"graph replay: {ms:.4f} ms per call")
+    return {"ms_per_step": ms, "graphs": len(graphs)}
+
+
 def measure_peaks(moe, torch):
     """What this GPU sustains: a 4 GiB streaming read and the MFMA issue
     rates of the three instructions the path uses (the library's probes),
@@ -243,6 +271,9 @@ def main():
     ap.add_argument("--with-accept", action="store_true",
                     help="also time the DFlash verify acceptance (rejection sampling) of the batch's "
                          "sequences over a full vocabulary, as its own figure")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the same calls replayed from captured HIP graphs (one per weight copy): the "
+                         "difference to the eager time is what launching costs")
     ap.add_argument("--peaks", action="store_true",
                     help="also measure this GPU's streaming-read rate and MFMA issue rates (library probes) and "
                          "report the roofline fraction against them too")
@@ -379,6 +410,8 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         result["router_projection_us"] = e0.elapsed_time(e1) * 1e3 / args.steps
+    if args.graph:
+        result["graph_replay"] = time_graph_replay(layers, x, lg, out, ws, wr, args, torch)
     if args.peaks:
         peaks = measure_peaks(moe, torch)
         result["measured_peaks"] = peaks

@@ -147,3 +147,20 @@ def test_forward_replays_from_a_hip_graph(small):
         y_eager = layer(x, lg)
         torch.cuda.synchronize()
         assert torch.equal(y_graph, y_eager), i
+
+
+def test_empty_calls_are_no_ops(small):
+    moe = _moe()
+    w, acts, wts, dev = small
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T, out_dtype=moe.OUT_F32)
+    x, lg = _inputs(acts, w.T)
+    y0 = layer(x, lg).clone()
+    y = layer(x[:0], lg[:0])                        # no tokens: nothing launched, nothing written
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, w.d)
+    n, tok = moe.dflash_accept(torch.zeros((0, 8), dtype=torch.int32, device="cuda"),
+                               torch.zeros((0, 8, 16), device="cuda"), torch.zeros((0, 9, 16), device="cuda"),
+                               torch.zeros((0, 8), device="cuda"), torch.zeros(0, device="cuda"))
+    torch.cuda.synchronize()
+    assert n.numel() == 0 and tok.numel() == 0
+    assert torch.equal(layer(x, lg), y0)            # the context is unaffected
