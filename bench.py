@@ -13,6 +13,13 @@ several copies of the weights so that no step finds another step's weights
 in the 256 MB last-level cache.  The CPU oracle is timed on a bounded token
 sample as a reported baseline (rank 0, one GPU only).
 
+Beside the metric, the line carries: per-stage times (HIP events), p10 /
+p50 / p90 of single calls, the GPU's measured streaming-read and MFMA
+rates (library probes) with the roofline fraction against them, and for
+the verify workloads the DFlash acceptance pass over the batch's sequences
+as its own figure (with the oracle's time on the same batch).  --graph adds
+the same calls replayed from captured HIP graphs.
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
