@@ -313,9 +313,11 @@ def dflash_accept(draft, p_draft, p_target, u, r, n_accepted=None, next_token=No
     V = p_target.shape[2]
     if p_target.shape != (B, G + 1, V) or p_draft.shape != (B, G, V) or u.shape != (B, G) or r.shape != (B,):
         raise ValueError("dflash_accept: inconsistent shapes")
-    for t in (draft, p_draft, p_target, u, r):
-        if not t.is_contiguous():
-            raise ValueError("dflash_accept: inputs must be contiguous")
+    want = ((draft, torch.int32), (p_draft, torch.float32), (p_target, torch.float32), (u, torch.float32),
+            (r, torch.float32))
+    for t, dt in want:
+        if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("dflash_accept: draft must be int32 and the rest float32, all contiguous CUDA tensors")
     if n_accepted is None:
         n_accepted = torch.empty(B, dtype=torch.int32, device=p_target.device)
     if next_token is None:

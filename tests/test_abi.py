@@ -271,3 +271,16 @@ def test_quantize_act_validation():
     assert q(FAKE, -1, 64, FAKE, FAKE, None) == 1
     assert q(FAKE + 2, 4, 64, FAKE, FAKE, None) == 4
     assert q(FAKE, 0, 64, FAKE, FAKE, None) == 0
+
+
+def test_dflash_binding_rejects_wrong_dtypes_before_the_library():
+    torch = pytest.importorskip("torch")
+    B, G, V = 2, 3, 8
+    args = [torch.zeros((B, G), dtype=torch.int32), torch.zeros((B, G, V)), torch.zeros((B, G + 1, V)),
+            torch.zeros((B, G)), torch.zeros(B)]
+    with pytest.raises(ValueError):                  # CPU tensors
+        moe.dflash_accept(*args)
+    bad = list(args)
+    bad[2] = torch.zeros((B, G + 2, V))
+    with pytest.raises(ValueError):                  # inconsistent shapes
+        moe.dflash_accept(*bad)
