@@ -126,6 +126,13 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _require(t, dtype, shape, name):
+    """Argument check of the binding: a contiguous CUDA tensor of this dtype and shape."""
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous CUDA {dtype} tensor of shape {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)} on {t.device}")
+
+
 def _stream(stream=None):
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -193,6 +200,12 @@ class MoeMxfp4:
         if (logits is None) == (w_router is None):
             raise ValueError("pass exactly one of logits and w_router")
         T = hidden.shape[0]
+        E, d = self.cfg.num_experts, self.cfg.d_model
+        _require(hidden, torch.bfloat16, (T, d), "hidden")
+        if logits is not None:
+            _require(logits, torch.float32, (T, E), "logits")
+        else:
+            _require(w_router, torch.bfloat16, (E, d), "w_router")
         if out is None:
             dt = torch.bfloat16 if self.out_dtype == OUT_BF16 else torch.float32
             out = torch.empty((T, self.cfg.d_model), dtype=dt, device=hidden.device)
@@ -215,6 +228,8 @@ class MoeMxfp4:
         """hidden: bf16 [T, d]; w_router: bf16 [E, d] -> float32 logits [T, E]."""
         import torch
         T = hidden.shape[0]
+        _require(hidden, torch.bfloat16, (T, self.cfg.d_model), "hidden")
+        _require(w_router, torch.bfloat16, (self.cfg.num_experts, self.cfg.d_model), "w_router")
         if out is None:
             out = torch.empty((T, self.cfg.num_experts), dtype=torch.float32, device=hidden.device)
         _check(lib().moe_mxfp4_router_logits(self._ctx, _ptr(hidden), _ptr(w_router), T, _ptr(out),
