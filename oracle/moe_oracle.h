@@ -13,6 +13,12 @@
  *   - techllm.github.io, "Xiaomi MiMo x TileRT: 1T parameters at 1000+
  *     tokens/s", section "1. MXFP4 — MoE에만 걸린 양자화": FP4 is applied to
  *     the expert weights, which hold most of the parameters.
+ *   - the same page, section "3. TileRT": tokens are routed to their experts
+ *     (the router form and the top-k rule are readings, stated where used).
+ *   - the same page, section "2. DFlash": a drafted block is verified by the
+ *     target model, with a final rejection-sampling pass that keeps the
+ *     output distribution the target's (the acceptance rule is the standard
+ *     speculative-sampling one, stated where used).
  *   - The pages only name the format "MXFP4"; the bit-level meaning of an
  *     E2M1 element, an E8M0 scale, an E4M3 element and the scalar-to-MX
  *     conversion rule are those of the OCP Microscaling Formats (MX)
