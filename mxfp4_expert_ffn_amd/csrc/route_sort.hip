@@ -457,6 +457,82 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __rest
     sort_single(dm, ids_lds, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows);
 }
 
+// The permutation of at most 64 pairs over at most 64 experts by one
+// wavefront, with no workgroup barrier: lane p holds pair p, lane e expert e.
+// Same outputs as sort_single (a stable counting sort; experts ranked by
+// descending count, ties to the lower index).  A chunk never splits, since
+// the caller guarantees P <= chunk_rows, so active expert r is chunk record r.
+// ids: P expert ids (LDS); scratch: 64 counts, 64 offsets, 64 keys.
+__device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, int32_t* cnt, int32_t* exo,
+                                          uint64_t* keys, int lane, int32_t* __restrict__ offsets,
+                                          int32_t* __restrict__ sorted, int32_t* __restrict__ active,
+                                          int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks) {
+    const int E = dm.E, P = dm.P;
+    const bool valid = lane < P;
+    const int ep = valid ? ids[lane] : 0;
+    // lanes holding the same expert: one ballot per id bit
+    uint64_t peers = __ballot(valid);
+    for (int b = 0, nb = id_bits(E); b < nb; ++b) {
+        const bool bit = (ep >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    const int rank = __popcll(peers & below);          // earlier pairs of the same expert
+    cnt[lane] = 0;
+    wave_sync_lds();
+    if (valid && rank == 0) cnt[ep] = __popcll(peers);
+    wave_sync_lds();
+    const int c = lane < E ? cnt[lane] : 0;
+    const int excl = wave_inclusive_scan(c, lane) - c;
+    exo[lane] = excl;
+    keys[lane] = ((uint64_t)(uint32_t)c << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)lane);
+    if (lane < E) offsets[lane] = excl;
+    wave_sync_lds();
+    // rank of an active expert = number of experts with a larger key (experts
+    // past E have count 0 and never outrank an active one)
+    int r = 0;
+    const uint64_t mine = keys[lane];
+    for (int e2 = 0; e2 < E; ++e2) r += keys[e2] > mine;
+    const int na = __popcll(__ballot(lane < E && c > 0));
+    if (lane < E && c > 0) {
+        active[r] = lane;
+        int32_t* rec = chunks + kChunkRec * r;
+        rec[0] = lane;
+        rec[1] = excl;
+        rec[2] = c;
+        rec[3] = 0;
+    }
+    if (lane == 0) {
+        offsets[E] = P;
+        active[E] = na;
+        *nchunks = na;
+    }
+    if (valid) sorted[exo[ep] + rank] = lane;
+}
+
+// Batches of at most 64 pairs over at most 64 experts: routing (one wave per
+// token) and then sort_wave on wave 0 -- one barrier in all, against the
+// single-workgroup sort's barrier per phase.  Block = min(T, 16) waves.
+__global__ __launch_bounds__(kSortThreads) void k_route_sort_tiny(const float* __restrict__ logits, Dims dm,
+                                                                  int32_t* __restrict__ ids,
+                                                                  float* __restrict__ wts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ sorted,
+                                                                  int32_t* __restrict__ active,
+                                                                  int32_t* __restrict__ chunks,
+                                                                  int32_t* __restrict__ nchunks) {
+    __shared__ RankScratch<1> sc[kSortWaves];
+    __shared__ int32_t ids_lds[kWave];
+    __shared__ int32_t cnt[kWave];
+    __shared__ int32_t exo[kWave];
+    __shared__ uint64_t keys[kWave];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    for (int t = wave; t < dm.T; t += nw) route_token_rank<1>(logits, dm, t, lane, sc[wave], ids, wts, ids_lds);
+    __syncthreads();
+    if (wave == 0) sort_wave(dm, ids_lds, cnt, exo, keys, lane, offsets, sorted, active, chunks, nchunks);
+}
+
 // Many pairs: tiles of kSortTile pairs, one 256-thread workgroup each (the
 // 4 waves split the tile in order).  k_sort_hist stores each tile's expert
 // histogram; k_sort_scan turns them into every tile's first position per
@@ -593,6 +669,12 @@ bool route_sort_fused(const Dims& dm) {
 
 hipError_t launch_route_sort(const float* logits, const Dims& dm, const Workspace& ws, int chunk_rows,
                              hipStream_t s) {
+    if (dm.P <= kWave && dm.P <= chunk_rows) {        // dm.E <= 64 holds for every fused batch
+        const int waves = dm.T < kSortWaves ? dm.T : kSortWaves;
+        hipLaunchKernelGGL(k_route_sort_tiny, dim3(1), dim3(waves * kWave), 0, s, logits, dm, ws.topk_ids,
+                           ws.topk_w, ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks);
+        return hipGetLastError();
+    }
     const size_t lds = sort_lds_bytes(dm.E) + (((size_t)dm.P * sizeof(int32_t) + 15) & ~(size_t)15) +
                        kSortWaves * sizeof(RankScratch<1>);
     hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(kSortThreads), lds, s, logits, dm, ws.topk_ids, ws.topk_w,

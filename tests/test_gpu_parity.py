@@ -170,6 +170,24 @@ def test_edge_shapes(T, E, k):
     assert problems.rel_max_err(got["y"], ref) <= TOL
 
 
+@pytest.mark.parametrize("T,E,k", [(64, 64, 1), (8, 64, 8), (1, 1, 1), (21, 3, 3), (32, 64, 2), (17, 50, 3),
+                                   (16, 2, 2), (9, 7, 7)])
+def test_single_wave_permutation_shapes(T, E, k):
+    # at most 64 pairs over at most 64 experts: routing, then the permutation
+    # by one wavefront (64 pairs exactly, 64 experts, k = 1, more tokens than
+    # routing waves, skewed and tie-heavy logits)
+    rng = np.random.default_rng(70 + T + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if T % 2:
+        lg = np.round(lg * 2) / 2                      # many exact ties
+    lg[:, E // 2] += 3.0                                # one hot expert
+    w, acts, wts = _custom(T, 256, 256, E, k, seed=90 + T, logits=lg)
+    got, _ = _run(w, acts, problems.to_device(wts))
+    _check_routing(w, acts, got)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)["y"]
+    assert problems.rel_max_err(got["y"], ref) <= TOL
+
+
 @pytest.mark.parametrize("d,f", [(8704, 512), (512, 8704), (256, 1024)])
 def test_k_extents(d, f):
     # 68 K steps on either projection, and the 2-step (K = 256) pipeline
