@@ -200,13 +200,13 @@ def cpu_baseline_accept(inp):
             "sample": f"the whole batch ({B} sequences), {reps} calls; {dt * 1e3:.2f} ms per call"}
 
 
-def measured_traffic(workload, mx8):
+def measured_traffic(workload, mx8, root=None):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy
     of known size), or None when there is none or the kernel source changed
-    since the counters were taken."""
+    since the counters were taken.  root: the repository (default: here)."""
     import hashlib
-    root = os.path.dirname(os.path.abspath(__file__))
+    root = root or os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"hbm_traffic_{workload}.md")
     src = os.path.join(root, "mxfp4_expert_ffn_amd", "csrc", "dense_gemm.hip" if mx8 else "expert_gemm.hip")
     if not os.path.exists(path):

@@ -47,3 +47,27 @@ def test_zipf_bias_makes_top_expert_about_ten_times_median():
     n = np.bincount(top.ravel(), minlength=w.E)
     ratio = n.max() / np.median(n)
     assert 5.0 < ratio < 20.0, ratio
+
+
+def test_dflash_batches_are_seeded_distributions_with_drafts_in_range():
+    a = synth.dflash_batch(3, 4, 1000, seed=7)
+    b = synth.dflash_batch(3, 4, 1000, seed=7)
+    c = synth.dflash_batch(3, 4, 1000, seed=8)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    assert not np.array_equal(a["p_target"], c["p_target"])
+    assert a["draft"].shape == (3, 4) and a["draft"].dtype == np.int32
+    assert a["p_draft"].shape == (3, 4, 1000) and a["p_target"].shape == (3, 5, 1000)
+    assert a["u"].shape == (3, 4) and a["r"].shape == (3,)
+    assert np.all((a["draft"] >= 0) & (a["draft"] < 1000))
+    for p in (a["p_draft"], a["p_target"]):
+        assert p.dtype == np.float32 and np.all(p >= 0)
+        np.testing.assert_allclose(p.sum(axis=-1, dtype=np.float64), 1.0, atol=1e-5)
+    assert np.all((a["u"] >= 0) & (a["u"] < 1)) and np.all((a["r"] >= 0) & (a["r"] < 1))
+
+
+def test_dflash_drafter_tracks_the_target():
+    # the drafter perturbs the target's logits slightly: most of the mass overlaps
+    a = synth.dflash_batch(4, 2, 20000, seed=9)
+    overlap = np.minimum(a["p_draft"], a["p_target"][:, :2]).sum(axis=-1)
+    assert overlap.mean() > 0.9
