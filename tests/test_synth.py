@@ -71,3 +71,14 @@ def test_dflash_drafter_tracks_the_target():
     a = synth.dflash_batch(4, 2, 20000, seed=9)
     overlap = np.minimum(a["p_draft"], a["p_target"][:, :2]).sum(axis=-1)
     assert overlap.mean() > 0.9
+
+
+def test_dflash_recipe_reproduces_the_pages_coding_acceptance_length():
+    # the synthetic drafter is calibrated to the pages' coding figure: the
+    # oracle's acceptance pass over 512 synthetic sequences accepts about
+    # 6.3 of 8 drafted tokens (standard error of the mean ~0.1)
+    import oracle
+    facts = json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+    d = synth.dflash_batch(512, facts["dflash_block_max"], 8192, seed=4001)
+    n, _ = oracle.dflash_accept(d["draft"], d["p_draft"], d["p_target"], d["u"], d["r"])
+    assert abs(n.mean() - facts["acceptance_length_coding"]) < 0.5, n.mean()
