@@ -10,7 +10,11 @@
 // Permutation: a stable counting sort of the pairs p = t*k + j by expert,
 // built from wavefront ballots (lanes holding the same expert find each
 // other with one ballot per expert-id bit), per-wave LDS histograms and a
-// prefix scan -- no atomics, so the order is deterministic.
+// prefix scan.  Positions never come from atomics, so the order is
+// deterministic; the only atomic adds sum integer ranks, whose total does not
+// depend on their order.  Sizes: up to 64 pairs, one wave after the routing
+// in the same launch; up to 8192, one workgroup (fused with the routing for
+// up to 64 tokens); beyond, tiles of 2048 pairs in three launches.
 #include "common.hpp"
 
 #include <float.h>
