@@ -164,3 +164,17 @@ def test_empty_calls_are_no_ops(small):
     torch.cuda.synchronize()
     assert n.numel() == 0 and tok.numel() == 0
     assert torch.equal(layer(x, lg), y0)            # the context is unaffected
+
+
+def test_probes_report_their_work_and_run():
+    moe = _moe()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    src = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    assert moe.probe(moe.PROBE_STREAM, src=src, sink=sink) == float(1 << 20)
+    # MFMA kinds: 2048 workgroups x 4 waves x 32 reps-rounds x 8 MFMAs
+    per = {moe.PROBE_MFMA_BF16: 2 * 16 * 16 * 32, moe.PROBE_MFMA_FP8_FP4: 2 * 16 * 16 * 128,
+           moe.PROBE_MFMA_FP4_FP4: 2 * 16 * 16 * 128}
+    for kind, flops in per.items():
+        assert moe.probe(kind, reps=1, sink=sink) == float(flops * 8 * 32 * 2048 * 4)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0                     # the sink is never written by real work

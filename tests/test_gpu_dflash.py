@@ -138,3 +138,33 @@ def test_dflash_workspace_holds_no_state_and_streams_work():
         got = moe.dflash_accept(*_dev(big), stream=side)
     side.synchronize()
     assert np.array_equal(got[0].cpu().numpy(), ref[0]) and np.array_equal(got[1].cpu().numpy(), ref[1])
+
+
+def test_dflash_replays_from_a_hip_graph():
+    # the pass allocates nothing, copies nothing and does not synchronise, so
+    # it can be captured; replays with new inputs match eager calls
+    moe = _moe()
+    B, G, V = 6, 8, 5000
+    first = synth.dflash_batch(B, G, V, seed=2401)
+    dev = _dev(first)
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(moe.dflash_workspace_bytes(B, V), dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.dflash_accept(*dev, n_accepted=n, next_token=tok, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.dflash_accept(*dev, n_accepted=n, next_token=tok, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        inp = synth.dflash_batch(B, G, V, seed=2410 + i)
+        for t, k in zip(dev, KEYS):
+            t.copy_(torch.from_numpy(np.ascontiguousarray(inp[k])).cuda())
+        g.replay()
+        torch.cuda.synchronize()
+        n_ref, tok_ref = oracle.dflash_accept(*[inp[k] for k in KEYS])
+        assert np.array_equal(n.cpu().numpy(), n_ref) and np.array_equal(tok.cpu().numpy(), tok_ref), i
