@@ -45,6 +45,11 @@
  *   - Preconditions that are NOT checked (undefined results if broken):
  *     finite logits and activations; no E8M0 scale byte 0xFF; products of
  *     decoded weights and activations that stay finite in float32.
+ *   - Fault injection, for tests of error propagation: with the environment
+ *     variable MOE_MXFP4_FAULT set to a launch site (router, route, sort,
+ *     quant, gateup, down, combine, dflash), a call that reaches that site
+ *     returns MOE_ERR_HIP there without launching, as a failed launch would;
+ *     the kernels queued before it stay queued.  Read on every call.
  *   - Thread safety: apart from the optional stage timing below, a context
  *     is immutable after create; concurrent forward calls on one context are
  *     safe when they use distinct workspaces and outputs and stage timing is

@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <cstdlib>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -57,6 +59,17 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     L.o = at;       at += round256(P * (size_t)c.d_model * sizeof(float));
     L.total = at;
     return L;
+}
+
+// Fault injection for tests of error propagation: with MOE_MXFP4_FAULT set
+// to a launch site's name, a call that reaches that site returns MOE_ERR_HIP
+// there instead of launching, as a failed launch would.  Sites: router,
+// route (the routing or fused routing + permutation launch), sort, quant,
+// gateup, down, combine, dflash.  Read on every call, so a test can set and
+// clear it between calls.
+bool fault_at(const char* site) {
+    const char* e = std::getenv("MOE_MXFP4_FAULT");
+    return e && std::strcmp(e, site) == 0;
 }
 
 moe_status check_config(const moe_mxfp4_config* c) {
@@ -235,28 +248,34 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     if (mark(0) != hipSuccess) return MOE_ERR_HIP;
     if (w_router) {
         // the projection is timed with the routing stage
-        if (moe::launch_router(x, static_cast<const uint16_t*>(w_router), ws_logits, dm, s) != hipSuccess)
+        if (fault_at("router") ||
+            moe::launch_router(x, static_cast<const uint16_t*>(w_router), ws_logits, dm, s) != hipSuccess)
             return MOE_ERR_HIP;
         router_logits = ws_logits;
     }
     const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
     if (moe::route_sort_fused(dm)) {
         // one launch; its time is recorded as the routing stage
-        if (moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s) != hipSuccess || mark(1) != hipSuccess ||
-            mark(2) != hipSuccess)
+        if (fault_at("route") || moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s) != hipSuccess ||
+            mark(1) != hipSuccess || mark(2) != hipSuccess)
             return MOE_ERR_HIP;
     } else {
-        if (moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess) return MOE_ERR_HIP;
-        if (moe::launch_sort(dm, ws, chunk_rows, s) != hipSuccess || mark(2) != hipSuccess) return MOE_ERR_HIP;
+        if (fault_at("route") || moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (fault_at("sort") || moe::launch_sort(dm, ws, chunk_rows, s) != hipSuccess || mark(2) != hipSuccess)
+            return MOE_ERR_HIP;
     }
-    if (mx8 && moe::launch_quant_x8(x, dm, ws, s) != hipSuccess) return MOE_ERR_HIP;
+    if (mx8 && (fault_at("quant") || moe::launch_quant_x8(x, dm, ws, s) != hipSuccess)) return MOE_ERR_HIP;
     if (mark(3) != hipSuccess) return MOE_ERR_HIP;
+    if (fault_at("gateup")) return MOE_ERR_HIP;
     const hipError_t gu = mx8 ? moe::launch_gateup_dense(ctx->w, dm, ws, s)
                               : moe::launch_gateup(x, ctx->w, dm, ws, s);
     if (gu != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
+    if (fault_at("down")) return MOE_ERR_HIP;
     const hipError_t dn = mx8 ? moe::launch_down_dense(ctx->w, dm, ws, s) : moe::launch_down(ctx->w, dm, ws, s);
     if (dn != hipSuccess || mark(5) != hipSuccess) return MOE_ERR_HIP;
-    if (moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess || mark(6) != hipSuccess)
+    if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess ||
+        mark(6) != hipSuccess)
         return MOE_ERR_HIP;
 
     if (debug_out) {
@@ -338,7 +357,8 @@ moe_status moe_mxfp4_dflash_accept(int32_t batch, int32_t block, int32_t vocab, 
         if (p && !aligned16(p)) return MOE_ERR_ALIGNMENT;
     if (!workspace || workspace_bytes < moe::dflash_workspace_bytes(batch, vocab)) return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MOE_ERR_ALIGNMENT;
-    if (moe::launch_dflash_accept(batch, block, vocab, draft, p_draft, p_target, u, r, n_accepted, next_token,
+    if (fault_at("dflash") ||
+        moe::launch_dflash_accept(batch, block, vocab, draft, p_draft, p_target, u, r, n_accepted, next_token,
                                   workspace, static_cast<hipStream_t>(hip_stream)) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;

@@ -178,3 +178,38 @@ def test_probes_report_their_work_and_run():
         assert moe.probe(kind, reps=1, sink=sink) == float(flops * 8 * 32 * 2048 * 4)
     torch.cuda.synchronize()
     assert int(sink.item()) == 0                     # the sink is never written by real work
+
+
+@pytest.mark.parametrize("site", ["route", "gateup", "down", "combine"])
+def test_a_failed_launch_is_reported_and_leaves_the_context_usable(small, site, monkeypatch):
+    # MOE_MXFP4_FAULT makes the call fail at one launch site as a failed
+    # launch would; the error comes back as MOE_ERR_HIP and the next call,
+    # with nothing failing, gives the same bits as before
+    moe = _moe()
+    w, acts, wts, dev = small
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T, out_dtype=moe.OUT_F32)
+    x, lg = _inputs(acts, w.T)
+    y0 = layer(x, lg).clone()
+    torch.cuda.synchronize()
+    monkeypatch.setenv("MOE_MXFP4_FAULT", site)
+    with pytest.raises(moe.MoeError) as ei:
+        layer(x, lg)
+    assert ei.value.status == 6                       # MOE_ERR_HIP
+    monkeypatch.delenv("MOE_MXFP4_FAULT")
+    torch.cuda.synchronize()
+    assert torch.equal(layer(x, lg), y0)
+
+
+def test_a_failed_acceptance_launch_is_reported(monkeypatch):
+    moe = _moe()
+    d = synth.dflash_batch(3, 4, 300, seed=12)
+    args = [torch.from_numpy(d[k]).cuda() for k in ("draft", "p_draft", "p_target", "u", "r")]
+    n0, t0 = [t.clone() for t in moe.dflash_accept(*args)]
+    monkeypatch.setenv("MOE_MXFP4_FAULT", "dflash")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.dflash_accept(*args)
+    assert ei.value.status == 6
+    monkeypatch.delenv("MOE_MXFP4_FAULT")
+    n1, t1 = moe.dflash_accept(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(n0, n1) and torch.equal(t0, t1)
