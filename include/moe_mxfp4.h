@@ -177,7 +177,8 @@ moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg,
                             const moe_mxfp4_weights* weights,
                             moe_mxfp4_ctx** out);
 
-/* Release a context (host memory only).  destroy(NULL) returns MOE_OK. */
+/* Release a context and its stage-timing events, if any (no device memory
+ * is involved).  destroy(NULL) returns MOE_OK. */
 moe_status moe_mxfp4_destroy(moe_mxfp4_ctx* ctx);
 
 /*
