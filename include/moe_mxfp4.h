@@ -296,6 +296,10 @@ moe_status moe_mxfp4_dflash_accept(int32_t batch, int32_t block, int32_t vocab,
  *   kind 1  v_mfma_f32_16x16x32_bf16 loop       (*work = flops)
  *   kind 2  v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 x E2M1 (flops)
  *   kind 3  the same, E2M1 x E2M1 (flops)
+ *   kind 4, 5, 6  kinds 1, 2, 3 on random finite operands that change from
+ *           one MFMA to the next: under the chip's power limit the clock
+ *           depends on how many operand bits toggle, so these are the rates
+ *           real data can reach, where kinds 1-3 repeat one operand pair
  * MFMA kinds run 2048 workgroups x 4 waves x 32 `reps` (reps 1 .. 2^20)
  * rounds of 8 independent MFMAs per wave, operands in registers; src and bytes are
  * ignored.  sink (device, 4 bytes) is written only with a value the probes

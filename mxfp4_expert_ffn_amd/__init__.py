@@ -347,6 +347,8 @@ def dflash_accept(draft, p_draft, p_target, u, r, n_accepted=None, next_token=No
 
 
 PROBE_STREAM, PROBE_MFMA_BF16, PROBE_MFMA_FP8_FP4, PROBE_MFMA_FP4_FP4 = 0, 1, 2, 3
+# the same instructions on random operands that change every MFMA
+PROBE_MFMA_BF16_RANDOM, PROBE_MFMA_FP8_FP4_RANDOM, PROBE_MFMA_FP4_FP4_RANDOM = 4, 5, 6
 
 
 def probe(kind: int, src=None, reps: int = 0, sink=None, stream=None) -> float:

@@ -329,7 +329,7 @@ moe_status moe_mxfp4_router_logits(const moe_mxfp4_ctx* ctx, const void* hidden,
 
 moe_status moe_mxfp4_probe(int32_t kind, const void* src, size_t bytes, int32_t reps, uint32_t* sink, double* work,
                            void* hip_stream) {
-    if (kind < 0 || kind > 3 || !sink || !work) return MOE_ERR_INVALID_ARG;
+    if (kind < 0 || kind > 6 || !sink || !work) return MOE_ERR_INVALID_ARG;
     if (kind == 0 && (!src || bytes == 0 || bytes % 16 != 0)) return MOE_ERR_INVALID_ARG;
     if (kind != 0 && (reps < 1 || reps > (1 << 20))) return MOE_ERR_INVALID_ARG;
     if ((kind == 0 && !aligned16(src)) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return MOE_ERR_ALIGNMENT;

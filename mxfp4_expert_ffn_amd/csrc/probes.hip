@@ -9,6 +9,11 @@
 //   kind 2  v_mfma_scale_f32_16x16x128_f8f6f4 with E4M3 x E2M1 operands (the
 //           8192-token chunk's)
 //   kind 3  the same with E2M1 x E2M1 operands (the MXFP4 peak)
+//   kinds 4, 5, 6  kinds 1, 2, 3 with random operands that change from one
+//           MFMA to the next (four register sets per operand, drawn from a
+//           hash; no NaN or infinite codes).  The chip's clock drops under
+//           its power limit when operand bits toggle, so these rates are the
+//           ones real data can reach; kinds 1-3 repeat one operand pair.
 //
 // MFMA kinds: 2048 workgroups of 4 waves, each wave 32 `reps` rounds of 8
 // independent accumulator chains (enough to cover the instruction's
@@ -49,13 +54,65 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_stream(const u32x4_t* _
     if (acc == 0x9e3779b9u) sink[0] = acc;
 }
 
+constexpr int kSets = 4;                    // operand register sets of the random kinds
+
+// 32-bit mix of (thread, index) for the random operands (a murmur3 finaliser)
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x85ebca6bu;
+    x ^= x >> 13;
+    x *= 0xc2b2ae35u;
+    return x ^ (x >> 16);
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kProbeThreads) void k_probe_mfma(int reps, uint32_t* sink) {
     const int lane = threadIdx.x % kWave;
     f32x4_t acc[kChains];
 #pragma unroll
     for (int c = 0; c < kChains; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if constexpr (KIND == 1) {
+    if constexpr (KIND >= 4) {
+        const uint32_t t = blockIdx.x * kProbeThreads + threadIdx.x;
+        if constexpr (KIND == 4) {
+            // bf16 values k/16 for k in [-32, 31]: finite, mixed signs and exponents
+            bf16x8_t a[kSets], b[kSets];
+#pragma unroll
+            for (int q = 0; q < kSets; ++q)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    a[q][i] = (__bf16)((float)((int)(mix32(t * 64u + q * 8u + i) % 64u) - 32) * 0.0625f);
+                    b[q][i] = (__bf16)((float)((int)(mix32(t * 64u + q * 8u + i + 32u) % 64u) - 32) * 0.0625f);
+                }
+            for (int r = 0; r < reps; ++r)
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                    for (int c = 0; c < kChains; ++c)
+                        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(u + c) % kSets], b[(u + 3 * c + 1) % kSets],
+                                                                         acc[c], 0, 0, 0);
+        } else {
+            // E4M3 bytes with the low exponent bit clear never encode NaN;
+            // every E2M1 code is finite
+            constexpr uint32_t amask = KIND == 5 ? 0xF7F7F7F7u : 0xFFFFFFFFu;
+            i32x8_t a[kSets], b[kSets];
+#pragma unroll
+            for (int q = 0; q < kSets; ++q)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    a[q][i] = (int)(mix32(t * 64u + q * 8u + i) & amask);
+                    b[q][i] = (int)mix32(t * 64u + q * 8u + i + 32u);
+                }
+            constexpr int fmt_a = KIND == 5 ? 0 : 4;
+            for (int r = 0; r < reps; ++r)
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                    for (int c = 0; c < kChains; ++c)
+                        acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            a[(u + c) % kSets], b[(u + 3 * c + 1) % kSets], acc[c], fmt_a, 4, 0, 0x7f7f7f7f, 0,
+                            0x7f7f7f7f);
+        }
+    } else if constexpr (KIND == 1) {
         bf16x8_t a, b;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -102,7 +159,10 @@ hipError_t launch_probe(int kind, const void* src, size_t bytes, int reps, uint3
         if (kind == 1) hipLaunchKernelGGL(k_probe_mfma<1>, grid, block, 0, s, reps, sink);
         if (kind == 2) hipLaunchKernelGGL(k_probe_mfma<2>, grid, block, 0, s, reps, sink);
         if (kind == 3) hipLaunchKernelGGL(k_probe_mfma<3>, grid, block, 0, s, reps, sink);
-        const double per = kind == 1 ? 2.0 * 16 * 16 * 32 : 2.0 * 16 * 16 * 128;
+        if (kind == 4) hipLaunchKernelGGL(k_probe_mfma<4>, grid, block, 0, s, reps, sink);
+        if (kind == 5) hipLaunchKernelGGL(k_probe_mfma<5>, grid, block, 0, s, reps, sink);
+        if (kind == 6) hipLaunchKernelGGL(k_probe_mfma<6>, grid, block, 0, s, reps, sink);
+        const double per = kind == 1 || kind == 4 ? 2.0 * 16 * 16 * 32 : 2.0 * 16 * 16 * 128;
         *work = per * kChains * kUnroll * (double)reps * (double)kProbeGroups * (kProbeThreads / kWave);
     }
     return hipGetLastError();

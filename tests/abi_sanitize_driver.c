@@ -93,6 +93,7 @@ int main(void) {
     CHECK(moe_mxfp4_dflash_accept(0, 8, 100, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL), MOE_OK);
     double work = 0;
     CHECK(moe_mxfp4_probe(7, FAKE, 16, 1, FAKE, &work, NULL), MOE_ERR_INVALID_ARG);
+    CHECK(moe_mxfp4_probe(6, NULL, 0, 0, FAKE, &work, NULL), MOE_ERR_INVALID_ARG);
     CHECK(moe_mxfp4_probe(0, FAKE, 24, 1, FAKE, &work, NULL), MOE_ERR_INVALID_ARG);
 
     for (int s = 0; s <= 7; ++s)

@@ -200,7 +200,7 @@ def test_probe_validates_before_any_launch():
     w = ctypes.c_double()
     W = ctypes.byref(w)
     assert pr(-1, FAKE, 16, 1, FAKE, W, None) == 1
-    assert pr(4, FAKE, 16, 1, FAKE, W, None) == 1
+    assert pr(7, FAKE, 16, 1, FAKE, W, None) == 1
     assert pr(0, None, 16, 1, FAKE, W, None) == 1                  # stream needs a source
     assert pr(0, FAKE, 0, 1, FAKE, W, None) == 1
     assert pr(0, FAKE, 24, 1, FAKE, W, None) == 1                  # not a multiple of 16

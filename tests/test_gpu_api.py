@@ -173,7 +173,8 @@ def test_probes_report_their_work_and_run():
     assert moe.probe(moe.PROBE_STREAM, src=src, sink=sink) == float(1 << 20)
     # MFMA kinds: 2048 workgroups x 4 waves x 32 reps-rounds x 8 MFMAs
     per = {moe.PROBE_MFMA_BF16: 2 * 16 * 16 * 32, moe.PROBE_MFMA_FP8_FP4: 2 * 16 * 16 * 128,
-           moe.PROBE_MFMA_FP4_FP4: 2 * 16 * 16 * 128}
+           moe.PROBE_MFMA_FP4_FP4: 2 * 16 * 16 * 128, moe.PROBE_MFMA_BF16_RANDOM: 2 * 16 * 16 * 32,
+           moe.PROBE_MFMA_FP8_FP4_RANDOM: 2 * 16 * 16 * 128, moe.PROBE_MFMA_FP4_FP4_RANDOM: 2 * 16 * 16 * 128}
     for kind, flops in per.items():
         assert moe.probe(kind, reps=1, sink=sink) == float(flops * 8 * 32 * 2048 * 4)
     torch.cuda.synchronize()
