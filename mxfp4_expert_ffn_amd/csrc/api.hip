@@ -234,6 +234,7 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     ws.h = reinterpret_cast<uint8_t*>(base + L.h);
     ws.hs = reinterpret_cast<uint8_t*>(base + L.hs);
     ws.o = reinterpret_cast<float*>(base + L.o);
+    ws.os = reinterpret_cast<uint8_t*>(base + L.o + (size_t)num_tokens * c.top_k * c.d_model * sizeof(uint16_t));
 
     moe::Dims dm{num_tokens, c.d_model, c.d_ff, c.num_experts, c.top_k, num_tokens * c.top_k};
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -274,7 +275,7 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     if (fault_at("down")) return MOE_ERR_HIP;
     const hipError_t dn = mx8 ? moe::launch_down_dense(ctx->w, dm, ws, s) : moe::launch_down(ctx->w, dm, ws, s);
     if (dn != hipSuccess || mark(5) != hipSuccess) return MOE_ERR_HIP;
-    if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, s) != hipSuccess ||
+    if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, mx8, s) != hipSuccess ||
         mark(6) != hipSuccess)
         return MOE_ERR_HIP;
 

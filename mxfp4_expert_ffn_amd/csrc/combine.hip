@@ -4,7 +4,9 @@
 //
 // Combine: y[t] = sum_j w[t][j] * o[t][j].  The down projection stores the
 // output of pair p = t*k + j at row p, so a token's k rows form one
-// contiguous block.  Each product is rounded to float32 on its own (no fused
+// contiguous block.  The streaming path stores o in float32; the dense path
+// stores fp16 codes with one power-of-two scale per 128 columns, decoded here
+// exactly.  Each product is rounded to float32 on its own (no fused
 // multiply-add), the k products are added in slot order j = 0..k-1 (fixed
 // order: deterministic), and the sum is rounded once to the output type.
 #include "common.hpp"
@@ -14,11 +16,30 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// 4 consecutive values of an o row as float32.  OT = float: float32 values;
+// OT = uint16_t: fp16 codes times 2^(scale byte - 127) (exact products).
+template <typename OT>
+__device__ __forceinline__ f32x4_t load_o4(const OT* p, const uint8_t* sc) {
+    if constexpr (sizeof(OT) == 4) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    } else {
+        const u32x2_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        const int se = (int)*sc - 127;
+        auto f = [&](uint32_t h) { return ldexpf((float)__builtin_bit_cast(_Float16, (uint16_t)h), se); };
+        return f32x4_t{f(b.x & 0xFFFFu), f(b.x >> 16), f(b.y & 0xFFFFu), f(b.y >> 16)};
+    }
+}
+
 // One thread per 4 consecutive output columns of one token.  KK > 0: k is
 // KK and the k row loads are all issued before the sum (the rows are read
-// once, so they bypass the caches' retention).
-template <int KK>
-__global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const float* __restrict__ o,
+// once, so they bypass the caches' retention).  o holds float32 values
+// (streaming path) or fp16 codes with a scale byte per 128 columns in os
+// (dense path).
+template <int KK, typename OT>
+__global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const OT* __restrict__ o,
+                                                       const uint8_t* __restrict__ os,
                                                        const float* __restrict__ topk_w,
                                                        void* __restrict__ out, int out_dtype) {
 #pragma clang fp contract(off)
@@ -27,21 +48,22 @@ __global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const float* __r
     if (gid >= (size_t)dm.T * q) return;
     const int t = (int)(gid / q), c = (int)(gid % q) * 4;
     const int k = KK > 0 ? KK : dm.k;
-    const float* ot = o + (size_t)t * k * dm.d + c;
+    const OT* ot = o + (size_t)t * k * dm.d + c;
+    const int ng = dm.d / 128;
+    const uint8_t* st = os + (size_t)t * k * ng + c / 128;
     const float* wt = topk_w + (size_t)t * k;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (KK > 0) {
         static_assert(KK % 4 == 0, "weights are read 4 at a time");
         f32x4_t v[KK], w4[KK / 4];
 #pragma unroll
-        for (int j = 0; j < KK; ++j)
-            v[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(ot + (size_t)j * dm.d));
+        for (int j = 0; j < KK; ++j) v[j] = load_o4(ot + (size_t)j * dm.d, st + j * ng);
 #pragma unroll
         for (int j = 0; j < KK / 4; ++j) w4[j] = reinterpret_cast<const f32x4_t*>(wt)[j];
 #pragma unroll
         for (int j = 0; j < KK; ++j) acc += w4[j / 4][j % 4] * v[j];
     } else {
-        for (int j = 0; j < k; ++j) acc += wt[j] * *reinterpret_cast<const f32x4_t*>(ot + (size_t)j * dm.d);
+        for (int j = 0; j < k; ++j) acc += wt[j] * load_o4(ot + (size_t)j * dm.d, st + j * ng);
     }
     if (out_dtype == MOE_OUT_F32) {
         *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + (size_t)t * dm.d + c) = acc;
@@ -161,13 +183,19 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, hipStream_t s) {
+hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, bool o_f16,
+                           hipStream_t s) {
     const size_t n = (size_t)dm.T * (dm.d / 4);
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads)), block(kThreads);
-    if (dm.k == 8)
-        hipLaunchKernelGGL(k_finalize<8>, grid, block, 0, s, dm, ws.o, ws.topk_w, out, out_dtype);
+    const uint16_t* o16 = reinterpret_cast<const uint16_t*>(ws.o);
+    if (dm.k == 8 && o_f16)
+        hipLaunchKernelGGL((k_finalize<8, uint16_t>), grid, block, 0, s, dm, o16, ws.os, ws.topk_w, out, out_dtype);
+    else if (dm.k == 8)
+        hipLaunchKernelGGL((k_finalize<8, float>), grid, block, 0, s, dm, ws.o, ws.os, ws.topk_w, out, out_dtype);
+    else if (o_f16)
+        hipLaunchKernelGGL((k_finalize<0, uint16_t>), grid, block, 0, s, dm, o16, ws.os, ws.topk_w, out, out_dtype);
     else
-        hipLaunchKernelGGL(k_finalize<0>, grid, block, 0, s, dm, ws.o, ws.topk_w, out, out_dtype);
+        hipLaunchKernelGGL((k_finalize<0, float>), grid, block, 0, s, dm, ws.o, ws.os, ws.topk_w, out, out_dtype);
     return hipGetLastError();
 }
 

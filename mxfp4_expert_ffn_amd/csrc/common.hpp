@@ -99,7 +99,10 @@ struct Workspace {
     uint8_t* xs;              // MXFP8 mode: [T][d/32] E8M0 scales of x
     uint8_t* h;               // [P][f] bf16 (or E4M3 codes in MXFP8 mode), rows in sorted order
     uint8_t* hs;              // MXFP8 mode: [P][f/32] E8M0 scales of h
-    float* o;                 // [P][d] expert outputs, row p = pair p (token-major)
+    float* o;                 // [P][d] expert outputs, row p = pair p (token-major); MXFP8
+                              // mode: fp16 codes in the first half of that space
+    uint8_t* os;              // MXFP8 mode: [P][d/128] scale exponents + 127 of o's fp16
+                              // codes, placed after them inside o's space
 };
 
 // Problem description passed by value to kernels.
@@ -151,7 +154,9 @@ hipError_t launch_gateup_dense(const moe_mxfp4_weights& w, const Dims& dm, const
                                hipStream_t s);
 hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
                              hipStream_t s);
-hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype,
+// o_f16: the per-pair outputs are fp16 codes in ws.o with scales in ws.os
+// (dense path), else float32 in ws.o
+hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, bool o_f16,
                            hipStream_t s);
 hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t row0,
                                 int32_t nrows, float* out, hipStream_t s);

@@ -35,8 +35,9 @@
 // the W_up rows of the same columns, and a wave's tiles j and j + kJ/2 meet
 // in one lane, so SwiGLU and the MXFP8 re-quantisation of h (each run of 32
 // h columns is one MX block) run in the epilogue.  Down: the epilogue stores
-// each float32 result row at its pair's own row p = t*k + j (the combine
-// applies the routing weights).
+// each result row at its pair's own row p = t*k + j as fp16 codes with one
+// power-of-two scale per 128 columns (the combine applies the routing
+// weights).
 #include "common.hpp"
 
 namespace moe {
@@ -49,6 +50,7 @@ constexpr int kASlot = kTM * kKStep;        // E4M3 rows of one step
 constexpr int kBSlot = kTiles * 1024;       // FP4 tiles of one step
 constexpr int kBsSlot = kTiles * 256;       // weight scales of 4 steps
 constexpr int kAsSlot = kTM * 16;           // activation scales of 4 steps
+constexpr int kOStride = 256 * 2 + 16;      // bytes per row of down's bf16 output tile (padded: no bank conflicts)
 constexpr int kRsrcWord3 = 0x00020000;      // gfx9 raw buffer descriptor, dword 3
 
 enum { kGateUp = 0, kDown = 1 };
@@ -66,7 +68,8 @@ struct DenseArgs {
     const int32_t* nchunks;
     uint8_t* h_out;              // gate/up: [P][f] E4M3
     uint8_t* h_scale_out;        // gate/up: [P][f/32]
-    float* o_out;                // down: [P][d], row = pair index
+    uint16_t* o_out;             // down: [P][d] fp16 codes, row = pair index
+    uint8_t* o_scale_out;        // down: [P][d/128] scale exponents + 127 of those codes
     int32_t K, N, n_tiles, k_top, ldo;
 };
 
@@ -89,6 +92,19 @@ __device__ __forceinline__ void wait_barrier() {
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Largest value over the 16 lanes of each DPP row (all 16 get it): quad
+// swaps, then the half-row and row mirrors.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = dpp_max<0xB1>(v);       // quad_perm [1, 0, 3, 2]
+    v = dpp_max<0x4E>(v);       // quad_perm [2, 3, 0, 1]
+    v = dpp_max<0x141>(v);      // row_half_mirror
+    return dpp_max<0x140>(v);   // row_mirror
 }
 
 // Tile shape: 2 x WN wavefronts, each 64 pairs x (256 / WN) weight rows;
@@ -117,6 +133,8 @@ template <int MODE, int WN, int STAGES>
 struct Dense {
     using S = Shape<WN, STAGES>;
     static constexpr int kW = S::kW, kJ = S::kJ, kQ = S::kQ;
+    static_assert(MODE != kDown || kTM * kOStride + kTM * 4 <= S::kLds, "down's output tile fits the LDS ring");
+    static_assert(MODE != kDown || (WN == 2 && kJ * 16 == 128), "down: 256-column units, 128 columns per wave");
 
     struct Ctx {
         __amdgpu_buffer_rsrc_t ra, ras, rw, rs;   // activations, their scales, this wave's B matrix + scales
@@ -333,7 +351,14 @@ struct Dense {
             main_loop<false>(c, acc, sbw, nms, wm, wn, lane);
 
         // Epilogue.  Lane holds D[pair wm*64 + ms*16 + 4g + r][column li] of
-        // tile jj.
+        // tile jj.  Down scales each row's 128 columns of this wave by a
+        // power of two (their largest magnitude lands in [2^14, 2^15)),
+        // rounds them to fp16 into an LDS tile (the operand ring is free once
+        // every wave is past the main loop) and then stores whole 512-byte
+        // row pieces.
+        uint8_t* ostage = smem;                      // [kTM rows][kOStride bytes]
+        int32_t* orows = reinterpret_cast<int32_t*>(smem + kTM * kOStride);
+        if constexpr (MODE == kDown) __syncthreads();
 #pragma unroll
         for (int ms = 0; ms < kMs; ++ms) {
             if (ms >= nms) continue;
@@ -362,12 +387,35 @@ struct Dense {
                         }
                     }
                 } else {
-                    if (idx < M) {
-                        float* orow_p = a.o_out + (size_t)pr[ms][r] * a.ldo + nt * 256 + wn * kJ * 16 + li;
+                    const int lr = wm * 64 + ms * 16 + 4 * g + r;
+                    float m = 0.f;
 #pragma unroll
-                        for (int jj = 0; jj < kJ; ++jj) __builtin_nontemporal_store(acc[ms][jj][r], orow_p + jj * 16);
+                    for (int jj = 0; jj < kJ; ++jj) m = fmaxf(m, fabsf(acc[ms][jj][r]));
+                    m = row16_max(m);
+                    // m >= 0: its biased exponent field is floor(log2 m) + 127
+                    // (0 for zero and subnormals, which the clamp covers)
+                    const int se = max((int)(__float_as_uint(m) >> 23) - 127 - 14, -127);
+                    const float inv = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, se <= 113
+                    uint8_t* srow = ostage + lr * kOStride + (wn * kJ * 16 + li) * 2;
+#pragma unroll
+                    for (int jj = 0; jj < kJ; ++jj)
+                        *reinterpret_cast<_Float16*>(srow + jj * 32) = (_Float16)(acc[ms][jj][r] * inv);
+                    if (li == 0) {
+                        if (wn == 0) orows[lr] = pr[ms][r];
+                        if (idx < M) a.o_scale_out[(size_t)pr[ms][r] * (a.ldo / 128) + nt * 2 + wn] = (uint8_t)(se + 127);
                     }
                 }
+            }
+        }
+        if constexpr (MODE == kDown) {
+            __syncthreads();
+            // 32 lanes x 16 bytes per row; kT / 32 rows per pass
+            constexpr int kRowsPerPass = S::kT / 32;
+            const int piece = tid % 32;
+            for (int row = tid / 32; row < rows; row += kRowsPerPass) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ostage + row * kOStride + piece * 16);
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(a.o_out + (size_t)orows[row] * a.ldo +
+                                                                          nt * 256 + piece * 8));
             }
         }
     }
@@ -428,7 +476,8 @@ hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const W
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
     a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
-    a.h_out = nullptr; a.h_scale_out = nullptr; a.o_out = ws.o;
+    a.h_out = nullptr; a.h_scale_out = nullptr;
+    a.o_out = reinterpret_cast<uint16_t*>(ws.o); a.o_scale_out = ws.os;
     a.K = dm.f; a.N = dm.d; a.n_tiles = dm.d / 256; a.k_top = dm.k; a.ldo = dm.d;
     return launch<kDown>(a, max_dense_chunks(dm) * a.n_tiles, s);
 }
