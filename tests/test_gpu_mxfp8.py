@@ -116,3 +116,26 @@ def test_chunk_8192_sampled_parity():
     print(f"chunk_8192: bf16-out rel max err {err:.3e} over {len(sample)} tokens "
           f"(bf16 rounding of the reference alone: {floor:.3e})")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("shifts", [(40, 40, 40, 40), (-60, -60, -60, -60), (40, -40, 0, 0)])
+def test_mxfp8_outputs_outside_the_fp16_range(shifts):
+    # the dense path stores each pair's outputs as fp16 codes with a
+    # power-of-two scale per 128 columns: outputs near 1e10 (past fp16's
+    # largest value), near 1e-20 (below its smallest), and experts of both
+    # kinds inside one token must come back within the tolerance
+    moe = _moe()
+    w = synth.Workload("mx8", 24, 256, 512, 4, 2, "mxfp8", "none", 95)
+    acts = synth.make_activations(w)
+    wts = problems.pack_experts(w)
+    s = wts["w_down_scale"].astype(np.int32) + np.array(shifts, np.int32)[:, None, None]
+    assert s.min() >= 0 and s.max() <= 254                   # stays a finite E8M0 byte
+    wts["w_down_scale"] = s.astype(np.uint8)
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, w.k, act_mode=oracle.ACT_MXFP8)["y"]
+    assert np.isfinite(ref).all()
+    amax = np.abs(ref).max()
+    assert amax > 1e6 or amax < 1e-8 or shifts[0] != shifts[1]
+    y32, _ = _run(w, acts, problems.to_device(wts), moe.OUT_F32)
+    err = problems.rel_max_err(y32, ref)
+    print(f"mxfp8 down-scale shifts {shifts}: max |y| {amax:.3e}, f32-out rel max err {err:.3e}")
+    assert err <= TOL
