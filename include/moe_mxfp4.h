@@ -50,6 +50,10 @@
  *     quant, gateup, down, combine, dflash), a call that reaches that site
  *     returns MOE_ERR_HIP there without launching, as a failed launch would;
  *     the kernels queued before it stay queued.  Read on every call.
+ *   - Logging: with MOE_MXFP4_LOG set (to anything but "0") when a context
+ *     is created, create prints the configuration and each forward call
+ *     whose token count differs from the previous call's prints its launch
+ *     sequence (the kernel path taken), on stderr.
  *   - Thread safety: apart from the optional stage timing below, a context
  *     is immutable after create; concurrent forward calls on one context are
  *     safe when they use distinct workspaces and outputs and stage timing is
@@ -90,15 +94,33 @@ typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
 typedef struct {
     uint32_t struct_size;    /* sizeof(moe_mxfp4_config)                        */
     int32_t num_experts;     /* E, 1..512                                       */
-    int32_t d_model;         /* d, 256 or a multiple of 512                     */
-    int32_t d_ff;            /* f, 256 or a multiple of 512                     */
+    int32_t d_model;         /* d, 256 or a multiple of 512 (see below)         */
+    int32_t d_ff;            /* f, 256 or a multiple of 512 (see below)         */
     int32_t top_k;           /* k, 1..min(E, 32)                                */
-    int32_t max_tokens;      /* upper bound of num_tokens per forward call, >= 1 */
-    int32_t act_mode;        /* moe_act_mode; MXFP8 needs max_tokens*d and
-                                max_tokens*k*f below 2^32                       */
+    int32_t max_tokens;      /* upper bound of num_tokens per forward call, >= 1;
+                                the activation rows the projections read must
+                                stay below 4 GiB: max_tokens*d and
+                                max_tokens*k*f times 2 bytes (bf16) or 1 byte
+                                (MXFP8) below 2^32                              */
+    int32_t act_mode;        /* moe_act_mode                                    */
     int32_t out_dtype;       /* moe_out_dtype                                   */
     uint32_t flags;          /* reserved, must be 0                             */
 } moe_mxfp4_config;
+
+/*
+ * Shape limits (moe_mxfp4_create returns MOE_ERR_UNSUPPORTED_SHAPE outside
+ * them).  The format itself only needs K (d_model for gate/up, d_ff for
+ * down) to be a multiple of the MX block of 32.  The kernels consume K in
+ * steps of 128 (four MX blocks, one per group of 16 lanes of a wavefront)
+ * through a software pipeline 4 steps deep, or 2 steps deep for K = 256, so
+ * every K is 256 or a multiple of 512; every shape of the workloads in the
+ * tests and the benchmark (256, 512, 1536, 2048, 4096, 6144) is one.  A
+ * caller with another K pads each expert matrix with all-zero MX blocks and
+ * the activations with zero columns up to the next allowed K: zero elements
+ * add nothing to any dot product, so the result is unchanged.  Also:
+ * max_tokens*k <= 2^30 and d_model*d_ff <= 2^30 (one expert matrix is
+ * addressed with 32-bit offsets).
+ */
 
 /*
  * MXFP4 matrices.  Every expert matrix has one output unit per row and the
@@ -338,11 +360,12 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
  * and one after each stage, into slot (call index % capacity); capacity 0
  * destroys the events and stops recording.  Errors: INVALID_ARG, HIP.
  *
- * moe_mxfp4_stage_times(ctx, total_ms, calls): waits for the last recorded
- * event, writes the summed milliseconds of each stage over the recorded
+ * moe_mxfp4_stage_times(ctx, total_ms, calls): waits for the recorded
+ * events, writes the summed milliseconds of each stage over the recorded
  * calls still held (at most capacity) into total_ms (host float
  * [MOE_MXFP4_NUM_STAGES]) and their number into *calls (host), then starts
- * a new count.  Stage i of a call spans event i to event i+1, so it includes
+ * a new count.  A call that returned an error holds no slot: its partly
+ * recorded events are never summed, and the next call reuses the slot.  Stage i of a call spans event i to event i+1, so it includes
  * any launch gap before that stage's kernel.  Errors: INVALID_ARG (null
  * pointer, timing not enabled), HIP.  Timing calls are not thread safe.
  */

@@ -133,10 +133,37 @@ def _require(t, dtype, shape, name):
                          f"{t.dtype} {tuple(t.shape)} on {t.device}")
 
 
-def _stream(stream=None):
+def _torch_stream(stream=None):
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream(stream=None):
+    return ctypes.c_void_p(_torch_stream(stream).cuda_stream)
+
+
+ROUTING_FIELDS = ("topk_ids", "topk_w", "expert_offsets", "sorted_pairs")
+
+
+def _routing_struct(routing, T, k, E):
+    """Routing outputs (dict of optional CUDA tensors) -> the C struct, after
+    checking each tensor's dtype, size and contiguity."""
+    import torch
+    if routing is None:
+        return None
+    unknown = set(routing) - set(ROUTING_FIELDS)
+    if unknown:
+        raise ValueError(f"routing: unknown outputs {sorted(unknown)}")
+    want = {"topk_ids": (torch.int32, T * k), "topk_w": (torch.float32, T * k),
+            "expert_offsets": (torch.int32, E + 1), "sorted_pairs": (torch.int32, T * k)}
+    for n, t in routing.items():
+        if t is None:
+            continue
+        dt, numel = want[n]
+        if t.dtype != dt or t.numel() < numel or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"routing[{n!r}]: expected a contiguous CUDA {dt} tensor of at least {numel} "
+                             f"elements, got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return Routing(*[_ptr(routing.get(n)) for n in ROUTING_FIELDS])
 
 
 def make_config(num_experts, d_model, d_ff, top_k, max_tokens, act_mode=ACT_BF16,
@@ -165,7 +192,7 @@ class MoeMxfp4:
         _check(lib().moe_mxfp4_create(ctypes.byref(self.cfg), ctypes.byref(w), ctypes.byref(h)),
                "moe_mxfp4_create")
         self._ctx = h
-        self._ws = None
+        self._ws = {}            # cached workspace per stream handle
 
     def close(self):
         if getattr(self, "_ctx", None) is not None and self._ctx.value:
@@ -181,13 +208,29 @@ class MoeMxfp4:
     def workspace_bytes(self, num_tokens: int) -> int:
         return lib().moe_mxfp4_workspace_bytes(self._ctx, num_tokens)
 
-    def workspace(self, num_tokens: int):
-        """A cached uint8 workspace large enough for ``num_tokens``."""
+    def workspace(self, num_tokens: int, stream=None):
+        """A cached uint8 workspace large enough for ``num_tokens``, one per
+        stream (calls that may run at the same time need distinct
+        workspaces).  It is allocated on that stream, so the caching
+        allocator reuses its memory only after the stream's queued work."""
         import torch
+        s = _torch_stream(stream)
         need = self.workspace_bytes(num_tokens)
-        if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
-        return self._ws
+        ws = self._ws.get(s.cuda_stream)
+        if ws is None or ws.numel() < need:
+            with torch.cuda.stream(s):
+                ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+            self._ws[s.cuda_stream] = ws
+        return ws
+
+    def _out(self, out, T, device, stream):
+        import torch
+        dt = torch.bfloat16 if self.out_dtype == OUT_BF16 else torch.float32
+        if out is None:
+            with torch.cuda.stream(_torch_stream(stream)):
+                return torch.empty((T, self.cfg.d_model), dtype=dt, device=device)
+        _require(out, dt, (T, self.cfg.d_model), "out")
+        return out
 
     def forward(self, hidden, logits, out=None, workspace=None, routing: dict | None = None,
                 stream=None, w_router=None):
@@ -206,14 +249,9 @@ class MoeMxfp4:
             _require(logits, torch.float32, (T, E), "logits")
         else:
             _require(w_router, torch.bfloat16, (E, d), "w_router")
-        if out is None:
-            dt = torch.bfloat16 if self.out_dtype == OUT_BF16 else torch.float32
-            out = torch.empty((T, self.cfg.d_model), dtype=dt, device=hidden.device)
-        ws = self.workspace(T) if workspace is None else workspace
-        r = None
-        if routing is not None:
-            r = Routing(*[_ptr(routing.get(n)) for n in ("topk_ids", "topk_w", "expert_offsets",
-                                                         "sorted_pairs")])
+        out = self._out(out, T, hidden.device, stream)
+        ws = self.workspace(T, stream) if workspace is None else workspace
+        r = _routing_struct(routing, T, self.cfg.top_k, E)
         fn, name = ((lib().moe_mxfp4_forward, "moe_mxfp4_forward") if w_router is None else
                     (lib().moe_mxfp4_forward_hidden, "moe_mxfp4_forward_hidden"))
         st = fn(self._ctx, _ptr(hidden), _ptr(logits if w_router is None else w_router), T, _ptr(out),

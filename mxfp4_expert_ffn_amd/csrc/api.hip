@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/moe_mxfp4.h: argument checks,
 // workspace carve-up and the launch sequence of one forward call.
 //
-// A forward call is five to eight launches on the caller's stream and nothing else
+// A forward call is four to eight launches on the caller's stream and nothing else
 // (no allocation, no host synchronisation, no device-to-host copy), so it can
 // be captured into a HIP graph: the pages stress that at microsecond
 // operator times the gaps between operators matter (techllm.github.io
@@ -9,6 +9,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
+#include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -19,10 +22,16 @@
 struct moe_mxfp4_ctx {
     moe_mxfp4_config cfg;
     moe_mxfp4_weights w;
-    // optional stage timing: capacity slots of NUM_STAGES + 1 events each
+    // optional stage timing: capacity slots of NUM_STAGES + 1 events each;
+    // valid[slot] is set once every event of a call was recorded into it
     std::vector<hipEvent_t> events;
+    std::vector<char> valid;
     int32_t capacity = 0;
     int64_t ncalls = 0;
+    // MOE_MXFP4_LOG=1 at create: print the launch sequence of a call when
+    // it differs from the previous call's
+    bool log = false;
+    std::atomic<int32_t> logged_tokens{-1};
 };
 
 namespace {
@@ -87,11 +96,13 @@ moe_status check_config(const moe_mxfp4_config* c) {
         if (K != 256 && K % 512 != 0) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->max_tokens * c->top_k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
     if ((int64_t)c->d_model * c->d_ff > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED_SHAPE;
-    // MXFP8 activation codes (x: T x d bytes, h: P x f bytes) are read through
-    // buffer resources, whose offsets and record counts are 32-bit
-    if (c->act_mode == MOE_ACT_MXFP8_E4M3 &&
-        ((int64_t)c->max_tokens * c->d_model >= (int64_t)1 << 32 ||
-         (int64_t)c->max_tokens * c->top_k * c->d_ff >= (int64_t)1 << 32))
+    // The activation rows the expert kernels read (x: T rows of d, h: P rows
+    // of f) are addressed by 32-bit byte offsets: buffer-resource offsets for
+    // the MXFP8 codes (1 byte each), direct-to-LDS source offsets for bf16
+    // (2 bytes each).  Both arrays must stay below 4 GiB.
+    const int64_t act_bytes = c->act_mode == MOE_ACT_MXFP8_E4M3 ? 1 : 2;
+    if ((int64_t)c->max_tokens * c->d_model * act_bytes >= (int64_t)1 << 32 ||
+        (int64_t)c->max_tokens * c->top_k * c->d_ff * act_bytes >= (int64_t)1 << 32)
         return MOE_ERR_UNSUPPORTED_SHAPE;
     return MOE_OK;
 }
@@ -131,6 +142,13 @@ moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg, const moe_mxfp4_weights
     if (!ctx) return MOE_ERR_INTERNAL;
     ctx->cfg = *cfg;
     ctx->w = *weights;
+    const char* lg = std::getenv("MOE_MXFP4_LOG");
+    ctx->log = lg && *lg && std::strcmp(lg, "0") != 0;
+    if (ctx->log)
+        std::fprintf(stderr, "moe_mxfp4: create E=%d d=%d f=%d k=%d max_tokens=%d act=%s out=%s\n", cfg->num_experts,
+                     cfg->d_model, cfg->d_ff, cfg->top_k, cfg->max_tokens,
+                     cfg->act_mode == MOE_ACT_MXFP8_E4M3 ? "mxfp8" : "bf16",
+                     cfg->out_dtype == MOE_OUT_F32 ? "f32" : "bf16");
     *out = ctx;
     return MOE_OK;
 }
@@ -146,6 +164,7 @@ moe_status moe_mxfp4_stage_timing(moe_mxfp4_ctx* ctx, int32_t capacity) {
     if (!ctx || capacity < 0) return MOE_ERR_INVALID_ARG;
     for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
     ctx->events.clear();
+    ctx->valid.clear();
     ctx->capacity = 0;
     ctx->ncalls = 0;
     if (capacity == 0) return MOE_OK;
@@ -160,30 +179,32 @@ moe_status moe_mxfp4_stage_timing(moe_mxfp4_ctx* ctx, int32_t capacity) {
         }
         ctx->events.push_back(e);
     }
+    ctx->valid.assign((size_t)capacity, 0);
     ctx->capacity = capacity;
     return MOE_OK;
 }
 
 moe_status moe_mxfp4_stage_times(moe_mxfp4_ctx* ctx, float* total_ms, int32_t* calls) {
     if (!ctx || !total_ms || !calls || ctx->capacity == 0) return MOE_ERR_INVALID_ARG;
+    // slots 0 .. held-1 were written; a slot whose call failed part-way is
+    // not valid and is skipped
     const int64_t held = ctx->ncalls < ctx->capacity ? ctx->ncalls : ctx->capacity;
     for (int i = 0; i < MOE_MXFP4_NUM_STAGES; ++i) total_ms[i] = 0.f;
-    *calls = (int32_t)held;
-    if (held > 0) {
-        const int64_t last = (ctx->ncalls - 1) % ctx->capacity;
-        if (hipEventSynchronize(ctx->events[last * (MOE_MXFP4_NUM_STAGES + 1) + MOE_MXFP4_NUM_STAGES]) !=
-            hipSuccess)
-            return MOE_ERR_HIP;
-        for (int64_t slot = 0; slot < held; ++slot) {
-            hipEvent_t* ev = &ctx->events[slot * (MOE_MXFP4_NUM_STAGES + 1)];
-            for (int i = 0; i < MOE_MXFP4_NUM_STAGES; ++i) {
-                float ms = 0.f;
-                if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) return MOE_ERR_HIP;
-                total_ms[i] += ms;
-            }
+    int32_t counted = 0;
+    for (int64_t slot = 0; slot < held; ++slot) {
+        if (!ctx->valid[slot]) continue;
+        hipEvent_t* ev = &ctx->events[slot * (MOE_MXFP4_NUM_STAGES + 1)];
+        if (hipEventSynchronize(ev[MOE_MXFP4_NUM_STAGES]) != hipSuccess) return MOE_ERR_HIP;
+        for (int i = 0; i < MOE_MXFP4_NUM_STAGES; ++i) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, ev[i], ev[i + 1]) != hipSuccess) return MOE_ERR_HIP;
+            total_ms[i] += ms;
         }
+        ++counted;
     }
+    *calls = counted;
     ctx->ncalls = 0;
+    std::fill(ctx->valid.begin(), ctx->valid.end(), 0);
     return MOE_OK;
 }
 
@@ -195,6 +216,70 @@ size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_ctx* ctx, int32_t num_tokens) {
 }  // extern "C"
 
 namespace {
+
+// The launches of one forward call on stream s, the workspace already
+// carved; mark(i) records stage-timing event i (a no-op when timing is off).
+template <typename Mark>
+moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router_logits, const void* w_router,
+                      float* ws_logits, const moe::Dims& dm, const moe::Workspace& ws, void* out,
+                      const moe_mxfp4_routing* debug_out, hipStream_t s, Mark mark) {
+    const moe_mxfp4_config& c = ctx->cfg;
+    const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
+    if (mark(0) != hipSuccess) return MOE_ERR_HIP;
+    if (w_router) {
+        // the projection is timed with the routing stage
+        if (fault_at("router") ||
+            moe::launch_router(x, static_cast<const uint16_t*>(w_router), ws_logits, dm, s) != hipSuccess)
+            return MOE_ERR_HIP;
+        router_logits = ws_logits;
+    }
+    const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
+    const bool fused_rs = moe::route_sort_fused(dm);
+    if (fused_rs) {
+        // one launch; its time is recorded as the routing stage
+        if (fault_at("route") || moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s) != hipSuccess ||
+            mark(1) != hipSuccess || mark(2) != hipSuccess)
+            return MOE_ERR_HIP;
+    } else {
+        if (fault_at("route") || moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (fault_at("sort") || moe::launch_sort(dm, ws, chunk_rows, s) != hipSuccess || mark(2) != hipSuccess)
+            return MOE_ERR_HIP;
+    }
+    if (mx8 && (fault_at("quant") || moe::launch_quant_x8(x, dm, ws, s) != hipSuccess)) return MOE_ERR_HIP;
+    if (mark(3) != hipSuccess) return MOE_ERR_HIP;
+    if (fault_at("gateup")) return MOE_ERR_HIP;
+    const hipError_t gu = mx8 ? moe::launch_gateup_dense(ctx->w, dm, ws, s) : moe::launch_gateup(x, ctx->w, dm, ws, s);
+    if (gu != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
+    if (fault_at("down")) return MOE_ERR_HIP;
+    const hipError_t dn = mx8 ? moe::launch_down_dense(ctx->w, dm, ws, s) : moe::launch_down(ctx->w, dm, ws, s);
+    if (dn != hipSuccess || mark(5) != hipSuccess) return MOE_ERR_HIP;
+    if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, mx8, s) != hipSuccess ||
+        mark(6) != hipSuccess)
+        return MOE_ERR_HIP;
+
+    if (ctx->log && ctx->logged_tokens.exchange(dm.T) != dm.T)
+        std::fprintf(stderr, "moe_mxfp4: T=%d P=%d E=%d d=%d f=%d k=%d: %s%s%s%s, combine (%s per-pair outputs)\n",
+                     dm.T, dm.P, dm.E, dm.d, dm.f, dm.k, w_router ? "router projection, " : "",
+                     fused_rs ? "routing+permutation (one launch)" : "routing, permutation",
+                     mx8 ? ", MXFP8 quantisation of x" : "",
+                     mx8 ? ", dense gate/up + SwiGLU (FP8 x FP4 scaled MFMA), dense down"
+                         : ", streaming gate/up + SwiGLU (FP4->bf16 MFMA), streaming down",
+                     mx8 ? "fp16-coded" : "float32");
+
+    if (debug_out) {
+        const size_t P = (size_t)dm.P;
+        struct { void* dst; const void* src; size_t n; } cp[4] = {
+            {debug_out->topk_ids, ws.topk_ids, P * sizeof(int32_t)},
+            {debug_out->topk_w, ws.topk_w, P * sizeof(float)},
+            {debug_out->expert_offsets, ws.offsets, (size_t)(c.num_experts + 1) * sizeof(int32_t)},
+            {debug_out->sorted_pairs, ws.sorted_pairs, P * sizeof(int32_t)}};
+        for (auto& k : cp)
+            if (k.dst && hipMemcpyAsync(k.dst, k.src, k.n, hipMemcpyDeviceToDevice, s) != hipSuccess)
+                return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
 
 // One forward call: router logits given (w_router == NULL) or projected from
 // the hidden states with w_router into the workspace first.
@@ -240,57 +325,21 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const uint16_t* x = static_cast<const uint16_t*>(hidden);
 
-    hipEvent_t* ev = nullptr;
-    if (ctx->capacity > 0)
-        ev = &ctx->events[(size_t)(ctx->ncalls++ % ctx->capacity) * (MOE_MXFP4_NUM_STAGES + 1)];
-    auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
-
-    const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
-    if (mark(0) != hipSuccess) return MOE_ERR_HIP;
-    if (w_router) {
-        // the projection is timed with the routing stage
-        if (fault_at("router") ||
-            moe::launch_router(x, static_cast<const uint16_t*>(w_router), ws_logits, dm, s) != hipSuccess)
-            return MOE_ERR_HIP;
-        router_logits = ws_logits;
+    if (ctx->capacity == 0)
+        return launch_all(ctx, x, router_logits, w_router, ws_logits, dm, ws, out, debug_out, s,
+                          [](int) { return hipSuccess; });
+    // stage timing: the call's events go to slot ncalls % capacity, which
+    // counts only if every launch and event of the call succeeded
+    const int64_t slot = ctx->ncalls % ctx->capacity;
+    hipEvent_t* ev = &ctx->events[(size_t)slot * (MOE_MXFP4_NUM_STAGES + 1)];
+    ctx->valid[slot] = 0;
+    const moe_status st = launch_all(ctx, x, router_logits, w_router, ws_logits, dm, ws, out, debug_out, s,
+                                     [&](int i) { return hipEventRecord(ev[i], s); });
+    if (st == MOE_OK) {
+        ctx->valid[slot] = 1;
+        ++ctx->ncalls;
     }
-    const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
-    if (moe::route_sort_fused(dm)) {
-        // one launch; its time is recorded as the routing stage
-        if (fault_at("route") || moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s) != hipSuccess ||
-            mark(1) != hipSuccess || mark(2) != hipSuccess)
-            return MOE_ERR_HIP;
-    } else {
-        if (fault_at("route") || moe::launch_route(router_logits, dm, ws, s) != hipSuccess || mark(1) != hipSuccess)
-            return MOE_ERR_HIP;
-        if (fault_at("sort") || moe::launch_sort(dm, ws, chunk_rows, s) != hipSuccess || mark(2) != hipSuccess)
-            return MOE_ERR_HIP;
-    }
-    if (mx8 && (fault_at("quant") || moe::launch_quant_x8(x, dm, ws, s) != hipSuccess)) return MOE_ERR_HIP;
-    if (mark(3) != hipSuccess) return MOE_ERR_HIP;
-    if (fault_at("gateup")) return MOE_ERR_HIP;
-    const hipError_t gu = mx8 ? moe::launch_gateup_dense(ctx->w, dm, ws, s)
-                              : moe::launch_gateup(x, ctx->w, dm, ws, s);
-    if (gu != hipSuccess || mark(4) != hipSuccess) return MOE_ERR_HIP;
-    if (fault_at("down")) return MOE_ERR_HIP;
-    const hipError_t dn = mx8 ? moe::launch_down_dense(ctx->w, dm, ws, s) : moe::launch_down(ctx->w, dm, ws, s);
-    if (dn != hipSuccess || mark(5) != hipSuccess) return MOE_ERR_HIP;
-    if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, mx8, s) != hipSuccess ||
-        mark(6) != hipSuccess)
-        return MOE_ERR_HIP;
-
-    if (debug_out) {
-        const size_t P = (size_t)dm.P;
-        struct { void* dst; const void* src; size_t n; } cp[4] = {
-            {debug_out->topk_ids, ws.topk_ids, P * sizeof(int32_t)},
-            {debug_out->topk_w, ws.topk_w, P * sizeof(float)},
-            {debug_out->expert_offsets, ws.offsets, (size_t)(c.num_experts + 1) * sizeof(int32_t)},
-            {debug_out->sorted_pairs, ws.sorted_pairs, P * sizeof(int32_t)}};
-        for (auto& k : cp)
-            if (k.dst && hipMemcpyAsync(k.dst, k.src, k.n, hipMemcpyDeviceToDevice, s) != hipSuccess)
-                return MOE_ERR_HIP;
-    }
-    return MOE_OK;
+    return st;
 }
 
 }  // namespace

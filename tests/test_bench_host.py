@@ -1,5 +1,7 @@
 """Host-side logic of bench.py (CPU only: nothing here touches a GPU)."""
+import hashlib
 import os
+import re
 import subprocess
 import sys
 
@@ -23,7 +25,7 @@ def test_traffic_comes_from_the_committed_counter_summary(workload, mx8):
     # the summary's own figure while the kernel source is the one it was
     # taken on; null otherwise (a kernel edited after its counters were read)
     t = bench.measured_traffic(workload, mx8)
-    text = open(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")).read()
+    text = open(os.path.join(ROOT, "profiles", f"beyond_l2_bytes_{workload}.md")).read()
     assert t is None or (t > 0 and f"traffic bytes per launch: {t:.0f}" in text)
 
 
@@ -32,9 +34,12 @@ def test_traffic_is_dropped_once_the_kernel_source_changes(tmp_path):
     (tmp_path / "profiles").mkdir()
     csrc = tmp_path / "mxfp4_expert_ffn_amd" / "csrc"
     csrc.mkdir(parents=True)
-    prof = open(os.path.join(ROOT, "profiles", "hbm_traffic_verify_32seq.md")).read()
-    (tmp_path / "profiles" / "hbm_traffic_verify_32seq.md").write_text(prof)
-    src = open(os.path.join(ROOT, "mxfp4_expert_ffn_amd", "csrc", "expert_gemm.hip")).read()
+    prof = open(os.path.join(ROOT, "profiles", "beyond_l2_bytes_verify_32seq.md")).read()
+    src = "// a kernel source\n"
+    digest = hashlib.sha256(src.encode()).hexdigest()
+    prof = re.sub(r"kernel source sha256: `[0-9a-f]+`", f"kernel source sha256: `{digest}`", prof)
+    prof = re.sub(r"kernel source: `[^`]+`", "kernel source: `mxfp4_expert_ffn_amd/csrc/expert_gemm.hip`", prof)
+    (tmp_path / "profiles" / "beyond_l2_bytes_verify_32seq.md").write_text(prof)
     (csrc / "expert_gemm.hip").write_text(src)
     root = str(tmp_path)
     assert bench.measured_traffic("verify_32seq", False, root) is not None      # same bytes: kept

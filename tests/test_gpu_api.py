@@ -201,6 +201,37 @@ def test_a_failed_launch_is_reported_and_leaves_the_context_usable(small, site, 
     assert torch.equal(layer(x, lg), y0)
 
 
+@pytest.mark.parametrize("site", ["gateup", "combine"])
+def test_a_failed_call_is_not_counted_by_stage_timing(small, site, monkeypatch):
+    # a call that fails part-way has recorded only some of its events: it
+    # must not be summed, and the slot it used must be reusable
+    moe = _moe()
+    w, acts, wts, dev = small
+    layer = moe.MoeMxfp4(dev, w.E, w.d, w.f, w.k, max_tokens=w.T)
+    x, lg = _inputs(acts, w.T)
+    for cap, good_before, expect in ((4, 2, 2), (2, 2, 1)):
+        layer.stage_timing(cap)
+        for _ in range(good_before):
+            layer(x, lg)
+        monkeypatch.setenv("MOE_MXFP4_FAULT", site)
+        with pytest.raises(moe.MoeError):
+            layer(x, lg)
+        monkeypatch.delenv("MOE_MXFP4_FAULT")
+        torch.cuda.synchronize()
+        # cap 4: slots 0, 1 hold good calls, the failed one is not counted;
+        # cap 2: the failed call reused slot 0, so only slot 1 is whole
+        times, n = layer.stage_times()
+        assert n == expect, (cap, n)
+        assert all(v >= 0.0 for v in times.values())
+        assert times["gateup"] > 0.0 and times["combine"] > 0.0
+        # after the failure the next good call records normally
+        layer(x, lg)
+        torch.cuda.synchronize()
+        times, n = layer.stage_times()
+        assert n == 1 and times["combine"] > 0.0
+    layer.stage_timing(0)
+
+
 def test_a_failed_acceptance_launch_is_reported(monkeypatch):
     moe = _moe()
     d = synth.dflash_batch(3, 4, 300, seed=12)
