@@ -233,6 +233,29 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden,
                              void* hip_stream, const moe_mxfp4_routing* debug_out);
 
 /*
+ * moe_mxfp4_forward for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as moe_mxfp4_forward
+ * minus the workspace: the call uses a scratch array of
+ * MOE_MXFP4_NOALLOC_SCRATCH_BYTES that the library holds in device memory,
+ * one per GPU, from the first call on that GPU until the process ends (the
+ * first call on a GPU looks up its address; no call allocates or frees).
+ * The scratch keeps the last call's contents and every call on a GPU shares
+ * it, so calls on one GPU whose executions overlap in time (concurrent
+ * streams, or concurrent host threads) race and give undefined results;
+ * serialise them (one stream, or events).  Nothing in it needs clearing:
+ * every value a call reads from it was written earlier in the same call.
+ * Errors: as moe_mxfp4_forward; WORKSPACE when the call would need more
+ * scratch than MOE_MXFP4_NOALLOC_SCRATCH_BYTES (moe_mxfp4_workspace_bytes
+ * gives the figure; 256 tokens at d_model 4096, d_ff 1536, top-8 need about
+ * 40 MB), checked before anything touches the device.
+ */
+#define MOE_MXFP4_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, const float* router_logits,
+                                     int32_t num_tokens, void* out, void* hip_stream,
+                                     const moe_mxfp4_routing* debug_out);
+
+/*
  * Router projection, the step in front of the routing:
  *   logits[t][e] = sum_i hidden[t][i] * w_router[e][i]
  * with bf16 inputs and float32 accumulation on the matrix cores, in an order

@@ -31,7 +31,10 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create
            "moe_mxfp4_debug_dequant", "moe_mxfp4_quantize_weights", "moe_mxfp4_stage_timing",
            "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights",
            "moe_mxfp4_quantize_act_mxfp8", "moe_mxfp4_router_logits", "moe_mxfp4_forward_hidden",
-           "moe_mxfp4_dflash_workspace_bytes", "moe_mxfp4_dflash_accept", "moe_mxfp4_probe")
+           "moe_mxfp4_dflash_workspace_bytes", "moe_mxfp4_dflash_accept", "moe_mxfp4_probe",
+           "moe_mxfp4_forward_noalloc")
+# Scratch bytes moe_mxfp4_forward_noalloc holds per GPU (MOE_MXFP4_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 NUM_STAGES = 6
 STAGES = ("route", "sort", "quant", "gateup", "down", "combine")
 
@@ -84,6 +87,8 @@ def lib():
         L.moe_mxfp4_workspace_bytes.restype = sz
         L.moe_mxfp4_forward.argtypes = [P, P, P, i32, P, P, sz, P, ctypes.POINTER(Routing)]
         L.moe_mxfp4_forward.restype = ctypes.c_int
+        L.moe_mxfp4_forward_noalloc.argtypes = [P, P, P, i32, P, P, ctypes.POINTER(Routing)]
+        L.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
         L.moe_mxfp4_forward_hidden.argtypes = [P, P, P, i32, P, P, sz, P, ctypes.POINTER(Routing)]
         L.moe_mxfp4_forward_hidden.restype = ctypes.c_int
         L.moe_mxfp4_router_logits.argtypes = [P, P, P, i32, P, P]
@@ -261,6 +266,22 @@ class MoeMxfp4:
         return out
 
     __call__ = forward
+
+    def forward_noalloc(self, hidden, logits, out, routing: dict | None = None, stream=None):
+        """moe_mxfp4_forward_noalloc: as ``forward`` with the logits given,
+        but on the library's own per-GPU scratch (no workspace, nothing
+        allocated); ``out`` must be given.  Calls on one GPU share the
+        scratch, so they must not overlap in time."""
+        import torch
+        T = hidden.shape[0]
+        _require(hidden, torch.bfloat16, (T, self.cfg.d_model), "hidden")
+        _require(logits, torch.float32, (T, self.cfg.num_experts), "logits")
+        out = self._out(out, T, hidden.device, stream)
+        r = _routing_struct(routing, T, self.cfg.top_k, self.cfg.num_experts)
+        _check(lib().moe_mxfp4_forward_noalloc(self._ctx, _ptr(hidden), _ptr(logits), T, _ptr(out), _stream(stream),
+                                               ctypes.byref(r) if r is not None else None),
+               "moe_mxfp4_forward_noalloc")
+        return out
 
     def router_logits(self, hidden, w_router, out=None, stream=None):
         """hidden: bf16 [T, d]; w_router: bf16 [E, d] -> float32 logits [T, E]."""

@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -342,6 +343,29 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     return st;
 }
 
+// Scratch of moe_mxfp4_forward_noalloc: a device array of fixed size (one
+// per GPU, held until the process ends).  In host code `scratch` names a
+// host-side stand-in, so its device address is looked up once per device
+// with hipGetSymbolAddress and only that address is ever handed to kernels.
+__device__ __align__(256) uint8_t scratch[MOE_MXFP4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (nullptr on a HIP error).
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        scratch_ptr[dev] = p;
+    }
+    return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,6 +376,22 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden, const float
     if (!router_logits && num_tokens > 0) return MOE_ERR_INVALID_ARG;
     return forward_impl(ctx, hidden, router_logits, nullptr, num_tokens, out, workspace, workspace_bytes,
                         hip_stream, debug_out);
+}
+
+moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, const float* router_logits,
+                                     int32_t num_tokens, void* out, void* hip_stream,
+                                     const moe_mxfp4_routing* debug_out) {
+    if (!ctx || num_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (num_tokens > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    if (num_tokens == 0) return MOE_OK;
+    if (!router_logits) return MOE_ERR_INVALID_ARG;
+    // size check before anything touches the device
+    if (make_layout(ctx->cfg, num_tokens).total > (size_t)MOE_MXFP4_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    if (!hidden || !out) return MOE_ERR_INVALID_ARG;
+    void* ws = scratch_for_current_device();
+    if (!ws) return MOE_ERR_HIP;
+    return forward_impl(ctx, hidden, router_logits, nullptr, num_tokens, out, ws,
+                        (size_t)MOE_MXFP4_NOALLOC_SCRATCH_BYTES, hip_stream, debug_out);
 }
 
 moe_status moe_mxfp4_forward_hidden(moe_mxfp4_ctx* ctx, const void* hidden, const void* w_router,

@@ -137,6 +137,28 @@ def test_forward_validation_happens_before_any_launch():
         L.moe_mxfp4_destroy(h)
 
 
+def test_noalloc_forward_validates_before_touching_the_device():
+    st, h = _create(max_tokens=1 << 16)
+    L = moe.lib()
+    na = L.moe_mxfp4_forward_noalloc
+    try:
+        assert moe.NOALLOC_SCRATCH_BYTES == 64 << 20
+        assert na(None, FAKE, FAKE, 1, FAKE, None, None) == 1
+        assert na(h, FAKE, FAKE, -1, FAKE, None, None) == 1
+        assert na(h, FAKE, FAKE, (1 << 16) + 1, FAKE, None, None) == 3     # > max_tokens
+        assert na(h, None, None, 0, None, None, None) == 0                 # T = 0 no-op
+        assert na(h, FAKE, None, 8, FAKE, None, None) == 1                 # no logits
+        # a call whose workspace exceeds the scratch is refused (WORKSPACE)
+        big = next(T for T in range(1024, 1 << 16, 1024)
+                   if L.moe_mxfp4_workspace_bytes(h, T) > moe.NOALLOC_SCRATCH_BYTES)
+        assert L.moe_mxfp4_workspace_bytes(h, big - 1024) <= moe.NOALLOC_SCRATCH_BYTES
+        assert na(h, FAKE, FAKE, big, FAKE, None, None) == 5
+        assert na(h, None, FAKE, 8, FAKE, None, None) == 1
+        assert na(h, FAKE, FAKE, 8, None, None, None) == 1
+    finally:
+        L.moe_mxfp4_destroy(h)
+
+
 def test_router_entry_points_validate_before_any_launch():
     st, h = _create()
     L = moe.lib()
