@@ -299,6 +299,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="verify_32seq")
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated across steps")
+    ap.add_argument("--path", choices=("stream", "fused"), default=None,
+                    help="kernel path of the bf16 workloads (MOE_MXFP4_PATH): one launch per phase, or the "
+                         "persistent fused kernel; default: the library's")
     ap.add_argument("--cpu-tokens", type=int, default=128)       # about 10 s of oracle time on 16 cores
     ap.add_argument("--cpu-tokens-1thread", type=int, default=8,
                     help="tokens of the single-threaded oracle leg (8-, 256-token verify and tiny workloads)")
@@ -333,6 +336,8 @@ def main():
     import mxfp4_expert_ffn_amd as moe
     import synth
 
+    if args.path:
+        os.environ["MOE_MXFP4_PATH"] = args.path
     w = synth.workload(args.workload)
     mx8 = w.act == "mxfp8"
     torch.cuda.set_device(0)

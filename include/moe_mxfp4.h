@@ -256,6 +256,34 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
                                      const moe_mxfp4_routing* debug_out);
 
 /*
+ * Kernel paths (bf16 activations).  MOE_MXFP4_PATH, read when a context is
+ * created, selects how a forward call runs the steps after routing:
+ *   "stream" (default)  one launch per phase: permutation, gate/up + SwiGLU,
+ *                       down, combine;
+ *   "fused"             one persistent kernel for the permutation, gate/up
+ *                       and down (then the combine), whose work items hand
+ *                       over through counters in the workspace, so down work
+ *                       starts while gate/up still streams weights.  The
+ *                       pages' runtime keeps one engine kernel resident so
+ *                       that microsecond operators pay no gap between them
+ *                       (techllm.github.io "Xiaomi MiMo x TileRT", section
+ *                       "3. TileRT"); batches up to 8192 pairs.
+ * Both give bit-identical outputs.  Any other value makes create fail with
+ * MOE_ERR_INVALID_ARG.  MXFP8 mode has one path (the dense kernels).
+ *
+ * The fused kernel's waits for other workgroups are bounded; past the
+ * bound (or with MOE_MXFP4_SPIN_LIMIT set to a negative value, read on every
+ * call, for tests of this path) it raises an error word in the workspace,
+ * its workgroups exit normally and the call's outputs are undefined.
+ * moe_mxfp4_device_status waits for hip_stream and writes that word of the
+ * most recent call with `num_tokens` tokens on `workspace` (device) to
+ * *status (host): 0 = no wait gave up; always 0 on paths without such
+ * waits.  Errors: INVALID_ARG, CAPACITY, HIP.
+ */
+moe_status moe_mxfp4_device_status(const moe_mxfp4_ctx* ctx, const void* workspace, int32_t num_tokens,
+                                   int32_t* status, void* hip_stream);
+
+/*
  * Router projection, the step in front of the routing:
  *   logits[t][e] = sum_i hidden[t][i] * w_router[e][i]
  * with bf16 inputs and float32 accumulation on the matrix cores, in an order

@@ -32,7 +32,7 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create
            "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights",
            "moe_mxfp4_quantize_act_mxfp8", "moe_mxfp4_router_logits", "moe_mxfp4_forward_hidden",
            "moe_mxfp4_dflash_workspace_bytes", "moe_mxfp4_dflash_accept", "moe_mxfp4_probe",
-           "moe_mxfp4_forward_noalloc")
+           "moe_mxfp4_forward_noalloc", "moe_mxfp4_device_status")
 # Scratch bytes moe_mxfp4_forward_noalloc holds per GPU (MOE_MXFP4_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 NUM_STAGES = 6
@@ -89,6 +89,8 @@ def lib():
         L.moe_mxfp4_forward.restype = ctypes.c_int
         L.moe_mxfp4_forward_noalloc.argtypes = [P, P, P, i32, P, P, ctypes.POINTER(Routing)]
         L.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
+        L.moe_mxfp4_device_status.argtypes = [P, P, i32, ctypes.POINTER(i32), P]
+        L.moe_mxfp4_device_status.restype = ctypes.c_int
         L.moe_mxfp4_forward_hidden.argtypes = [P, P, P, i32, P, P, sz, P, ctypes.POINTER(Routing)]
         L.moe_mxfp4_forward_hidden.restype = ctypes.c_int
         L.moe_mxfp4_router_logits.argtypes = [P, P, P, i32, P, P]
@@ -282,6 +284,16 @@ class MoeMxfp4:
                                                ctypes.byref(r) if r is not None else None),
                "moe_mxfp4_forward_noalloc")
         return out
+
+    def device_status(self, num_tokens: int, workspace=None, stream=None) -> int:
+        """The fused kernel's error word of the last call with ``num_tokens``
+        tokens on ``workspace`` (default: this object's cached workspace for
+        ``stream``); waits for the stream.  0 = no device-side wait gave up."""
+        ws = self.workspace(num_tokens, stream) if workspace is None else workspace
+        st = ctypes.c_int32()
+        _check(lib().moe_mxfp4_device_status(self._ctx, _ptr(ws), num_tokens, ctypes.byref(st), _stream(stream)),
+               "moe_mxfp4_device_status")
+        return st.value
 
     def router_logits(self, hidden, w_router, out=None, stream=None):
         """hidden: bf16 [T, d]; w_router: bf16 [E, d] -> float32 logits [T, E]."""

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["api.hip", "router.hip", "dflash.hip", "probes.hip", "route_sort.hip", "expert_gemm.hip", "dense_gemm.hip", "combine.hip",
+SOURCES = ["api.hip", "router.hip", "dflash.hip", "probes.hip", "route_sort.hip", "expert_gemm.hip", "fused.hip", "dense_gemm.hip", "combine.hip",
            "quant_act.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -19,6 +19,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# fused.hip: one lane takes the next work unit with an atomic whose result is
+# only needed at the end of the current unit; the compiler's atomic optimizer
+# would rewrite it into a wave-wide form that waits for the result at once.
+EXTRA = {"fused.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -27,7 +31,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

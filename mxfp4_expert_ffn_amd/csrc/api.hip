@@ -33,6 +33,9 @@ struct moe_mxfp4_ctx {
     // it differs from the previous call's
     bool log = false;
     std::atomic<int32_t> logged_tokens{-1};
+    // bf16 activations: the persistent fused kernel ("fused") or one launch
+    // per phase ("stream", the default), from MOE_MXFP4_PATH at create
+    bool fused = false;
 };
 
 namespace {
@@ -44,7 +47,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t logits, ids, w, offsets, sorted, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, total;
+    size_t logits, ids, w, offsets, sorted, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, fctl, fcounts,
+        flists, total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
@@ -67,6 +71,11 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     L.h = at;       at += round256(P * (size_t)c.d_ff * (mx8 ? 1 : sizeof(uint16_t)));
     L.hs = at;      at += mx8 ? round256(P * (size_t)(c.d_ff / MOE_MXFP4_BLOCK)) : 0;
     L.o = at;       at += round256(P * (size_t)c.d_model * sizeof(float));
+    // the fused path's counters and per-expert pair lists (bf16 mode)
+    const bool fz = !mx8 && moe::fused_supported(dm);
+    L.fctl = at;    at += fz ? round256((size_t)moe::fused_ctl_ints(dm) * sizeof(int32_t)) : 0;
+    L.fcounts = at; at += fz ? round256((size_t)c.num_experts * sizeof(int32_t)) : 0;
+    L.flists = at;  at += fz ? round256((size_t)c.num_experts * T * sizeof(int32_t)) : 0;
     L.total = at;
     return L;
 }
@@ -80,6 +89,16 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
 bool fault_at(const char* site) {
     const char* e = std::getenv("MOE_MXFP4_FAULT");
     return e && std::strcmp(e, site) == 0;
+}
+
+// Poll rounds before a device-side wait of the fused kernel gives up (each
+// round sleeps ~0.1 us).  MOE_MXFP4_SPIN_LIMIT overrides it, for tests of
+// the error path: a negative value makes every wait give up at once, so the
+// kernel raises its error flag and every workgroup exits normally.  Read on
+// every call.
+int spin_limit() {
+    const char* e = std::getenv("MOE_MXFP4_SPIN_LIMIT");
+    return e && *e ? std::atoi(e) : (1 << 22);
 }
 
 moe_status check_config(const moe_mxfp4_config* c) {
@@ -139,17 +158,22 @@ moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg, const moe_mxfp4_weights
         if (!p) return MOE_ERR_INVALID_ARG;
     for (const void* p : ptrs)
         if (!aligned16(p)) return MOE_ERR_ALIGNMENT;
+    const char* path = std::getenv("MOE_MXFP4_PATH");
+    if (path && *path && std::strcmp(path, "fused") != 0 && std::strcmp(path, "stream") != 0)
+        return MOE_ERR_INVALID_ARG;
     moe_mxfp4_ctx* ctx = new (std::nothrow) moe_mxfp4_ctx;
     if (!ctx) return MOE_ERR_INTERNAL;
     ctx->cfg = *cfg;
     ctx->w = *weights;
+    ctx->fused = path && std::strcmp(path, "fused") == 0;
     const char* lg = std::getenv("MOE_MXFP4_LOG");
     ctx->log = lg && *lg && std::strcmp(lg, "0") != 0;
     if (ctx->log)
-        std::fprintf(stderr, "moe_mxfp4: create E=%d d=%d f=%d k=%d max_tokens=%d act=%s out=%s\n", cfg->num_experts,
-                     cfg->d_model, cfg->d_ff, cfg->top_k, cfg->max_tokens,
+        std::fprintf(stderr, "moe_mxfp4: create E=%d d=%d f=%d k=%d max_tokens=%d act=%s out=%s path=%s\n",
+                     cfg->num_experts, cfg->d_model, cfg->d_ff, cfg->top_k, cfg->max_tokens,
                      cfg->act_mode == MOE_ACT_MXFP8_E4M3 ? "mxfp8" : "bf16",
-                     cfg->out_dtype == MOE_OUT_F32 ? "f32" : "bf16");
+                     cfg->out_dtype == MOE_OUT_F32 ? "f32" : "bf16",
+                     cfg->act_mode == MOE_ACT_MXFP8_E4M3 ? "dense" : ctx->fused ? "fused" : "stream");
     *out = ctx;
     return MOE_OK;
 }
@@ -218,6 +242,22 @@ size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_ctx* ctx, int32_t num_tokens) {
 
 namespace {
 
+// The optional routing outputs, copied from the workspace on stream s.
+moe_status copy_debug(const moe_mxfp4_config& c, const moe::Dims& dm, const moe::Workspace& ws,
+                      const moe_mxfp4_routing* debug_out, hipStream_t s) {
+    if (!debug_out) return MOE_OK;
+    const size_t P = (size_t)dm.P;
+    struct { void* dst; const void* src; size_t n; } cp[4] = {
+        {debug_out->topk_ids, ws.topk_ids, P * sizeof(int32_t)},
+        {debug_out->topk_w, ws.topk_w, P * sizeof(float)},
+        {debug_out->expert_offsets, ws.offsets, (size_t)(c.num_experts + 1) * sizeof(int32_t)},
+        {debug_out->sorted_pairs, ws.sorted_pairs, P * sizeof(int32_t)}};
+    for (auto& k : cp)
+        if (k.dst && hipMemcpyAsync(k.dst, k.src, k.n, hipMemcpyDeviceToDevice, s) != hipSuccess)
+            return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 // The launches of one forward call on stream s, the workspace already
 // carved; mark(i) records stage-timing event i (a no-op when timing is off).
 template <typename Mark>
@@ -235,6 +275,30 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
         router_logits = ws_logits;
     }
     const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
+    if (!mx8 && ctx->fused && moe::fused_supported(dm)) {
+        // routing (which clears the fused kernel's counters), the per-expert
+        // pair lists and chunk list (timed as the permutation stage), the
+        // persistent kernel (gate/up and down: timed as the gate/up stage),
+        // the combine
+        if (fault_at("route") ||
+            moe::launch_route(router_logits, dm, ws, s, ws.fctl, moe::fused_ctl_ints(dm)) != hipSuccess ||
+            mark(1) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (fault_at("sort") || moe::launch_fused_lists(dm, ws, s) != hipSuccess || mark(2) != hipSuccess ||
+            mark(3) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (fault_at("gateup") || moe::launch_fused(x, ctx->w, dm, ws, spin_limit(), s) != hipSuccess ||
+            mark(4) != hipSuccess || mark(5) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, false, s) != hipSuccess ||
+            mark(6) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (ctx->log && ctx->logged_tokens.exchange(dm.T) != dm.T)
+            std::fprintf(stderr, "moe_mxfp4: T=%d P=%d E=%d d=%d f=%d k=%d: %srouting, per-expert pair lists, "
+                         "persistent kernel (gate/up + SwiGLU, down), combine (float32 per-pair outputs)\n",
+                         dm.T, dm.P, dm.E, dm.d, dm.f, dm.k, w_router ? "router projection, " : "");
+        return copy_debug(c, dm, ws, debug_out, s);
+    }
     const bool fused_rs = moe::route_sort_fused(dm);
     if (fused_rs) {
         // one launch; its time is recorded as the routing stage
@@ -268,18 +332,7 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
                          : ", streaming gate/up + SwiGLU (FP4->bf16 MFMA), streaming down",
                      mx8 ? "fp16-coded" : "float32");
 
-    if (debug_out) {
-        const size_t P = (size_t)dm.P;
-        struct { void* dst; const void* src; size_t n; } cp[4] = {
-            {debug_out->topk_ids, ws.topk_ids, P * sizeof(int32_t)},
-            {debug_out->topk_w, ws.topk_w, P * sizeof(float)},
-            {debug_out->expert_offsets, ws.offsets, (size_t)(c.num_experts + 1) * sizeof(int32_t)},
-            {debug_out->sorted_pairs, ws.sorted_pairs, P * sizeof(int32_t)}};
-        for (auto& k : cp)
-            if (k.dst && hipMemcpyAsync(k.dst, k.src, k.n, hipMemcpyDeviceToDevice, s) != hipSuccess)
-                return MOE_ERR_HIP;
-    }
-    return MOE_OK;
+    return copy_debug(c, dm, ws, debug_out, s);
 }
 
 // One forward call: router logits given (w_router == NULL) or projected from
@@ -321,6 +374,9 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     ws.hs = reinterpret_cast<uint8_t*>(base + L.hs);
     ws.o = reinterpret_cast<float*>(base + L.o);
     ws.os = reinterpret_cast<uint8_t*>(base + L.o + (size_t)num_tokens * c.top_k * c.d_model * sizeof(uint16_t));
+    ws.fctl = reinterpret_cast<int32_t*>(base + L.fctl);
+    ws.fcounts = reinterpret_cast<int32_t*>(base + L.fcounts);
+    ws.flists = reinterpret_cast<int32_t*>(base + L.flists);
 
     moe::Dims dm{num_tokens, c.d_model, c.d_ff, c.num_experts, c.top_k, num_tokens * c.top_k};
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
@@ -400,6 +456,27 @@ moe_status moe_mxfp4_forward_hidden(moe_mxfp4_ctx* ctx, const void* hidden, cons
     if (!w_router && num_tokens > 0) return MOE_ERR_INVALID_ARG;
     return forward_impl(ctx, hidden, nullptr, w_router, num_tokens, out, workspace, workspace_bytes, hip_stream,
                         debug_out);
+}
+
+moe_status moe_mxfp4_device_status(const moe_mxfp4_ctx* ctx, const void* workspace, int32_t num_tokens,
+                                   int32_t* status, void* hip_stream) {
+    if (!ctx || !status || num_tokens < 0) return MOE_ERR_INVALID_ARG;
+    if (num_tokens > ctx->cfg.max_tokens) return MOE_ERR_CAPACITY;
+    *status = 0;
+    const moe::Dims dm{num_tokens, ctx->cfg.d_model, ctx->cfg.d_ff, ctx->cfg.num_experts, ctx->cfg.top_k,
+                       num_tokens * ctx->cfg.top_k};
+    if (num_tokens == 0 || ctx->cfg.act_mode != MOE_ACT_BF16 || !ctx->fused || !moe::fused_supported(dm))
+        return MOE_OK;                                // no device-side waits on this path
+    if (!workspace) return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(ctx->cfg, num_tokens);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    int32_t word = 0;
+    const char* src = static_cast<const char*>(workspace) + L.fctl + moe::kFusedErrorWord * sizeof(int32_t);
+    if (hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return MOE_ERR_HIP;
+    *status = word;
+    return MOE_OK;
 }
 
 moe_status moe_mxfp4_router_logits(const moe_mxfp4_ctx* ctx, const void* hidden, const void* w_router,

@@ -103,6 +103,9 @@ struct Workspace {
                               // mode: fp16 codes in the first half of that space
     uint8_t* os;              // MXFP8 mode: [P][d/128] scale exponents + 127 of o's fp16
                               // codes, placed after them inside o's space
+    int32_t* fctl;            // fused path: work-queue, error and completion counters
+    int32_t* fcounts;         // fused path: [E] pairs per expert
+    int32_t* flists;          // fused path: [E][T] pair ids of each expert, ascending
 };
 
 // Problem description passed by value to kernels.
@@ -122,6 +125,21 @@ inline int max_chunks(const Dims& dm) {
     return active + dm.P / kChunk;
 }
 
+// The fused path (bf16 activations): after the routing launch (which clears
+// the fused_ctl_ints(dm) counters), launch_fused_lists builds the stable
+// per-expert pair lists, the expert offsets and the chunk list, and
+// launch_fused runs gate/up and down as work units of one persistent
+// kernel.  Up to kFusedMaxPairs pairs.
+constexpr int kFusedMaxPairs = 8192;
+bool fused_supported(const Dims& dm);
+int fused_ctl_ints(const Dims& dm);
+// Index of the error word in the counters: nonzero after a call in which a
+// device-side wait gave up.
+constexpr int kFusedErrorWord = 64;   // ints from the start of the counters
+hipError_t launch_fused_lists(const Dims& dm, const Workspace& ws, hipStream_t s);
+hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
+                        int spin_limit, hipStream_t s);
+
 // Kernel launchers (each returns hipGetLastError() of its launch).
 // Router projection: logits [T][E] = x [T][d] . w [E][d]^T (bf16 in, float32 out).
 hipError_t launch_router(const uint16_t* x, const uint16_t* w, float* logits, const Dims& dm, hipStream_t s);
@@ -135,7 +153,10 @@ size_t dflash_workspace_bytes(int32_t B, int32_t V);
 hipError_t launch_dflash_accept(int32_t B, int32_t G, int32_t V, const int32_t* draft, const float* p_draft,
                                 const float* p_target, const float* u, const float* r, int32_t* n_accepted,
                                 int32_t* next_token, void* workspace, hipStream_t s);
-hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s);
+// Routing (topk_ids, topk_w); with zero != nullptr the launch also clears
+// zero[0 .. nzero).
+hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s,
+                        int32_t* zero = nullptr, int nzero = 0);
 hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipStream_t s);
 // Small batches: routing and permutation in one launch (when route_sort_fused).
 bool route_sort_fused(const Dims& dm);

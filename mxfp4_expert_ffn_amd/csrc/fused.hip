@@ -1,0 +1,333 @@
+// The expert layer after routing as ONE resident kernel: gate/up + SwiGLU
+// and the down projection run as work items of a persistent grid, so the
+// two phases overlap instead of each draining the GPU before the next launch
+// ramps up.  A small launch in front of it builds the permutation.
+//
+// The pages' runtime keeps a single engine kernel resident on the GPU so
+// that microsecond operators pay no launch or synchronisation gap between
+// them, and streams the next tile while the current one computes
+// (techllm.github.io "Xiaomi MiMo x TileRT", section "3. TileRT — GPU에 상주하는
+// 런타임"; dothoosh.com article, section "TileRT: عصر فشار بر GPU").  On gfx950
+// the same idea takes this form:
+//
+//   - k_expert_lists (one workgroup per expert): the ids of expert e's pairs
+//     in ascending pair order -- a stable counting sort, each expert
+//     independent -- and their count; the last workgroup to finish (a
+//     counter) turns the counts into expert offsets and the chunk list
+//     (chunks of <= 64 pairs, expert by expert).
+//   - k_fused (as many workgroups as the GPU holds at once): workgroup b
+//     first runs the gate/up units (chunk, column tile) b, b + G, b + 2G, ...
+//     -- a fixed assignment, no queue atomics, and a gate/up unit never
+//     waits -- and then takes down units from a queue (one atomic per unit)
+//     in chunk order, so the workgroups that finish gate/up first take the
+//     down work of the chunks that finished first.  A down unit of chunk c
+//     waits only for the gate/up units of chunk c (a counter per chunk),
+//     which resident workgroups finish without waiting on anything.  Down
+//     work starts while gate/up still streams the weights of later chunks.
+//   - Every wait is bounded: past the limit the kernel raises an error word
+//     in the workspace and its workgroups exit normally (a grid larger than
+//     what the GPU holds, for example because another kernel occupies it,
+//     can only delay the units of workgroups not yet started).
+//   - The gate/up -> down handoff crosses XCDs, whose L2 caches are not kept
+//     coherent with each other: gate/up stores h with device-coherent
+//     (agent-scope) stores, every wave waits for them, and then one lane
+//     bumps the chunk's counter; the consumer's lane 0 polls with agent-scope
+//     loads and invalidates its caches (agent-scope acquire) before the
+//     workgroup reads h.  (Writing the whole L2 back after every gate/up
+//     unit instead, the usual release, measured ~18 us slower at 256
+//     tokens.)
+//   - The counters are cleared by the routing launch that precedes these
+//     kernels in every call (no memset, so the call stays capturable).
+//
+// The unit bodies are the per-phase kernels' own pipeline (stream_pipe.hpp),
+// so every h and o value is bit-identical to the multi-launch path.
+#include "stream_pipe.hpp"
+
+namespace moe {
+namespace fused {
+namespace {
+
+using stream::GemmArgs;
+using stream::kDown;
+using stream::kGateUp;
+using stream::kSlot;
+using stream::kThreads;
+
+// ctl[] words.  Each counter sits on a 256-byte line of its own, so the
+// polls of waiting workgroups and the atomics on other counters do not queue
+// behind each other at one memory channel.
+constexpr int kLine = 64;                       // ints per 256 bytes
+enum { kScanDone = 0, kError = kLine, kDownQueue = 2 * kLine, kChunkDone = 3 * kLine };
+static_assert(kError == kFusedErrorWord, "the host reads the error word at this index");
+
+struct FusedArgs {
+    GemmArgs gu, dn;
+    const int32_t* ids;        // [P] expert of each pair (routing output)
+    int32_t* ctl;              // counters (cleared by the routing launch)
+    int32_t* counts;           // [E] pairs per expert
+    int32_t* lists;            // [E][T] pair ids of each expert, ascending
+    int32_t* offsets;          // [E+1] first sorted position of each expert
+    int32_t* sorted;           // [P] the permutation (written by the tile-0 gate/up units)
+    int32_t* chunks;           // chunk records (expert, first sorted position, pairs, rank of the first pair)
+    int32_t* nchunks;
+    int32_t E, T, P;
+    int32_t ntg, ntd;          // column tiles per chunk: gate/up, down
+    int32_t spin_limit;        // poll rounds before a wait gives up; < 0: every wait gives up at once
+};
+
+__device__ __forceinline__ int32_t load_agent(const int32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (one lane) until *p >= target.  False if the error flag is up (read
+// every 32 polls) or the poll limit runs out (then it raises the flag).
+__device__ bool wait_geq(const FusedArgs& f, const int32_t* p, int32_t target) {
+    for (int i = 0;; ++i) {
+        if (f.spin_limit >= 0 && load_agent(p) >= target) return true;
+        if (i % 32 == 31 && load_agent(f.ctl + kError) != 0) return false;
+        if (i >= f.spin_limit) {
+            __hip_atomic_fetch_or(f.ctl + kError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+// Every wave waits for its own stores (the h rows, stored device-coherent),
+// then the workgroup meets and lane 0 adds 1 to the chunk's counter.
+__device__ __forceinline__ void publish(int32_t* p) {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));        // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Lane 0 waits for *p >= target and acquires (its invalidation covers the
+// CU's vector L1 and the XCD's L2, which the workgroup's waves share); the
+// barrier then orders every wave's later reads after it.  Uniform result:
+// false when the wait failed.
+__device__ __forceinline__ bool await(const FusedArgs& f, const int32_t* p, int32_t target, int32_t* s_flag) {
+    if (threadIdx.x == 0) {
+        const bool ok = wait_geq(f, p, target);
+        if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_flag = ok;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+// Exclusive scan of one value per thread over the 256-thread workgroup;
+// *total gets the sum.  s_tmp: 4 ints of LDS.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int incl = wave_incl_scan(v, lane);
+    if (lane == kWave - 1) s_tmp[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+        const int t = s_tmp[w];
+        before += w < wave ? t : 0;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+// The pairs of expert blockIdx.x in ascending order.  Thread i owns the
+// contiguous ids [i*Q, i*Q + Q): it counts its matches, an exclusive scan
+// over the threads gives its first rank, and it writes its matches in
+// order.  The last workgroup to finish (the counter) then builds the expert
+// offsets and the chunk list from all counts: thread i takes experts 2i and
+// 2i + 1 (E <= 512).
+__global__ __launch_bounds__(kThreads) void k_expert_lists(FusedArgs f) {
+    __shared__ int32_t s_tmp[4], s_last;
+    const int e = blockIdx.x;
+    const int Q = (f.P + kThreads - 1) / kThreads;
+    const int p0 = threadIdx.x * Q, p1 = min(p0 + Q, f.P);
+    int n = 0;
+    for (int p = p0; p < p1; ++p) n += f.ids[p] == e;
+    int total;
+    int at = block_excl_scan(n, s_tmp, &total);
+    int32_t* list = f.lists + (size_t)e * f.T;
+    for (int p = p0; p < p1; ++p)
+        if (f.ids[p] == e) list[at++] = p;
+    if (threadIdx.x == 0) f.counts[e] = total;
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));        // vmcnt(0): this wave's stores done
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const int done = __hip_atomic_fetch_add(f.ctl + kScanDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == f.E - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_last = done == f.E - 1;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    const int n0 = e0 < f.E ? f.counts[e0] : 0, n1 = e1 < f.E ? f.counts[e1] : 0;
+    const int c0 = (n0 + kChunk - 1) / kChunk, c1 = (n1 + kChunk - 1) / kChunk;
+    int npairs, nch;
+    const int off = block_excl_scan(n0 + n1, s_tmp, &npairs);
+    const int coff = block_excl_scan(c0 + c1, s_tmp, &nch);
+    auto emit = [&](int ex, int nx, int first_pos, int first_chunk) {
+        f.offsets[ex] = first_pos;
+        for (int c = 0; c * kChunk < nx; ++c) {
+            int32_t* rec = f.chunks + kChunkRec * (first_chunk + c);
+            rec[0] = ex;
+            rec[1] = first_pos + c * kChunk;
+            rec[2] = min(kChunk, nx - c * kChunk);
+            rec[3] = c * kChunk;
+        }
+    };
+    if (e0 < f.E) emit(e0, n0, off, coff);
+    if (e1 < f.E) emit(e1, n1, off + n0, coff + c0);
+    if (threadIdx.x == 0) {
+        f.offsets[f.E] = npairs;
+        *f.nchunks = nch;
+    }
+}
+
+template <int RT, int DG, int DD>
+__global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
+    constexpr int kRing = DG > DD ? DG : DD;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kSlot];
+    __shared__ int32_t s_flag, s_next;
+    const int nc = __builtin_amdgcn_readfirstlane(*f.nchunks);
+    const int nG = nc * f.ntg, nD = nc * f.ntd;
+    // Gate/up units u = b, b + G, ... (never waiting), then down units from
+    // the down queue in chunk order, so a workgroup that finishes its gate/up
+    // work early takes the down work whose chunks finished first.  Two loops
+    // keep the two pipelines' registers apart.
+    for (int u = blockIdx.x; u < nG; u += gridDim.x) {
+        const int chunk = u / f.ntg, nt = u % f.ntg;
+        const int32_t* rec = f.chunks + kChunkRec * chunk;
+        const int e = __builtin_amdgcn_readfirstlane(rec[0]);
+        const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
+        const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
+        const int first = __builtin_amdgcn_readfirstlane(rec[3]);
+        const int32_t* pairs = f.lists + (size_t)e * f.T + first;
+        if (nt == 0 && (int)threadIdx.x < rows) f.sorted[m0 + threadIdx.x] = pairs[threadIdx.x];
+        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, pairs, m0, rows, [] {});
+        publish(f.ctl + kChunkDone + kLine * chunk);
+        __syncthreads();               // the LDS ring is free again
+    }
+    if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(f.ctl + kDownQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int v = __builtin_amdgcn_readfirstlane(s_next);
+    int next = 0;
+    // the next down unit is taken right before this one's first loads, and
+    // its index handed over through LDS at the end
+    auto take = [&] {
+        if (threadIdx.x == 0) next = __hip_atomic_fetch_add(f.ctl + kDownQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    while (v < nD) {
+        const int chunk = v / f.ntd, nt = v % f.ntd;
+        const int32_t* rec = f.chunks + kChunkRec * chunk;
+        const int e = __builtin_amdgcn_readfirstlane(rec[0]);
+        const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
+        const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
+        const int first = __builtin_amdgcn_readfirstlane(rec[3]);
+        const int32_t* pairs = f.lists + (size_t)e * f.T + first;
+        if (!await(f, f.ctl + kChunkDone + kLine * chunk, f.ntg, &s_flag)) return;
+        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, pairs, m0, rows, take);
+        if (threadIdx.x == 0) s_next = next;
+        __syncthreads();               // s_next holds the next unit; the LDS ring is free again
+        v = __builtin_amdgcn_readfirstlane(s_next);
+    }
+}
+
+template <int RT, int DG, int DD>
+hipError_t launch_variant(const FusedArgs& f, int items, hipStream_t s) {
+    // grid = the workgroups the GPU holds at once (no more are useful: each
+    // loops over items), found once per device
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_fused<RT, DG, DD>),
+                                                         kThreads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidValue;
+        cached[dev] = per_cu * cus > 0 ? per_cu * cus : 1;
+    }
+    const int grid = items < cached[dev] ? items : cached[dev];
+    hipLaunchKernelGGL((k_fused<RT, DG, DD>), dim3(grid), dim3(kThreads), 0, s, f);
+    return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fused
+
+int fused_ctl_ints(const Dims& dm) { return fused::kChunkDone + fused::kLine * max_chunks(dm); }
+
+bool fused_supported(const Dims& dm) { return dm.P <= kFusedMaxPairs && dm.E <= 2 * stream::kThreads; }
+
+namespace fused {
+namespace {
+
+FusedArgs make_args(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
+                    int spin_limit) {
+    using namespace stream;
+    FusedArgs f{};
+    const int RT = tiles_per_wave(dm);
+    f.gu.act = reinterpret_cast<const uint8_t*>(x);
+    f.gu.w0 = w.w_gate; f.gu.s0 = w.w_gate_scale;
+    f.gu.w1 = w.w_up;   f.gu.s1 = w.w_up_scale;
+    f.gu.h_out = ws.h;
+    f.gu.K = dm.d; f.gu.N = dm.f; f.gu.k_top = dm.k; f.gu.ldo = dm.f;
+    f.dn.act = ws.h;
+    f.dn.w0 = w.w_down; f.dn.s0 = w.w_down_scale;
+    f.dn.o_out = ws.o;
+    f.dn.K = dm.f; f.dn.N = dm.d; f.dn.k_top = dm.k; f.dn.ldo = dm.d;
+    f.ids = ws.topk_ids;
+    f.ctl = ws.fctl; f.counts = ws.fcounts; f.lists = ws.flists;
+    f.offsets = ws.offsets; f.sorted = ws.sorted_pairs; f.chunks = ws.chunks; f.nchunks = ws.nchunks;
+    f.E = dm.E; f.T = dm.T; f.P = dm.P;
+    f.ntg = RT == 2 ? col_tiles<kGateUp, 2>(dm.f) : col_tiles<kGateUp, 4>(dm.f);
+    f.ntd = RT == 2 ? col_tiles<kDown, 2>(dm.d) : col_tiles<kDown, 4>(dm.d);
+    f.gu.n_tiles = f.ntg;
+    f.dn.n_tiles = f.ntd;
+    f.spin_limit = spin_limit;
+    return f;
+}
+
+}  // namespace
+}  // namespace fused
+
+hipError_t launch_fused_lists(const Dims& dm, const Workspace& ws, hipStream_t s) {
+    const moe_mxfp4_weights none{};
+    const fused::FusedArgs f = fused::make_args(nullptr, none, dm, ws, 0);
+    hipLaunchKernelGGL(fused::k_expert_lists, dim3(dm.E), dim3(stream::kThreads), 0, s, f);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
+                        int spin_limit, hipStream_t s) {
+    using namespace stream;
+    const fused::FusedArgs f = fused::make_args(x, w, dm, ws, spin_limit);
+    const int RT = tiles_per_wave(dm);
+    const int items = max_chunks(dm) * (f.ntg + f.ntd);
+    const bool g4 = (dm.d / kKStep) % 4 == 0, d4 = (dm.f / kKStep) % 4 == 0;
+    if (RT == 2) {
+        if (g4 && d4) return fused::launch_variant<2, 4, 4>(f, items, s);
+        if (g4) return fused::launch_variant<2, 4, 2>(f, items, s);
+        if (d4) return fused::launch_variant<2, 2, 4>(f, items, s);
+        return fused::launch_variant<2, 2, 2>(f, items, s);
+    }
+    if (g4 && d4) return fused::launch_variant<4, 4, 4>(f, items, s);
+    if (g4) return fused::launch_variant<4, 4, 2>(f, items, s);
+    if (d4) return fused::launch_variant<4, 2, 4>(f, items, s);
+    return fused::launch_variant<4, 2, 2>(f, items, s);
+}
+
+}  // namespace moe

@@ -105,11 +105,19 @@ __device__ __forceinline__ void route_token_rank(const float* __restrict__ logit
 }
 
 // One wavefront per token, E <= 64 * NV.
+// Clear zero[0 .. nzero) with every thread of the grid (the persistent
+// kernel's work counters, which must start at zero in every call).
+__device__ __forceinline__ void clear_counters(int32_t* __restrict__ zero, int nzero) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nzero; i += gridDim.x * blockDim.x) zero[i] = 0;
+}
+
 template <int NV>
 __global__ __launch_bounds__(kRouteWaves * kWave) void k_route_rank(const float* __restrict__ logits,
                                                                     Dims dm, int32_t* __restrict__ ids,
-                                                                    float* __restrict__ wts) {
+                                                                    float* __restrict__ wts,
+                                                                    int32_t* __restrict__ zero, int nzero) {
     __shared__ RankScratch<NV> sc[kRouteWaves];
+    clear_counters(zero, nzero);
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int t = blockIdx.x * kRouteWaves + wave;
     if (t >= dm.T) return;                       // whole wave exits; waves share no LDS
@@ -170,7 +178,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int NV>
 __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __restrict__ logits,
                                                                Dims dm, int32_t* __restrict__ ids,
-                                                               float* __restrict__ wts) {
+                                                               float* __restrict__ wts,
+                                                               int32_t* __restrict__ zero, int nzero) {
+    clear_counters(zero, nzero);
     const int lane = threadIdx.x % kWave;
     const int t = blockIdx.x * kRouteWaves + threadIdx.x / kWave;
     if (t >= dm.T) return;                       // whole wave exits together
@@ -647,23 +657,24 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_sort_scatter(Dims dm, co
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s) {
+hipError_t launch_route(const float* logits, const Dims& dm, const Workspace& ws, hipStream_t s, int32_t* zero,
+                        int nzero) {
     const int grid = (dm.T + kRouteWaves - 1) / kRouteWaves;
     // ranking costs E compares per logit (each a 4-cycle wave64 VALU op):
     // it wins for one logit per lane; with two (E <= 128) it already takes
     // 1.3-1.4x as long as the k argmax rounds
     if (dm.E <= kWave)
         hipLaunchKernelGGL(k_route_rank<1>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
-                           ws.topk_ids, ws.topk_w);
+                           ws.topk_ids, ws.topk_w, zero, nzero);
     else if (dm.E <= 2 * kWave)
         hipLaunchKernelGGL(k_route<2>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
-                           ws.topk_ids, ws.topk_w);
+                           ws.topk_ids, ws.topk_w, zero, nzero);
     else if (dm.E <= 4 * kWave)
         hipLaunchKernelGGL(k_route<4>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
-                           ws.topk_ids, ws.topk_w);
+                           ws.topk_ids, ws.topk_w, zero, nzero);
     else
         hipLaunchKernelGGL(k_route<8>, dim3(grid), dim3(kRouteWaves * kWave), 0, s, logits, dm,
-                           ws.topk_ids, ws.topk_w);
+                           ws.topk_ids, ws.topk_w, zero, nzero);
     return hipGetLastError();
 }
 

@@ -159,6 +159,38 @@ def test_noalloc_forward_validates_before_touching_the_device():
         L.moe_mxfp4_destroy(h)
 
 
+def test_path_selection_and_device_status_validation(monkeypatch):
+    L = moe.lib()
+    for path, ok in (("stream", True), ("fused", True), ("", True), ("bogus", False)):
+        monkeypatch.setenv("MOE_MXFP4_PATH", path)
+        st, h = _create()
+        assert (st == 0) == ok, (path, st)
+        if st == 0:
+            L.moe_mxfp4_destroy(h)
+    monkeypatch.delenv("MOE_MXFP4_PATH")
+    ds = L.moe_mxfp4_device_status
+    st, h = _create()
+    out = ctypes.c_int32(7)
+    try:
+        assert ds(None, FAKE, 8, ctypes.byref(out), None) == 1
+        assert ds(h, FAKE, 8, None, None) == 1
+        assert ds(h, FAKE, -1, ctypes.byref(out), None) == 1
+        assert ds(h, FAKE, 9, ctypes.byref(out), None) == 3
+        # the per-phase path has no device-side waits: 0 without touching the device
+        assert ds(h, FAKE, 8, ctypes.byref(out), None) == 0 and out.value == 0
+    finally:
+        L.moe_mxfp4_destroy(h)
+    monkeypatch.setenv("MOE_MXFP4_PATH", "fused")
+    st, h = _create()
+    monkeypatch.delenv("MOE_MXFP4_PATH")
+    try:
+        out.value = 7
+        assert ds(h, None, 0, ctypes.byref(out), None) == 0 and out.value == 0     # no tokens
+        assert ds(h, None, 8, ctypes.byref(out), None) == 1                        # no workspace
+    finally:
+        L.moe_mxfp4_destroy(h)
+
+
 def test_router_entry_points_validate_before_any_launch():
     st, h = _create()
     L = moe.lib()
