@@ -395,6 +395,21 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert,
                                    float* out, void* hip_stream);
 
 /*
+ * Copy the intermediate activations h of the last forward call that ran
+ * with `num_tokens` tokens on `workspace` (device, as passed to that call),
+ * for checking its rounding decisions.  Rows are in expert-sorted order: row
+ * r belongs to pair sorted_pairs[r] of that call's routing outputs.
+ * MOE_ACT_MXFP8_E4M3: h (device) uint8 [P][d_ff] E4M3 codes and h_scales
+ * (device) uint8 [P][d_ff/32] E8M0 bytes (the MX blocks run along d_ff);
+ * MOE_ACT_BF16: h bf16 [P][d_ff] (uint16 bit patterns), h_scales unused
+ * (may be NULL).  P = num_tokens * top_k.  Queued on hip_stream after that
+ * call.  Errors: INVALID_ARG (null pointer, num_tokens <= 0), CAPACITY,
+ * ALIGNMENT, HIP.
+ */
+moe_status moe_mxfp4_debug_hidden(const moe_mxfp4_ctx* ctx, const void* workspace, int32_t num_tokens,
+                                  void* h, uint8_t* h_scales, void* hip_stream);
+
+/*
  * Per-stage timing of forward calls with HIP events, for measurement.  The
  * pages stress that at these speeds each operator lasts microseconds and the
  * gaps between operators matter (techllm.github.io "Xiaomi MiMo x TileRT",

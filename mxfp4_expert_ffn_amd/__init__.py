@@ -32,7 +32,7 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create
            "moe_mxfp4_stage_times", "moe_mxfp4_tiled_scale_bytes", "moe_mxfp4_tile_weights",
            "moe_mxfp4_quantize_act_mxfp8", "moe_mxfp4_router_logits", "moe_mxfp4_forward_hidden",
            "moe_mxfp4_dflash_workspace_bytes", "moe_mxfp4_dflash_accept", "moe_mxfp4_probe",
-           "moe_mxfp4_forward_noalloc", "moe_mxfp4_device_status")
+           "moe_mxfp4_forward_noalloc", "moe_mxfp4_device_status", "moe_mxfp4_debug_hidden")
 # Scratch bytes moe_mxfp4_forward_noalloc holds per GPU (MOE_MXFP4_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
 NUM_STAGES = 6
@@ -89,6 +89,8 @@ def lib():
         L.moe_mxfp4_forward.restype = ctypes.c_int
         L.moe_mxfp4_forward_noalloc.argtypes = [P, P, P, i32, P, P, ctypes.POINTER(Routing)]
         L.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
+        L.moe_mxfp4_debug_hidden.argtypes = [P, P, i32, P, P, P]
+        L.moe_mxfp4_debug_hidden.restype = ctypes.c_int
         L.moe_mxfp4_device_status.argtypes = [P, P, i32, ctypes.POINTER(i32), P]
         L.moe_mxfp4_device_status.restype = ctypes.c_int
         L.moe_mxfp4_forward_hidden.argtypes = [P, P, P, i32, P, P, sz, P, ctypes.POINTER(Routing)]
@@ -294,6 +296,23 @@ class MoeMxfp4:
         _check(lib().moe_mxfp4_device_status(self._ctx, _ptr(ws), num_tokens, ctypes.byref(st), _stream(stream)),
                "moe_mxfp4_device_status")
         return st.value
+
+    def debug_hidden(self, num_tokens: int, workspace=None, stream=None):
+        """h of the last call with ``num_tokens`` tokens on ``workspace``
+        (default: the cached one), rows in expert-sorted order: MXFP8 mode
+        (uint8 codes [P, d_ff], uint8 E8M0 scales [P, d_ff/32]); bf16 mode
+        (bf16 [P, d_ff], None)."""
+        import torch
+        ws = self.workspace(num_tokens, stream) if workspace is None else workspace
+        P, f = num_tokens * self.cfg.top_k, self.cfg.d_ff
+        if self.cfg.act_mode == ACT_MXFP8_E4M3:
+            h = torch.empty((P, f), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((P, f // 32), dtype=torch.uint8, device="cuda")
+        else:
+            h, sc = torch.empty((P, f), dtype=torch.bfloat16, device="cuda"), None
+        _check(lib().moe_mxfp4_debug_hidden(self._ctx, _ptr(ws), num_tokens, _ptr(h), _ptr(sc), _stream(stream)),
+               "moe_mxfp4_debug_hidden")
+        return h, sc
 
     def router_logits(self, hidden, w_router, out=None, stream=None):
         """hidden: bf16 [T, d]; w_router: bf16 [E, d] -> float32 logits [T, E]."""

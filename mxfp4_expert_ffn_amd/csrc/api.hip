@@ -551,6 +551,26 @@ moe_status moe_mxfp4_debug_dequant(const moe_mxfp4_ctx* ctx, int32_t expert, int
     return MOE_OK;
 }
 
+moe_status moe_mxfp4_debug_hidden(const moe_mxfp4_ctx* ctx, const void* workspace, int32_t num_tokens, void* h,
+                                  uint8_t* h_scales, void* hip_stream) {
+    if (!ctx || !workspace || !h || num_tokens <= 0) return MOE_ERR_INVALID_ARG;
+    const moe_mxfp4_config& c = ctx->cfg;
+    if (num_tokens > c.max_tokens) return MOE_ERR_CAPACITY;
+    const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
+    if (mx8 && !h_scales) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(workspace) || !aligned16(h) || (mx8 && !aligned16(h_scales))) return MOE_ERR_ALIGNMENT;
+    const Layout L = make_layout(c, num_tokens);
+    const size_t P = (size_t)num_tokens * c.top_k;
+    const char* base = static_cast<const char*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (hipMemcpyAsync(h, base + L.h, P * c.d_ff * (mx8 ? 1 : 2), hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (mx8 && hipMemcpyAsync(h_scales, base + L.hs, P * (c.d_ff / MOE_MXFP4_BLOCK), hipMemcpyDeviceToDevice, s) !=
+                   hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 moe_status moe_mxfp4_quantize_weights(const float* w, int64_t rows, int64_t K, uint8_t* packed,
                                       uint8_t* scales, void* hip_stream) {
     if (!w || !packed || !scales || rows < 0 || K <= 0 || K % MOE_MXFP4_BLOCK != 0)

@@ -162,6 +162,31 @@ def test_fused_replays_from_a_hip_graph(monkeypatch):
         assert torch.equal(y_graph, y_eager), i
 
 
+def test_fused_alternating_inputs_on_one_workspace(monkeypatch):
+    # consecutive calls with different inputs (and routing) on the same
+    # workspace: every value a call reads must come from that call, so a
+    # stale h row, list or count from the previous call would show here
+    moe = _moe()
+    w = synth.workload("verify_32seq")
+    acts, wts = problems.problem(w)
+    stream_l, fused_l = _layers(monkeypatch, problems.to_device(wts), w, w.T, 0)
+    ws = torch.empty(fused_l.workspace_bytes(w.T), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(11)
+    inputs = []
+    for _ in range(3):
+        xi = synth.bf16_bits_from_f32(rng.standard_normal((w.T, w.d)).astype(np.float32))
+        x = torch.from_numpy(xi.view(np.int16)).cuda().view(torch.bfloat16)
+        lg = torch.from_numpy(rng.standard_normal((w.T, w.E)).astype(np.float32) * 2).cuda()
+        inputs.append((x, lg, stream_l(x, lg).clone()))
+    torch.cuda.synchronize()
+    for i in range(9):
+        x, lg, y_ref = inputs[i % 3]
+        y = fused_l(x, lg, workspace=ws)
+        torch.cuda.synchronize()
+        assert fused_l.device_status(w.T, workspace=ws) == 0
+        assert torch.equal(y, y_ref), i
+
+
 def test_fused_repeated_calls_are_bit_identical(monkeypatch):
     w = synth.workload("verify_32seq")
     acts, wts = problems.problem(w)

@@ -2,16 +2,21 @@
 
 The activation quantiser must match the oracle's MXFP8 quantiser bit for bit
 (every rounding decision is taken on a bf16 value scaled by a power of two).
-h is re-quantised on both sides from differently rounded float values, so a
-few of its E4M3 codes may differ by one step; the layer output is checked
-against the tolerance max|y - y_ref| <= 2e-2 * RMS(y_ref).
+h is re-quantised on both sides from differently rounded values (float32
+sums on the GPU, float64 in the oracle), so where the exact h sits within
+float32 error of an E4M3 rounding boundary either code is correct; the
+checks (tests/mx8_check.py) are that every h code and scale the GPU chose is
+a correct rounding of an admissible value, and that the layer output equals
+the oracle's down projection and combine of the GPU's own h within
+max|y - y_ref| <= 2e-2 * RMS(y_ref).  The error against the oracle's own h is
+printed beside it.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests import problems
+from tests import mx8_check, pins, problems
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -59,8 +64,27 @@ def _run(w, acts, dev, out_dtype, T=None):
          "expert_offsets": torch.empty(w.E + 1, dtype=torch.int32, device="cuda"),
          "sorted_pairs": torch.empty(P, dtype=torch.int32, device="cuda")}
     y = layer(_bf16(acts["x_bf16"][:T]), torch.from_numpy(acts["logits"][:T]).cuda(), routing=r)
+    codes, scales = layer.debug_hidden(T)
     torch.cuda.synchronize()
-    return y.float().cpu().numpy(), {k: v.cpu().numpy() for k, v in r.items()}
+    out = {k: v.cpu().numpy() for k, v in r.items()}
+    out["h_codes"], out["h_scales"] = codes.cpu().numpy(), scales.cpu().numpy()
+    return y.float().cpu().numpy(), out
+
+
+def _check(w, acts, wts, y, r, tokens, ref):
+    """(error against the down + combine of the GPU's own h, error against
+    the oracle, h elements within float32 error of a rounding boundary, h
+    codes that differ from the exact h's), after checking every GPU h code."""
+    ids, wt = oracle.route(acts["logits"][: len(r["topk_ids"]) // w.k], w.k)
+    c, s = mx8_check.gpu_h_by_pair(r["h_codes"], r["h_scales"], r["sorted_pairs"], w.k, tokens)
+    h, dh = mx8_check.exact_h(acts, wts, ids, tokens)
+    amb, differ = mx8_check.check_h(h.reshape(-1, w.f), dh.reshape(-1, w.f), c.reshape(-1, w.f),
+                                    s.reshape(-1, w.f // 32))
+    hdec = pins.dequant_mxfp8_np(c.reshape(-1, w.f), s.reshape(-1, w.f // 32)).reshape(h.shape)
+    y_own = mx8_check.down_combine(hdec, ids, wt, wts, tokens)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return (float(np.abs(y[tokens] - y_own).max()) / rms, float(np.abs(y[tokens] - ref).max()) / rms,
+            amb, differ)
 
 
 @pytest.mark.parametrize("T,E,k", [
@@ -69,18 +93,28 @@ def _run(w, acts, dev, out_dtype, T=None):
     (64, 1, 1),               # one expert, exactly half a chunk
 ])
 def test_mxfp8_small_forward(T, E, k):
+    """Eight seeds per shape; every one within the tolerance.  The error comes
+    from single-step disagreements of h's E4M3 codes, whose rate is printed."""
     moe = _moe()
-    w = synth.Workload("mx8", T, 256, 512, E, k, "mxfp8", "none", 90 + T)
-    acts = synth.make_activations(w)
-    wts = problems.pack_experts(w)
-    dev = problems.to_device(wts)
-    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k, act_mode=oracle.ACT_MXFP8)
-    y32, r = _run(w, acts, dev, moe.OUT_F32)
-    ids, _ = oracle.route(acts["logits"], k)
-    assert np.array_equal(r["topk_ids"], ids.reshape(-1))
-    err = problems.rel_max_err(y32, ref["y"])
-    print(f"mxfp8 T={T} E={E} k={k}: f32-out rel max err {err:.3e}")
-    assert err <= TOL
+    own, strict, amb, differ = [], [], 0, 0
+    for seed in range(8):
+        w = synth.Workload("mx8", T, 256, 512, E, k, "mxfp8", "none", 90 + T + 1000 * seed)
+        acts = synth.make_activations(w)
+        wts = problems.pack_experts(w)
+        dev = problems.to_device(wts)
+        ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k, act_mode=oracle.ACT_MXFP8)
+        y32, r = _run(w, acts, dev, moe.OUT_F32)
+        ids, _ = oracle.route(acts["logits"], k)
+        assert np.array_equal(r["topk_ids"], ids.reshape(-1))
+        e_own, e_ref, a, dfr = _check(w, acts, wts, y32, r, np.arange(T), ref["y"])
+        own.append(e_own)
+        strict.append(e_ref)
+        amb += a
+        differ += dfr
+    print(f"mxfp8 T={T} E={E} k={k}, 8 seeds: f32-out rel max err vs the GPU's own h: max {max(own):.3e}; "
+          f"vs the oracle: max {max(strict):.3e}, mean {np.mean(strict):.3e}; h codes within float32 error of "
+          f"a tie: {amb}, of which the GPU rounded the other way: {differ}")
+    assert max(own) <= TOL, own
 
 
 @pytest.mark.parametrize("d,f", [(8704, 512), (512, 8704), (256, 1024)])
@@ -90,10 +124,11 @@ def test_mxfp8_k_extents(d, f):
     acts = synth.make_activations(w)
     wts = problems.pack_experts(w)
     ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, w.k, act_mode=oracle.ACT_MXFP8)
-    y32, _ = _run(w, acts, problems.to_device(wts), moe.OUT_F32)
-    err = problems.rel_max_err(y32, ref["y"])
-    print(f"mxfp8 d={d} f={f}: f32-out rel max err {err:.3e}")
-    assert err <= TOL
+    y32, r = _run(w, acts, problems.to_device(wts), moe.OUT_F32)
+    e_own, e_ref, amb, differ = _check(w, acts, wts, y32, r, np.arange(w.T), ref["y"])
+    print(f"mxfp8 d={d} f={f}: f32-out rel max err vs own h {e_own:.3e}, vs the oracle {e_ref:.3e} "
+          f"({differ} of {amb} tie codes the other way)")
+    assert e_own <= TOL
 
 
 def test_chunk_8192_sampled_parity():
@@ -111,11 +146,12 @@ def test_chunk_8192_sampled_parity():
     sample = np.sort(rng.choice(w.T, size=12, replace=False))
     ref = oracle.moe_forward(acts["x_bf16"][sample], acts["logits"][sample], wts, w.k,
                              act_mode=oracle.ACT_MXFP8, nthreads=problems.THREADS)["y"]
-    err = problems.rel_max_err(y16[sample], ref)
+    e_own, e_ref, amb, differ = _check(w, acts, wts, y16, r, sample, ref)
     floor = problems.rel_max_err(torch.from_numpy(ref).bfloat16().double().numpy(), ref)
-    print(f"chunk_8192: bf16-out rel max err {err:.3e} over {len(sample)} tokens "
-          f"(bf16 rounding of the reference alone: {floor:.3e})")
-    assert err <= TOL
+    print(f"chunk_8192: bf16-out rel max err over {len(sample)} tokens vs own h {e_own:.3e}, vs the oracle "
+          f"{e_ref:.3e} (bf16 rounding of the reference alone: {floor:.3e}; {differ} of {amb} tie codes "
+          f"the other way)")
+    assert e_own <= TOL
 
 
 @pytest.mark.parametrize("shifts", [(40, 40, 40, 40), (-60, -60, -60, -60), (40, -40, 0, 0)])

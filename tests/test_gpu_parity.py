@@ -127,26 +127,64 @@ def test_tiny_workload_full_parity():
                           torch.from_numpy(got["y"]).bfloat16().float().numpy())
 
 
-@pytest.mark.parametrize("name,nsample", [("verify_1seq", 8), ("verify_32seq", 12),
-                                          ("share_64seq", 12)])
-def test_full_size_workload_sampled_parity(name, nsample):
+@pytest.mark.parametrize("name,nsample", [("verify_1seq", 8), ("verify_32seq", 256),
+                                          ("share_64seq", 64)])
+def test_full_size_workload_parity(name, nsample):
+    """The whole 8- and 256-token batches against the oracle; at 512 tokens a
+    64-token sample that holds tokens of every 64-pair chunk of the most
+    loaded expert (the multi-chunk path).  Routing of every token is exact."""
     w = synth.workload(name)
     acts, wts = problems.problem(w)
     dev = problems.to_device(wts)
     got, _ = _run(w, acts, dev, out_dtype=0)            # bf16 output, as benchmarked
     _check_routing(w, acts, got)
-    rng = np.random.default_rng(7)
-    sample = np.sort(rng.choice(w.T, size=min(nsample, w.T), replace=False))
-    # include the tokens of the most loaded expert (the multi-chunk path)
-    ids = got["topk_ids"].reshape(w.T, w.k)
-    hot = np.bincount(ids.ravel(), minlength=w.E).argmax()
-    hot_tokens = np.nonzero((ids == hot).any(axis=1))[0][-2:]
-    sample = np.unique(np.concatenate([sample, hot_tokens]))
+    if nsample >= w.T:
+        sample = np.arange(w.T)
+    else:
+        # 4 tokens from each chunk of the hottest expert's pairs (in sorted
+        # order), the rest drawn at random
+        ids = got["topk_ids"].reshape(w.T, w.k)
+        hot = int(np.bincount(ids.ravel(), minlength=w.E).argmax())
+        lo, hi = got["expert_offsets"][hot], got["expert_offsets"][hot + 1]
+        hot_pairs = got["sorted_pairs"][lo:hi]
+        picks = [hot_pairs[c:c + 64][:: max(1, len(hot_pairs[c:c + 64]) // 4)][:4] // w.k
+                 for c in range(0, len(hot_pairs), 64)]
+        sample = np.unique(np.concatenate(picks))
+        assert len(picks) >= 2                      # the hot expert has several chunks
+        rng = np.random.default_rng(7)
+        rest = rng.permutation(np.setdiff1d(np.arange(w.T), sample))
+        sample = np.sort(np.concatenate([sample, rest[:nsample - len(sample)]]))
     ref = oracle.moe_forward(acts["x_bf16"][sample], acts["logits"][sample], wts, w.k,
                              nthreads=problems.THREADS)["y"]
     err = problems.rel_max_err(got["y"][sample], ref)
-    print(f"{name}: bf16-out rel max err over {len(sample)} tokens {err:.3e}")
-    assert err <= TOL
+    # where the error comes from: the same call with float32 output, and the
+    # bf16 rounding of the reference alone (the output format's floor)
+    got32, _ = _run(w, acts, dev, routing=False)
+    err32 = problems.rel_max_err(got32["y"][sample], ref)
+    floor = problems.rel_max_err(torch.from_numpy(ref).bfloat16().double().numpy(), ref)
+    print(f"{name}: rel max err over {len(sample)} tokens: bf16 out {err:.3e}, float32 out {err32:.3e}; "
+          f"bf16 rounding of the reference alone {floor:.3e}")
+    assert err <= TOL and err32 <= TOL
+
+
+@pytest.mark.parametrize("name", ["tiny", "verify_1seq", "verify_32seq"])
+def test_gpu_quantiser_on_every_weight_of_the_workload(name):
+    """The library's weight quantiser gives the oracle's bytes on every
+    expert matrix of the workload."""
+    from concurrent.futures import ThreadPoolExecutor
+    moe = _moe()
+    w = synth.workload(name)
+
+    def host(e):
+        mats = synth.expert_weights_f32(w, e)
+        return e, mats, [oracle.quant_mxfp4(m) for m in mats]
+
+    with ThreadPoolExecutor(problems.THREADS) as ex:
+        for e, mats, ref in ex.map(host, range(w.E)):
+            for m, (p_ref, s_ref) in zip(mats, ref):
+                p, sc = moe.quantize_weights(torch.from_numpy(m).cuda())
+                assert np.array_equal(p.cpu().numpy(), p_ref), e
+                assert np.array_equal(sc.cpu().numpy(), s_ref), e
 
 
 # -------------------------------------------------------------- edges ---

@@ -53,10 +53,13 @@ MUTANTS = {
 }
 
 # the pin tests to run against each mutant (all of them, minus the ones
-# that only re-check thread counts or argument validation)
+# that only re-check thread counts or argument validation, and the sweep of
+# the quantiser over whole workloads, which repeats the quantiser comparison
+# on more data for half a minute)
 PIN_TESTS = [(n, f) for n, f in inspect.getmembers(pins_mod, inspect.isfunction)
              if n.startswith("test_") and n not in ("test_forward_rejects_bad_shapes",
-                                                     "test_forward_threads_do_not_change_result")]
+                                                     "test_forward_threads_do_not_change_result",
+                                                     "test_quantizers_agree_on_every_weight_of_the_workload")]
 
 
 def _run_all_pins():

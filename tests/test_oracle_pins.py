@@ -162,6 +162,26 @@ def test_mxfp4_quantizer_matches_second_quantizer():
         assert np.array_equal(p1, p2)
 
 
+@pytest.mark.parametrize("name", ["tiny", "verify_1seq", "verify_32seq"])
+def test_quantizers_agree_on_every_weight_of_the_workload(name):
+    """The oracle's quantiser and the independent NumPy one give the same
+    bytes on every expert matrix of the workload (all 3 x E matrices)."""
+    from concurrent.futures import ThreadPoolExecutor
+    w = synth.workload(name)
+
+    def one(e):
+        for m in synth.expert_weights_f32(w, e):
+            p1, s1 = oracle.quant_mxfp4(m)
+            p2, s2 = pins.quant_mxfp4_np(m)
+            if not (np.array_equal(p1, p2) and np.array_equal(s1, s2)):
+                return e
+        return None
+
+    with ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+        bad = [e for e in ex.map(one, range(w.E)) if e is not None]
+    assert bad == []
+
+
 def test_mxfp4_dequant_matches_bitfield_decoder():
     rng = np.random.default_rng(8)
     packed = rng.integers(0, 256, (16, 64), dtype=np.uint8)
