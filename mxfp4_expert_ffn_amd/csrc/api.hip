@@ -47,8 +47,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t logits, ids, w, offsets, sorted, active, chunks, nchunks, sort_part, xq, xs, h, hs, o, fctl, fcounts,
-        flists, total;
+    size_t logits, ids, w, offsets, sorted, active, chunks, nchunks, xtab, sort_part, xq, xs, h, hs, o, fctl,
+        fcounts, flists, total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
@@ -64,6 +64,8 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     moe::Dims dm{(int32_t)T, c.d_model, c.d_ff, c.num_experts, c.top_k, (int32_t)P};
     L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * moe::kChunkRec * sizeof(int32_t));
     L.nchunks = at; at += 256;
+    L.xtab = at;    at += round256(((size_t)moe::kXtabHead + (size_t)moe::kXcds * moe::xcd_slots(dm) * moe::kChunkRec) *
+                                   sizeof(int32_t));
     L.sort_part = at; at += round256((size_t)moe::sort_tiles((int)P) * c.num_experts * sizeof(int32_t));
     const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;
     L.xq = at;      at += mx8 ? round256((size_t)T * c.d_model) : 0;
@@ -367,6 +369,7 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     ws.active = reinterpret_cast<int32_t*>(base + L.active);
     ws.chunks = reinterpret_cast<int32_t*>(base + L.chunks);
     ws.nchunks = reinterpret_cast<int32_t*>(base + L.nchunks);
+    ws.xtab = reinterpret_cast<int32_t*>(base + L.xtab);
     ws.sort_part = reinterpret_cast<int32_t*>(base + L.sort_part);
     ws.xq = reinterpret_cast<uint8_t*>(base + L.xq);
     ws.xs = reinterpret_cast<uint8_t*>(base + L.xs);

@@ -94,6 +94,8 @@ struct Workspace {
     int32_t* chunks;          // [max_chunks][4] (expert, position of the chunk's first pair in
                               //   sorted_pairs, pairs in the chunk, 0)
     int32_t* nchunks;         // [1] number of chunks
+    int32_t* xtab;            // per-XCD chunk table: [kXtabHead] chunks per XCD (kXcds used),
+                              //   then [kXcds][xcd_slots(dm)] chunk records
     int32_t* sort_part;       // [sort_tiles(P)][E] per-tile expert histograms / first positions
     uint8_t* xq;              // MXFP8 mode: [T][d] E4M3 codes of x
     uint8_t* xs;              // MXFP8 mode: [T][d/32] E8M0 scales of x
@@ -123,6 +125,24 @@ inline int sort_tiles(int P) { return P <= kSortSingleMax ? 0 : (P + 2047) / 204
 inline int max_chunks(const Dims& dm) {
     const int active = dm.E < dm.P ? dm.E : dm.P;
     return active + dm.P / kChunk;
+}
+
+// Per-XCD chunk table.  The GPU hands workgroups to its kXcds XCDs
+// round-robin by workgroup index, and each XCD has its own L2.  The sort
+// assigns every active expert to one XCD, in snake order over groups of
+// kXcds consecutive ranks (ranks 0..7 to XCDs 0..7, ranks 8..15 to XCDs
+// 7..0, ...), and lists each XCD's chunks expert by expert; the streaming
+// kernels run XCD x's chunks on workgroups x, x + kXcds, ..., so all the
+// units of an expert -- its weight tiles, and each chunk's activation rows
+// -- go through one L2.  Only the speed depends on that dispatch order.
+// Since chunk counts do not increase with rank, an XCD holds at most
+// nchunks / kXcds plus one expert's chunks (at most ceil(T / kChunk),
+// every token picking distinct experts), which bounds the table's slots.
+constexpr int kXcds = 8;
+constexpr int kXtabHead = 64;      // ints before the records
+inline int xcd_slots(const Dims& dm) {
+    const int T = dm.T < dm.P ? dm.T : dm.P;
+    return (max_chunks(dm) + kXcds - 1) / kXcds + (T + kChunk - 1) / kChunk;
 }
 
 // The fused path (bf16 activations): after the routing launch (which clears

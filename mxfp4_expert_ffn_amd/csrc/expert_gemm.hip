@@ -11,21 +11,34 @@ namespace {
 template <int MODE, int RT, int D>
 __global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[D * kSlot];
-    // Work unit = (chunk, column tile), chunk-major: the column tiles of a
-    // chunk (same activation rows) are adjacent.  Chunks are listed expert
-    // by expert, hottest expert first.  Workgroup-uniform values are kept in
-    // scalar registers so that the buffer descriptors built from them are
-    // scalar too.
-    const int unit = blockIdx.x;
-    const int chunk = unit / a.n_tiles;
-    const int nt = unit % a.n_tiles;
-    // the record (inside the chunk list for every unit of the grid) is read
-    // together with the count, so the weight loads wait on one round trip
-    const int* rec = a.chunks + kChunkRec * chunk;
+    // Work unit = (chunk, column tile).  With a per-XCD table (batches of
+    // more pairs than experts), workgroup g runs on XCD g mod kXcds (the
+    // GPU's round-robin) and takes the units of that XCD's chunk list in
+    // order; otherwise unit g of the global list.  Both are chunk-major: the
+    // column tiles of a chunk (same activation rows) are adjacent, and so are
+    // the chunks of an expert, hottest expert first.  The record and the
+    // chunk count are read together, so the weight loads wait on one round
+    // trip; workgroup-uniform values are kept in scalar registers so that the
+    // buffer descriptors built from them are scalar too.
+    const int* rec;
+    const int* count;
+    int slot, nt;
+    if (a.xtab) {
+        const int x = blockIdx.x % kXcds;
+        slot = blockIdx.x / kXcds / a.n_tiles;
+        nt = blockIdx.x / kXcds % a.n_tiles;
+        rec = a.xtab + kXtabHead + kChunkRec * (x * a.xstride + slot);
+        count = a.xtab + x;
+    } else {
+        slot = blockIdx.x / a.n_tiles;
+        nt = blockIdx.x % a.n_tiles;
+        rec = a.chunks + kChunkRec * slot;
+        count = a.nchunks;
+    }
     const int e = __builtin_amdgcn_readfirstlane(rec[0]);
     const int start = __builtin_amdgcn_readfirstlane(rec[1]);
     const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
-    if (chunk >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;     // uniform per workgroup
+    if (slot >= __builtin_amdgcn_readfirstlane(*count)) return;     // uniform per workgroup
     // the chunk's pairs sit at sorted positions start .. start + rows - 1
     run_unit<MODE, RT, D>(a, lds, e, nt, a.sorted + start, start, rows, [] {});
 }
@@ -34,7 +47,12 @@ template <int MODE, int RT>
 hipError_t launch_rt(GemmArgs a, const Dims& dm, hipStream_t s) {
     a.n_tiles = a.N / (kWaves * (MODE == kGateUp ? RT / 2 : RT) * 16);
     const int nsteps = a.K / kKStep;          // 2 (K = 256) or a multiple of 4
-    const dim3 grid(max_chunks(dm) * a.n_tiles), block(kThreads);
+    // the per-XCD table pays where experts have several chunks or a chunk
+    // several rows; at most one pair per expert on average it would only
+    // add workgroups (its bound is looser than the global list's)
+    a.xstride = xcd_slots(dm);
+    if (dm.P <= dm.E) a.xtab = nullptr;
+    const dim3 grid(a.xtab ? kXcds * a.xstride * a.n_tiles : max_chunks(dm) * a.n_tiles), block(kThreads);
     if (nsteps % 4 == 0)
         hipLaunchKernelGGL((k_expert<MODE, RT, 4>), grid, block, 0, s, a);
     else
@@ -60,7 +78,7 @@ hipError_t launch_gateup(const uint16_t* x, const moe_mxfp4_weights& w, const Di
     a.act = reinterpret_cast<const uint8_t*>(x);
     a.w0 = w.w_gate; a.s0 = w.w_gate_scale;
     a.w1 = w.w_up;   a.s1 = w.w_up_scale;
-    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks; a.xtab = ws.xtab;
     a.h_out = ws.h; a.o_out = nullptr;
     a.K = dm.d; a.N = dm.f;
     a.k_top = dm.k; a.ldo = dm.f;
@@ -72,7 +90,7 @@ hipError_t launch_down(const moe_mxfp4_weights& w, const Dims& dm, const Workspa
     a.act = ws.h;
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
-    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks; a.xtab = ws.xtab;
     a.h_out = nullptr; a.o_out = ws.o;
     a.K = dm.f; a.N = dm.d;
     a.k_top = dm.k; a.ldo = dm.d;

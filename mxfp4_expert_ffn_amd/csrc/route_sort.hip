@@ -286,7 +286,8 @@ __device__ __forceinline__ int id_bits(int E) {
 __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act, int32_t* rnk, int32_t* exoff,
                             int32_t* wsum, int E, int P, int chunk_rows,
                             int32_t* __restrict__ offsets, int32_t* __restrict__ active,
-                            int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks) {
+                            int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks,
+                            int32_t* __restrict__ xtab, int xstride) {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     int32_t* wsum2 = wsum + kSortWaves;
     // exclusive scan of counts over experts (E <= 512 <= 1024 threads), and
@@ -358,9 +359,29 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
             rec[2] = min(chunk_rows, n - q * chunk_rows);
             rec[3] = 0;
         }
+        rnk[tid] = first;                              // ranks are no longer needed: first chunk of rank tid
     }
     if (tid == kSortThreads - 1) *nchunks = cbefore + nincl;
     __syncthreads();
+    // per-XCD chunk table: wave x (< kXcds) takes XCD x, lane j the rank that
+    // group j of kXcds ranks gives it in snake order; a scan of their chunk
+    // counts places each expert's chunks in the XCD's list
+    if (tid < kXcds * kWave) {
+        const int x = wave, j = lane;
+        const int r = kXcds * j + ((j & 1) ? kXcds - 1 - x : x);
+        const int e = r < na ? act[r] : 0;
+        const int n = r < na ? counts[e] : 0;
+        const int m = (n + chunk_rows - 1) / chunk_rows;
+        const int incl = wave_inclusive_scan(m, lane);
+        if (lane == kWave - 1) xtab[x] = incl;
+        int32_t* rec = xtab + kXtabHead + kChunkRec * ((size_t)x * xstride + (incl - m));
+        for (int q = 0; q < m; ++q) {
+            rec[kChunkRec * q + 0] = e;
+            rec[kChunkRec * q + 1] = exoff[e] + q * chunk_rows;
+            rec[kChunkRec * q + 2] = min(chunk_rows, n - q * chunk_rows);
+            rec[kChunkRec * q + 3] = rnk[r] + q;      // the chunk's index in the global list
+        }
+    }
     return tid < E ? excl : 0;
 }
 
@@ -378,7 +399,8 @@ __host__ __device__ inline size_t sort_lds_bytes(int E) {
 __device__ __forceinline__ void sort_single(const Dims& dm, const int32_t* __restrict__ ids, uint64_t* sm64,
                             int32_t* __restrict__ offsets, int32_t* __restrict__ sorted,
                             int32_t* __restrict__ active, int32_t* __restrict__ chunks,
-                            int32_t* __restrict__ nchunks, int chunk_rows) {
+                            int32_t* __restrict__ nchunks, int chunk_rows, int32_t* __restrict__ xtab,
+                            int xstride) {
     const int E = dm.E, P = dm.P;
     const int E4 = (E + 3) & ~3;
     uint64_t* keys = sm64;                            // [E]
@@ -424,7 +446,8 @@ __device__ __forceinline__ void sort_single(const Dims& dm, const int32_t* __res
     }
     if (tid >= E && tid < E4) counts[tid] = 0;
     __syncthreads();
-    expert_lists(counts, keys, act, rnk, exoff, wsum, E, P, chunk_rows, offsets, active, chunks, nchunks);
+    expert_lists(counts, keys, act, rnk, exoff, wsum, E, P, chunk_rows, offsets, active, chunks, nchunks, xtab,
+                 xstride);
 
     // 3) scatter in the same visiting order: stable within each expert
     //    (position = expert offset + pairs of earlier waves and rounds + rank)
@@ -442,9 +465,10 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
                                                        int32_t* __restrict__ sorted,
                                                        int32_t* __restrict__ active,
                                                        int32_t* __restrict__ chunks,
-                                                       int32_t* __restrict__ nchunks, int chunk_rows) {
+                                                       int32_t* __restrict__ nchunks, int chunk_rows,
+                                                       int32_t* __restrict__ xtab, int xstride) {
     extern __shared__ uint64_t sm64[];
-    sort_single(dm, ids, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows);
+    sort_single(dm, ids, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows, xtab, xstride);
 }
 
 // Small batches (T <= kFusedMaxTokens, E <= 64): routing and the permutation
@@ -460,7 +484,8 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __rest
                                                              int32_t* __restrict__ sorted,
                                                              int32_t* __restrict__ active,
                                                              int32_t* __restrict__ chunks,
-                                                             int32_t* __restrict__ nchunks, int chunk_rows) {
+                                                             int32_t* __restrict__ nchunks, int chunk_rows,
+                                                             int32_t* __restrict__ xtab, int xstride) {
     extern __shared__ uint64_t sm64[];
     uint8_t* extra = reinterpret_cast<uint8_t*>(sm64) + sort_lds_bytes(dm.E);
     int32_t* ids_lds = reinterpret_cast<int32_t*>(extra);
@@ -468,7 +493,7 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __rest
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     for (int t = wave; t < dm.T; t += kSortWaves) route_token_rank<1>(logits, dm, t, lane, sc[wave], ids, wts, ids_lds);
     __syncthreads();
-    sort_single(dm, ids_lds, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows);
+    sort_single(dm, ids_lds, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows, xtab, xstride);
 }
 
 // The permutation of at most 64 pairs over at most 64 experts by one
@@ -480,7 +505,8 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __rest
 __device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, int32_t* cnt, int32_t* exo,
                                           uint64_t* keys, int lane, int32_t* __restrict__ offsets,
                                           int32_t* __restrict__ sorted, int32_t* __restrict__ active,
-                                          int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks) {
+                                          int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks,
+                                          int32_t* __restrict__ xtab, int xstride) {
     const int E = dm.E, P = dm.P;
     const bool valid = lane < P;
     const int ep = valid ? ids[lane] : 0;
@@ -516,6 +542,19 @@ __device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, in
         rec[1] = excl;
         rec[2] = c;
         rec[3] = 0;
+        // per-XCD table (the layout of expert_lists): one chunk per expert,
+        // so rank r sits in slot r / kXcds of its XCD's list
+        const int j = r / kXcds, i = r % kXcds;
+        int32_t* xr = xtab + kXtabHead + kChunkRec * ((size_t)((j & 1) ? kXcds - 1 - i : i) * xstride + j);
+        xr[0] = lane;
+        xr[1] = excl;
+        xr[2] = c;
+        xr[3] = r;
+    }
+    if (lane < kXcds) {
+        int n = 0;
+        for (int j = 0; kXcds * j < na; ++j) n += kXcds * j + ((j & 1) ? kXcds - 1 - lane : lane) < na;
+        xtab[lane] = n;
     }
     if (lane == 0) {
         offsets[E] = P;
@@ -535,7 +574,8 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort_tiny(const float* _
                                                                   int32_t* __restrict__ sorted,
                                                                   int32_t* __restrict__ active,
                                                                   int32_t* __restrict__ chunks,
-                                                                  int32_t* __restrict__ nchunks) {
+                                                                  int32_t* __restrict__ nchunks,
+                                                                  int32_t* __restrict__ xtab, int xstride) {
     __shared__ RankScratch<1> sc[kSortWaves];
     __shared__ int32_t ids_lds[kWave];
     __shared__ int32_t cnt[kWave];
@@ -544,7 +584,8 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort_tiny(const float* _
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
     for (int t = wave; t < dm.T; t += nw) route_token_rank<1>(logits, dm, t, lane, sc[wave], ids, wts, ids_lds);
     __syncthreads();
-    if (wave == 0) sort_wave(dm, ids_lds, cnt, exo, keys, lane, offsets, sorted, active, chunks, nchunks);
+    if (wave == 0)
+        sort_wave(dm, ids_lds, cnt, exo, keys, lane, offsets, sorted, active, chunks, nchunks, xtab, xstride);
 }
 
 // Many pairs: tiles of kSortTile pairs, one 256-thread workgroup each (the
@@ -581,7 +622,8 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ active,
                                                             int32_t* __restrict__ chunks,
-                                                            int32_t* __restrict__ nchunks, int chunk_rows) {
+                                                            int32_t* __restrict__ nchunks, int chunk_rows,
+                                                            int32_t* __restrict__ xtab, int xstride) {
     extern __shared__ uint64_t sm64[];
     const int E = dm.E, E4 = (E + 3) & ~3, tid = threadIdx.x;
     uint64_t* keys = sm64;                            // [E]
@@ -616,7 +658,7 @@ __global__ __launch_bounds__(kSortThreads) void k_sort_scan(Dims dm, int ntiles,
     }
     __syncthreads();
     const int excl = expert_lists(counts, keys, act, rnk, exoff, wsum, E, dm.P, chunk_rows, offsets, active, chunks,
-                                  nchunks);
+                                  nchunks, xtab, xstride);
     if (tid < E)
         for (int b = 0; b < ntiles; ++b) part[(size_t)b * E + tid] += excl;
 }
@@ -687,13 +729,15 @@ hipError_t launch_route_sort(const float* logits, const Dims& dm, const Workspac
     if (dm.P <= kWave && dm.P <= chunk_rows) {        // dm.E <= 64 holds for every fused batch
         const int waves = dm.T < kSortWaves ? dm.T : kSortWaves;
         hipLaunchKernelGGL(k_route_sort_tiny, dim3(1), dim3(waves * kWave), 0, s, logits, dm, ws.topk_ids,
-                           ws.topk_w, ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks);
+                           ws.topk_w, ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks, ws.xtab,
+                           xcd_slots(dm));
         return hipGetLastError();
     }
     const size_t lds = sort_lds_bytes(dm.E) + (((size_t)dm.P * sizeof(int32_t) + 15) & ~(size_t)15) +
                        kSortWaves * sizeof(RankScratch<1>);
     hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(kSortThreads), lds, s, logits, dm, ws.topk_ids, ws.topk_w,
-                       ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks, chunk_rows);
+                       ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks, chunk_rows, ws.xtab,
+                       xcd_slots(dm));
     return hipGetLastError();
 }
 
@@ -702,7 +746,7 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
     if (dm.P <= kSortSingleMax) {
         hipLaunchKernelGGL(k_sort, dim3(1), dim3(kSortThreads), sort_lds_bytes(dm.E), s, dm, ws.topk_ids, ws.offsets,
                            ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks,
-                           chunk_rows);
+                           chunk_rows, ws.xtab, xcd_slots(dm));
         return hipGetLastError();
     }
     const int ntiles = sort_tiles(dm.P);
@@ -711,7 +755,8 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
                        ws.sort_part);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(k_sort_scan, dim3(1), dim3(kSortThreads), sizeof(uint64_t) * E + sizeof(int32_t) * (E4 + 3 * E + 2 * kSortWaves), s, dm,
-                       ntiles, ws.sort_part, ws.offsets, ws.active, ws.chunks, ws.nchunks, chunk_rows);
+                       ntiles, ws.sort_part, ws.offsets, ws.active, ws.chunks, ws.nchunks, chunk_rows, ws.xtab,
+                       xcd_slots(dm));
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(k_sort_scatter, dim3(ntiles), dim3(kTileWaves * kWave), tile_lds, s, dm, ws.topk_ids,
                        ws.sort_part, ws.sorted_pairs);

@@ -81,6 +81,8 @@ struct GemmArgs {
     const int32_t* sorted;      // [P]
     const int32_t* chunks;      // chunk records
     const int32_t* nchunks;     // device count of chunks
+    const int32_t* xtab;        // per-XCD chunk table (per-phase kernels)
+    int32_t xstride;            // its slots per XCD
     uint8_t* h_out;             // gate/up: h [P][f] bf16
     float* o_out;               // down: [P][d], row = pair index
     int32_t K;                  // reduction length

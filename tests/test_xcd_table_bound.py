@@ -1,0 +1,69 @@
+"""The per-XCD chunk table of the streaming kernels: the sort assigns active
+experts (ranked by descending pair count) to the 8 XCDs in snake order over
+groups of 8 ranks and lists each XCD's chunks expert by expert.  The host
+sizes the table and the grid with ceil(max_chunks / 8) + ceil(T / 64) slots
+per XCD, max_chunks = min(E, P) + P // 64; this checks that no XCD's list
+ever needs more, over random routings and the extreme ones (every expert
+equally loaded, one expert taking every token, k = E)."""
+import numpy as np
+import pytest
+
+XCDS, CHUNK = 8, 64
+
+
+def slots_needed(counts, chunk_rows):
+    m = np.sort([(c + chunk_rows - 1) // chunk_rows for c in counts if c > 0])[::-1]
+    L = np.zeros(XCDS, int)
+    for r, mr in enumerate(m):
+        j, i = divmod(r, XCDS)
+        L[XCDS - 1 - i if j & 1 else i] += mr
+    return L
+
+
+def bound(T, E, k):
+    P = T * k
+    max_chunks = min(E, P) + P // CHUNK
+    return -(-max_chunks // XCDS) + -(-min(T, P) // CHUNK)
+
+
+def routing_counts(rng, T, E, k, skew):
+    logits = rng.standard_normal((T, E)) + skew * np.log1p(np.arange(E))[::-1]
+    ids = np.argsort(-logits, axis=1)[:, :k]
+    return np.bincount(ids.ravel(), minlength=E)
+
+
+@pytest.mark.parametrize("chunk_rows", [64, 128])
+def test_random_routings_fit_the_slot_bound(chunk_rows):
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        E = int(rng.choice([1, 2, 4, 8, 16, 64, 128, 300, 512]))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        T = int(rng.choice([1, 7, 64, 65, 200, 512, 4096, 8192]))
+        counts = routing_counts(rng, T, E, k, float(rng.choice([0.0, 1.0, 4.0])))
+        assert counts.sum() == T * k
+        L = slots_needed(counts, chunk_rows)
+        assert L.max() <= bound(T, E, k), (T, E, k)
+        # the lists hold every chunk once
+        assert L.sum() == sum((c + chunk_rows - 1) // chunk_rows for c in counts)
+
+
+@pytest.mark.parametrize("T,E,k", [(8192, 8, 8), (8192, 16, 8), (4096, 32, 32), (513, 512, 32), (1, 512, 32),
+                                   (64, 64, 1), (8191, 9, 8)])
+def test_extreme_routings_fit_the_slot_bound(T, E, k):
+    # every expert equally loaded, and the hottest possible experts (all T
+    # tokens on the first k experts) next to a long tail of single pairs
+    even = np.full(E, T * k // E)
+    even[: T * k - even.sum()] += 1
+    hot = np.zeros(E, int)
+    hot[:k] = T
+    # k - 1 experts on every token, each token's last pick spread one pair
+    # per expert over the rest, the leftover on the first of them
+    tail = hot.copy()
+    if E > k:
+        tail[k - 1] = 0
+        n = min(T, E - k + 1)
+        tail[k - 1:k - 1 + n] += 1
+        tail[k - 1] += T - n
+    for counts in (even, hot, tail):
+        assert counts.sum() == T * k and counts.max() <= T
+        assert slots_needed(counts, CHUNK).max() <= bound(T, E, k), (T, E, k)
