@@ -225,11 +225,15 @@ def measured_traffic(workload, mx8, root=None):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    src = os.path.join(root, fields.get("kernel source", "?"))
-    if not os.path.exists(src) or "traffic bytes per launch" not in fields:
+    # the kernel's source files (comma-separated: the kernel file and the
+    # headers it is built from), hashed as one concatenation in that order
+    srcs = [os.path.join(root, f.strip().strip("`")) for f in fields.get("kernel source", "?").split(",")]
+    if not all(os.path.exists(f) for f in srcs) or "traffic bytes per launch" not in fields:
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("kernel source sha256") != digest:
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    if fields.get("kernel source sha256") != h.hexdigest():
         return None
     return float(fields["traffic bytes per launch"])
 

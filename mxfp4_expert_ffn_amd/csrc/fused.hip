@@ -199,8 +199,13 @@ __global__ __launch_bounds__(kThreads) void k_expert_lists(FusedArgs f) {
 template <int RT, int DG, int DD>
 __global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
     constexpr int kRing = DG > DD ? DG : DD;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kSlot];
-    __shared__ int32_t s_flag, s_next;
+    // One LDS object: the ring, then two handoff words.  (A second
+    // __shared__ object costs the compiler its proof that a step's operand
+    // reads do not alias the direct-to-LDS loads in flight, and it then
+    // drains every load before each step's reads.)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kSlot + 2 * sizeof(int32_t)];
+    int32_t& s_flag = *reinterpret_cast<int32_t*>(lds + kRing * kSlot);
+    int32_t& s_next = *reinterpret_cast<int32_t*>(lds + kRing * kSlot + sizeof(int32_t));
     const int nc = __builtin_amdgcn_readfirstlane(*f.nchunks);
     const int nG = nc * f.ntg, nD = nc * f.ntd;
     // Gate/up units u = b, b + G, ... (never waiting), then down units from

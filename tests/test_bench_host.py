@@ -48,5 +48,26 @@ def test_traffic_is_dropped_once_the_kernel_source_changes(tmp_path):
     assert bench.measured_traffic("share_64seq", False, root) is None           # no summary: null
 
 
+def test_traffic_is_dropped_once_a_header_of_the_kernel_changes(tmp_path):
+    # a kernel built from several sources: the summary hashes them in order,
+    # so editing any of them (here the shared pipeline header) drops the figure
+    (tmp_path / "profiles").mkdir()
+    csrc = tmp_path / "mxfp4_expert_ffn_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    files = {"expert_gemm.hip": "// kernel\n", "stream_pipe.hpp": "// pipeline\n", "common.hpp": "// common\n"}
+    for n, t in files.items():
+        (csrc / n).write_text(t)
+    digest = hashlib.sha256("".join(files.values()).encode()).hexdigest()
+    listed = ", ".join(f"`mxfp4_expert_ffn_amd/csrc/{n}`" for n in files)
+    prof = open(os.path.join(ROOT, "profiles", "beyond_l2_bytes_verify_32seq.md")).read()
+    prof = re.sub(r"kernel source sha256: `[0-9a-f]+`", f"kernel source sha256: `{digest}`", prof)
+    prof = re.sub(r"kernel source: .*", f"kernel source: {listed}", prof)
+    (tmp_path / "profiles" / "beyond_l2_bytes_verify_32seq.md").write_text(prof)
+    root = str(tmp_path)
+    assert bench.measured_traffic("verify_32seq", False, root) is not None
+    (csrc / "stream_pipe.hpp").write_text("// pipeline, edited\n")
+    assert bench.measured_traffic("verify_32seq", False, root) is None
+
+
 def test_cpu_model_is_a_string():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
