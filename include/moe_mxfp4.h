@@ -260,10 +260,11 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
  * created, selects how a forward call runs the steps after routing:
  *   "stream" (default)  one launch per phase: permutation, gate/up + SwiGLU,
  *                       down, combine;
- *   "fused"             one persistent kernel for the permutation, gate/up
- *                       and down (then the combine), whose work items hand
- *                       over through counters in the workspace, so down work
- *                       starts while gate/up still streams weights.  The
+ *   "fused"             the permutation as per-expert pair lists (one
+ *                       launch), then one persistent kernel for gate/up and
+ *                       down, whose work items hand over through counters in
+ *                       the workspace, so down work starts while gate/up
+ *                       still streams weights, then the combine.  The
  *                       pages' runtime keeps one engine kernel resident so
  *                       that microsecond operators pay no gap between them
  *                       (techllm.github.io "Xiaomi MiMo x TileRT", section
