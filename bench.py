@@ -208,20 +208,36 @@ def cpu_baseline_accept(inp):
             "sample": f"the whole batch ({B} sequences), {reps} calls; {dt * 1e3:.2f} ms per call"}
 
 
-def measured_traffic(workload, mx8, root=None):
+def kernel_path(moe, w, mx8):
+    """The kernels a forward call of this workload runs: the dense FP8 x FP4
+    kernels in MXFP8 mode; for bf16 activations the fused path (the library's
+    default; MOE_MXFP4_PATH=stream selects the per-phase launches), in its
+    ticketed form where the batch has more pairs than experts, else its
+    persistent form, up to FUSED_MAX_PAIRS pairs."""
+    if mx8:
+        return "dense"
+    if os.environ.get("MOE_MXFP4_PATH") == "stream" or w.P > moe.FUSED_MAX_PAIRS:
+        return "stream"
+    return "fused (ticketed)" if w.P > w.E else "fused (persistent)"
+
+
+def measured_traffic(workload, mx8, root=None, path=None):
     """Bytes beyond L2 per launch of the dominant kernel (FETCH_SIZE +
     WRITE_SIZE, each scaled by what it reads for a plain copy of known size;
     includes hits in the last-level cache, so it bounds HBM bytes from
     above) from the committed counter summary of this workload, or None when
     there is none or the kernel's source file changed since the counters were
-    taken.  root: the repository (default: here)."""
+    taken.  root: the repository (default: here); path "stream": the
+    per-phase path's summary (the default path's otherwise)."""
     import hashlib
     root = root or os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(root, "profiles", f"beyond_l2_bytes_{workload}.md")
-    if not os.path.exists(path):
+    # the per-phase path's counters sit in a summary of their own
+    suffix = "_stream" if path == "stream" else ""
+    summary = os.path.join(root, "profiles", f"beyond_l2_bytes_{workload}{suffix}.md")
+    if not os.path.exists(summary):
         return None
     fields = {}
-    for line in open(path):
+    for line in open(summary):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
@@ -373,7 +389,11 @@ def main():
     if wr is not None:
         layer_bytes += w.E * w.d * 2                  # router weights
     gateup_bytes = touched * 2 * w.f * w.d * (1 / 2 + 1 / 32) + w.T * w.d * 2
+    # the fused kernel runs both projections: all expert bytes, x, and the
+    # float32 per-pair outputs it writes
+    fused_bytes = touched * per_expert + w.T * w.d * 2 + w.P * w.d * 4
     flops = 2.0 * w.P * 3 * w.d * w.f
+    kpath = kernel_path(moe, w, mx8)
 
     for i in range(args.warmup):
         layers[i % args.copies](x, lg, out=out, workspace=ws, w_router=wr)
@@ -412,7 +432,7 @@ def main():
     gateup_us = stage_avg_us["gateup"] - spacing
     gateup_s = gateup_us * 1e-6
     gateup_flops = 2.0 * w.P * 2 * w.d * w.f
-    traffic = measured_traffic(w.name, mx8)
+    traffic = measured_traffic(w.name, mx8, path="stream" if kpath == "stream" else None)
     duration = {"duration_us": gateup_us, "duration_source":
                 f"HIP events around the kernel on its launch stream over {args.steps} calls, minus the "
                 f"{spacing:.2f} us two back-to-back events measure"}
@@ -429,11 +449,20 @@ def main():
                                  "rate is the FP8 one (5.0 PFLOP/s nominal); half the MXFP4 peak (5.05 PFLOP/s) "
                                  "is above that instruction's whole nominal rate and above what it measures here "
                                  "(measured_peak); frac_of_measured is the fraction that bounds this kernel"}
-    else:
+    elif kpath == "stream":
         achieved = gateup_bytes / gateup_s / 1e9
         roofline = {"bound": "hbm", "kernel": "k_expert<gate/up>", "achieved": achieved,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                     "traffic": traffic, "traffic_counter": traffic_note, "algorithmic_bytes": gateup_bytes,
+                    **duration}
+    else:
+        # one kernel runs gate/up and down (the down stage launches nothing)
+        achieved = fused_bytes / gateup_s / 1e9
+        kname = "k_chain (gate/up and down units, one launch)" if "ticketed" in kpath else \
+            "k_fused (persistent: gate/up and down units)"
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": achieved,
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": traffic, "traffic_counter": traffic_note, "algorithmic_bytes": fused_bytes,
                     **duration}
     result = {
         "metric": "MoE expert-layer tokens/s + achieved HBM GB/s (% of peak), 256-token verify",
@@ -455,7 +484,7 @@ def main():
                                f"{'MXFP8 (E4M3 + E8M0 per 32)' if mx8 else 'bf16'} activations, bf16 out"
                                f"{', router projection in the call (bf16 W_router [E][d])' if wr is not None else ''}",
                    "T": w.T, "d_model": w.d, "d_ff": w.f, "experts": w.E, "top_k": w.k,
-                   "touched_experts": touched, "weight_copies": args.copies},
+                   "touched_experts": touched, "weight_copies": args.copies, "kernel_path": kpath},
         "layer_hbm_gbs": layer_bytes / (ms_per_step * 1e-3) / 1e9,
         "layer_hbm_frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_algorithmic_bytes": layer_bytes,

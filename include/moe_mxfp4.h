@@ -47,8 +47,10 @@
  *     decoded weights and activations that stay finite in float32.
  *   - Fault injection, for tests of error propagation: with the environment
  *     variable MOE_MXFP4_FAULT set to a launch site (router, route, sort,
- *     quant, gateup, down, combine, dflash), a call that reaches that site
- *     returns MOE_ERR_HIP there without launching, as a failed launch would;
+ *     quant, gateup, down, combine, dflash; the fused path's one launch of
+ *     both projections is the gateup and the down site), a call that
+ *     reaches that site returns MOE_ERR_HIP there without launching, as a
+ *     failed launch would;
  *     the kernels queued before it stay queued.  Read on every call.
  *   - Logging: with MOE_MXFP4_LOG set (to anything but "0") when a context
  *     is created, create prints the configuration and each forward call
@@ -258,17 +260,27 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
 /*
  * Kernel paths (bf16 activations).  MOE_MXFP4_PATH, read when a context is
  * created, selects how a forward call runs the steps after routing:
- *   "stream" (default)  one launch per phase: permutation, gate/up + SwiGLU,
- *                       down, combine;
- *   "fused"             the permutation as per-expert pair lists (one
- *                       launch), then one persistent kernel for gate/up and
- *                       down, whose work items hand over through counters in
- *                       the workspace, so down work starts while gate/up
- *                       still streams weights, then the combine.  The
- *                       pages' runtime keeps one engine kernel resident so
- *                       that microsecond operators pay no gap between them
+ *   "fused" (default)   gate/up + SwiGLU and down as work units of one
+ *                       launch, handing over through counters in the
+ *                       workspace, so down work starts while gate/up still
+ *                       streams weights; then the combine.  The pages'
+ *                       runtime keeps one engine kernel resident so that
+ *                       microsecond operators pay no gap between them
  *                       (techllm.github.io "Xiaomi MiMo x TileRT", section
- *                       "3. TileRT"); batches up to 8192 pairs.
+ *                       "3. TileRT").  Batches of more pairs than experts
+ *                       take the ticketed form: the permutation launch also
+ *                       lists each XCD's chunks, and every workgroup of the
+ *                       one launch takes a ticket and runs that unit
+ *                       (gate/up units first, then down units, each waiting
+ *                       for its chunk).  Smaller batches take the
+ *                       persistent form: per-expert pair lists (one launch),
+ *                       then a kernel of as many workgroups as the GPU
+ *                       holds, each looping over gate/up units and then
+ *                       taking down units from a queue.  Batches up to
+ *                       MOE_MXFP4_FUSED_MAX_PAIRS pairs; larger ones run
+ *                       "stream".
+ *   "stream"            one launch per phase: permutation, gate/up +
+ *                       SwiGLU, down, combine.
  * Both give bit-identical outputs.  Any other value makes create fail with
  * MOE_ERR_INVALID_ARG.  MXFP8 mode has one path (the dense kernels).
  *
@@ -281,6 +293,8 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
  * *status (host): 0 = no wait gave up; always 0 on paths without such
  * waits.  Errors: INVALID_ARG, CAPACITY, HIP.
  */
+#define MOE_MXFP4_FUSED_MAX_PAIRS 8192
+
 moe_status moe_mxfp4_device_status(const moe_mxfp4_ctx* ctx, const void* workspace, int32_t num_tokens,
                                    int32_t* status, void* hip_stream);
 

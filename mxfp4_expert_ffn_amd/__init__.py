@@ -35,6 +35,9 @@ EXPORTS = ("moe_mxfp4_status_string", "moe_mxfp4_abi_version", "moe_mxfp4_create
            "moe_mxfp4_forward_noalloc", "moe_mxfp4_device_status", "moe_mxfp4_debug_hidden")
 # Scratch bytes moe_mxfp4_forward_noalloc holds per GPU (MOE_MXFP4_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
+# Largest batch (tokens x top_k) the fused path runs (MOE_MXFP4_FUSED_MAX_PAIRS);
+# larger ones take the per-phase launches.
+FUSED_MAX_PAIRS = 8192
 NUM_STAGES = 6
 STAGES = ("route", "sort", "quant", "gateup", "down", "combine")
 

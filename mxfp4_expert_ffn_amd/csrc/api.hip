@@ -167,7 +167,7 @@ moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg, const moe_mxfp4_weights
     if (!ctx) return MOE_ERR_INTERNAL;
     ctx->cfg = *cfg;
     ctx->w = *weights;
-    ctx->fused = path && std::strcmp(path, "fused") == 0;
+    ctx->fused = !(path && std::strcmp(path, "stream") == 0);      // "fused" is the default
     const char* lg = std::getenv("MOE_MXFP4_LOG");
     ctx->log = lg && *lg && std::strcmp(lg, "0") != 0;
     if (ctx->log)
@@ -282,23 +282,38 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
         // pair lists and chunk list (timed as the permutation stage), the
         // persistent kernel (gate/up and down: timed as the gate/up stage),
         // the combine
-        if (fault_at("route") ||
-            moe::launch_route(router_logits, dm, ws, s, ws.fctl, moe::fused_ctl_ints(dm)) != hipSuccess ||
-            mark(1) != hipSuccess)
-            return MOE_ERR_HIP;
-        if (fault_at("sort") || moe::launch_fused_lists(dm, ws, s) != hipSuccess || mark(2) != hipSuccess ||
-            mark(3) != hipSuccess)
-            return MOE_ERR_HIP;
-        if (fault_at("gateup") || moe::launch_fused(x, ctx->w, dm, ws, spin_limit(), s) != hipSuccess ||
+        const bool chain = moe::fused_chain_form(dm);
+        if (chain && moe::route_sort_fused(dm)) {
+            if (fault_at("route") ||
+                moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s, ws.fctl, moe::fused_ctl_ints(dm)) !=
+                    hipSuccess ||
+                mark(1) != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess)
+                return MOE_ERR_HIP;
+        } else {
+            if (fault_at("route") ||
+                moe::launch_route(router_logits, dm, ws, s, ws.fctl, moe::fused_ctl_ints(dm)) != hipSuccess ||
+                mark(1) != hipSuccess)
+                return MOE_ERR_HIP;
+            if (fault_at("sort") ||
+                (chain ? moe::launch_sort(dm, ws, chunk_rows, s) : moe::launch_fused_lists(dm, ws, s)) != hipSuccess ||
+                mark(2) != hipSuccess || mark(3) != hipSuccess)
+                return MOE_ERR_HIP;
+        }
+        // one launch runs both projections: it is the gate/up and the down site
+        if (fault_at("gateup") || fault_at("down") ||
+            moe::launch_fused(x, ctx->w, dm, ws, spin_limit(), s) != hipSuccess ||
             mark(4) != hipSuccess || mark(5) != hipSuccess)
             return MOE_ERR_HIP;
         if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, false, s) != hipSuccess ||
             mark(6) != hipSuccess)
             return MOE_ERR_HIP;
         if (ctx->log && ctx->logged_tokens.exchange(dm.T) != dm.T)
-            std::fprintf(stderr, "moe_mxfp4: T=%d P=%d E=%d d=%d f=%d k=%d: %srouting, per-expert pair lists, "
-                         "persistent kernel (gate/up + SwiGLU, down), combine (float32 per-pair outputs)\n",
-                         dm.T, dm.P, dm.E, dm.d, dm.f, dm.k, w_router ? "router projection, " : "");
+            std::fprintf(stderr, "moe_mxfp4: T=%d P=%d E=%d d=%d f=%d k=%d: %s%s, combine (float32 per-pair "
+                         "outputs)\n",
+                         dm.T, dm.P, dm.E, dm.d, dm.f, dm.k, w_router ? "router projection, " : "",
+                         chain ? "routing, permutation + per-XCD chunk lists, one launch of ticketed gate/up and "
+                                 "down units"
+                               : "routing, per-expert pair lists, persistent kernel (gate/up + SwiGLU, down)");
         return copy_debug(c, dm, ws, debug_out, s);
     }
     const bool fused_rs = moe::route_sort_fused(dm);

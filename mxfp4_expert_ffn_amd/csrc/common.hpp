@@ -145,18 +145,20 @@ inline int xcd_slots(const Dims& dm) {
     return (max_chunks(dm) + kXcds - 1) / kXcds + (T + kChunk - 1) / kChunk;
 }
 
-// The fused path (bf16 activations): after the routing launch (which clears
-// the fused_ctl_ints(dm) counters), launch_fused_lists builds the stable
-// per-expert pair lists, the expert offsets and the chunk list, and
-// launch_fused runs gate/up and down as work units of one persistent
-// kernel.  Up to kFusedMaxPairs pairs.
-constexpr int kFusedMaxPairs = 8192;
+// The fused path (bf16 activations): the routing launch clears the
+// fused_ctl_ints(dm) counters; then, in the ticketed form
+// (fused_chain_form), the per-phase permutation launch (which also writes
+// the per-XCD chunk table), or else launch_fused_lists (stable per-expert
+// pair lists, expert offsets, chunk list); then launch_fused runs gate/up
+// and down as work units of one launch.  Up to kFusedMaxPairs pairs.
+constexpr int kFusedMaxPairs = MOE_MXFP4_FUSED_MAX_PAIRS;
 bool fused_supported(const Dims& dm);
 int fused_ctl_ints(const Dims& dm);
 // Index of the error word in the counters: nonzero after a call in which a
 // device-side wait gave up.
 constexpr int kFusedErrorWord = 64;   // ints from the start of the counters
 hipError_t launch_fused_lists(const Dims& dm, const Workspace& ws, hipStream_t s);
+bool fused_chain_form(const Dims& dm);
 hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
                         int spin_limit, hipStream_t s);
 
@@ -181,7 +183,7 @@ hipError_t launch_sort(const Dims& dm, const Workspace& ws, int chunk_rows, hipS
 // Small batches: routing and permutation in one launch (when route_sort_fused).
 bool route_sort_fused(const Dims& dm);
 hipError_t launch_route_sort(const float* logits, const Dims& dm, const Workspace& ws, int chunk_rows,
-                             hipStream_t s);
+                             hipStream_t s, int32_t* zero = nullptr, int nzero = 0);
 hipError_t launch_quant_x8(const uint16_t* x, const Dims& dm, const Workspace& ws, hipStream_t s);
 hipError_t launch_quant_act8(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);

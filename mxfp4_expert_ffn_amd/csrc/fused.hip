@@ -1,7 +1,19 @@
-// The expert layer after routing as ONE resident kernel: gate/up + SwiGLU
-// and the down projection run as work items of a persistent grid, so the
-// two phases overlap instead of each draining the GPU before the next launch
-// ramps up.  A small launch in front of it builds the permutation.
+// The expert layer after routing as ONE launch: gate/up + SwiGLU and the
+// down projection run as work units of a single grid, so the two phases
+// overlap instead of each draining the GPU before the next launch ramps up.
+// Two forms (fused_chain_form picks one per batch):
+//
+//   - ticketed (k_chain; batches with more pairs than experts): the
+//     per-phase permutation launch, which also lists each XCD's chunks,
+//     then one workgroup per unit, each taking a ticket (see k_chain);
+//   - persistent (k_fused; at most one pair per expert on average): a small
+//     launch builds per-expert pair lists, then a grid of as many
+//     workgroups as the GPU holds loops over the units, as described below.
+//
+// The unit bodies compile to the per-phase kernels' schedule only where a
+// workgroup runs one unit: inside a loop over units the compiler keeps one
+// activation fragment register and waits on every LDS read, which is what
+// the persistent form pays for its smaller grid.
 //
 // The pages' runtime keeps a single engine kernel resident on the GPU so
 // that microsecond operators pay no launch or synchronisation gap between
@@ -57,7 +69,8 @@ using stream::kThreads;
 // polls of waiting workgroups and the atomics on other counters do not queue
 // behind each other at one memory channel.
 constexpr int kLine = 64;                       // ints per 256 bytes
-enum { kScanDone = 0, kError = kLine, kDownQueue = 2 * kLine, kChunkDone = 3 * kLine };
+enum { kScanDone = 0, kError = kLine, kDownQueue = 2 * kLine, kTicket = 3 * kLine,
+       kChunkDone = kTicket + kXcds * kLine };
 static_assert(kError == kFusedErrorWord, "the host reads the error word at this index");
 
 struct FusedArgs {
@@ -73,6 +86,8 @@ struct FusedArgs {
     int32_t E, T, P;
     int32_t ntg, ntd;          // column tiles per chunk: gate/up, down
     int32_t spin_limit;        // poll rounds before a wait gives up; < 0: every wait gives up at once
+    const int32_t* xtab;       // per-XCD chunk table (ticketed form)
+    int32_t xstride;
 };
 
 __device__ __forceinline__ int32_t load_agent(const int32_t* p) {
@@ -250,6 +265,58 @@ __global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
     }
 }
 
+// Ticketed form: one unit per workgroup.  Workgroup b takes the next
+// ticket of counter b mod kXcds (so each counter serves exactly its share of
+// the grid whatever the dispatch order) and runs unit `ticket` of that
+// XCD's list in the per-XCD chunk table: first the gate/up units of its
+// chunks (chunk-major), then their down units in the same order.  A down
+// unit waits only for gate/up units of its chunk, which sit earlier in the
+// same list: their tickets were taken first, by workgroups that are running
+// or done and never wait, so every wait ends.  With the GPU's round-robin
+// dispatch, a list's units also run on one XCD and share its L2.
+template <int RT, int DG, int DD>
+__global__ __launch_bounds__(kThreads, 2) void k_chain(FusedArgs f) {
+    constexpr int kRing = DG > DD ? DG : DD;
+    // one LDS object (see k_fused): the ring, then two words
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kSlot + 2 * sizeof(int32_t)];
+    int32_t& s_flag = *reinterpret_cast<int32_t*>(lds + kRing * kSlot);
+    int32_t& s_tick = *reinterpret_cast<int32_t*>(lds + kRing * kSlot + sizeof(int32_t));
+    const int x = blockIdx.x % kXcds;
+    if (threadIdx.x == 0)
+        s_tick = __hip_atomic_fetch_add(f.ctl + kTicket + kLine * x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int nslots = __builtin_amdgcn_readfirstlane(f.xtab[x]);
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(s_tick);
+    const int nG = nslots * f.ntg, nD = nslots * f.ntd;
+    const bool gateup = t < nG;
+    if (!gateup && t - nG >= nD) return;                 // past the list: nothing to do
+    const int u = gateup ? t : t - nG;
+    const int nt_per = gateup ? f.ntg : f.ntd;
+    const int32_t* rec = f.xtab + kXtabHead + kChunkRec * (x * f.xstride + u / nt_per);
+    const int nt = u % nt_per;
+    const int e = __builtin_amdgcn_readfirstlane(rec[0]);
+    const int start = __builtin_amdgcn_readfirstlane(rec[1]);
+    const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
+    const int chunk = __builtin_amdgcn_readfirstlane(rec[3]);
+    // the chunk's pairs sit at sorted positions start .. start + rows - 1
+    if (gateup) {
+        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, f.sorted + start, start, rows, [] {});
+        publish(f.ctl + kChunkDone + kLine * chunk);
+    } else {
+        if (!await(f, f.ctl + kChunkDone + kLine * chunk, f.ntg, &s_flag)) return;
+        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, f.sorted + start, start, rows, [] {});
+    }
+}
+
+template <int RT, int DG, int DD>
+hipError_t launch_chain(const FusedArgs& f, const Dims& dm, hipStream_t s) {
+    // every counter gets xstride * (ntg + ntd) workgroups: at least the
+    // units of the longest list
+    const dim3 grid(kXcds * f.xstride * (f.ntg + f.ntd));
+    hipLaunchKernelGGL((k_chain<RT, DG, DD>), grid, dim3(kThreads), 0, s, f);
+    return hipGetLastError();
+}
+
 template <int RT, int DG, int DD>
 hipError_t launch_variant(const FusedArgs& f, int items, hipStream_t s) {
     // grid = the workgroups the GPU holds at once (no more are useful: each
@@ -303,6 +370,8 @@ FusedArgs make_args(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& d
     f.gu.n_tiles = f.ntg;
     f.dn.n_tiles = f.ntd;
     f.spin_limit = spin_limit;
+    f.xtab = ws.xtab;
+    f.xstride = xcd_slots(dm);
     return f;
 }
 
@@ -316,11 +385,31 @@ hipError_t launch_fused_lists(const Dims& dm, const Workspace& ws, hipStream_t s
     return hipGetLastError();
 }
 
+// The ticketed form wins where experts have several pairs (256 tokens:
+// 138 against 151 us for the persistent kernel, 145 for the per-phase
+// launches); at most one pair per expert on average the persistent kernel
+// (74 against 78 us at 8 tokens), whose grid is only the resident
+// workgroups.
+bool fused_chain_form(const Dims& dm) { return dm.P > dm.E; }
+
 hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
                         int spin_limit, hipStream_t s) {
     using namespace stream;
     const fused::FusedArgs f = fused::make_args(x, w, dm, ws, spin_limit);
     const int RT = tiles_per_wave(dm);
+    if (fused_chain_form(dm)) {
+        const bool g4 = (dm.d / kKStep) % 4 == 0, d4 = (dm.f / kKStep) % 4 == 0;
+        if (RT == 2) {
+            if (g4 && d4) return fused::launch_chain<2, 4, 4>(f, dm, s);
+            if (g4) return fused::launch_chain<2, 4, 2>(f, dm, s);
+            if (d4) return fused::launch_chain<2, 2, 4>(f, dm, s);
+            return fused::launch_chain<2, 2, 2>(f, dm, s);
+        }
+        if (g4 && d4) return fused::launch_chain<4, 4, 4>(f, dm, s);
+        if (g4) return fused::launch_chain<4, 4, 2>(f, dm, s);
+        if (d4) return fused::launch_chain<4, 2, 4>(f, dm, s);
+        return fused::launch_chain<4, 2, 2>(f, dm, s);
+    }
     const int items = max_chunks(dm) * (f.ntg + f.ntd);
     const bool g4 = (dm.d / kKStep) % 4 == 0, d4 = (dm.f / kKStep) % 4 == 0;
     if (RT == 2) {

@@ -485,8 +485,10 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __rest
                                                              int32_t* __restrict__ active,
                                                              int32_t* __restrict__ chunks,
                                                              int32_t* __restrict__ nchunks, int chunk_rows,
-                                                             int32_t* __restrict__ xtab, int xstride) {
+                                                             int32_t* __restrict__ xtab, int xstride,
+                                                             int32_t* __restrict__ zero, int nzero) {
     extern __shared__ uint64_t sm64[];
+    clear_counters(zero, nzero);
     uint8_t* extra = reinterpret_cast<uint8_t*>(sm64) + sort_lds_bytes(dm.E);
     int32_t* ids_lds = reinterpret_cast<int32_t*>(extra);
     RankScratch<1>* sc = reinterpret_cast<RankScratch<1>*>(extra + (((size_t)dm.P * sizeof(int32_t) + 15) & ~(size_t)15));
@@ -575,8 +577,10 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort_tiny(const float* _
                                                                   int32_t* __restrict__ active,
                                                                   int32_t* __restrict__ chunks,
                                                                   int32_t* __restrict__ nchunks,
-                                                                  int32_t* __restrict__ xtab, int xstride) {
+                                                                  int32_t* __restrict__ xtab, int xstride,
+                                                                  int32_t* __restrict__ zero, int nzero) {
     __shared__ RankScratch<1> sc[kSortWaves];
+    clear_counters(zero, nzero);
     __shared__ int32_t ids_lds[kWave];
     __shared__ int32_t cnt[kWave];
     __shared__ int32_t exo[kWave];
@@ -725,19 +729,19 @@ bool route_sort_fused(const Dims& dm) {
 }
 
 hipError_t launch_route_sort(const float* logits, const Dims& dm, const Workspace& ws, int chunk_rows,
-                             hipStream_t s) {
+                             hipStream_t s, int32_t* zero, int nzero) {
     if (dm.P <= kWave && dm.P <= chunk_rows) {        // dm.E <= 64 holds for every fused batch
         const int waves = dm.T < kSortWaves ? dm.T : kSortWaves;
         hipLaunchKernelGGL(k_route_sort_tiny, dim3(1), dim3(waves * kWave), 0, s, logits, dm, ws.topk_ids,
                            ws.topk_w, ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks, ws.xtab,
-                           xcd_slots(dm));
+                           xcd_slots(dm), zero, nzero);
         return hipGetLastError();
     }
     const size_t lds = sort_lds_bytes(dm.E) + (((size_t)dm.P * sizeof(int32_t) + 15) & ~(size_t)15) +
                        kSortWaves * sizeof(RankScratch<1>);
     hipLaunchKernelGGL(k_route_sort, dim3(1), dim3(kSortThreads), lds, s, logits, dm, ws.topk_ids, ws.topk_w,
                        ws.offsets, ws.sorted_pairs, ws.active, ws.chunks, ws.nchunks, chunk_rows, ws.xtab,
-                       xcd_slots(dm));
+                       xcd_slots(dm), zero, nzero);
     return hipGetLastError();
 }
 

@@ -167,9 +167,10 @@ def test_path_selection_and_device_status_validation(monkeypatch):
         assert (st == 0) == ok, (path, st)
         if st == 0:
             L.moe_mxfp4_destroy(h)
-    monkeypatch.delenv("MOE_MXFP4_PATH")
+    monkeypatch.setenv("MOE_MXFP4_PATH", "stream")
     ds = L.moe_mxfp4_device_status
     st, h = _create()
+    monkeypatch.delenv("MOE_MXFP4_PATH")
     out = ctypes.c_int32(7)
     try:
         assert ds(None, FAKE, 8, ctypes.byref(out), None) == 1
