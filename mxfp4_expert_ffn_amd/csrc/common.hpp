@@ -129,15 +129,16 @@ inline int max_chunks(const Dims& dm) {
 
 // Per-XCD chunk table.  The GPU hands workgroups to its kXcds XCDs
 // round-robin by workgroup index, and each XCD has its own L2.  The sort
-// assigns every active expert to one XCD, in snake order over groups of
-// kXcds consecutive ranks (ranks 0..7 to XCDs 0..7, ranks 8..15 to XCDs
-// 7..0, ...), and lists each XCD's chunks expert by expert; the streaming
-// kernels run XCD x's chunks on workgroups x, x + kXcds, ..., so all the
-// units of an expert -- its weight tiles, and each chunk's activation rows
-// -- go through one L2.  Only the speed depends on that dispatch order.
-// Since chunk counts do not increase with rank, an XCD holds at most
-// nchunks / kXcds plus one expert's chunks (at most ceil(T / kChunk),
-// every token picking distinct experts), which bounds the table's slots.
+// assigns every active expert to one XCD -- in rank order, each to the XCD
+// with the fewest chunks so far (greedy list scheduling) -- and lists each
+// XCD's chunks expert by expert; the streaming kernels run XCD x's chunks
+// on workgroups x, x + kXcds, ..., so all the units of an expert -- its
+// weight tiles, and each chunk's activation rows -- go through one L2.
+// Only the speed depends on that dispatch order.  When an XCD receives its
+// last expert it holds the fewest chunks, at most floor((nchunks - m) /
+// kXcds), so no list exceeds floor(nchunks / kXcds) plus one expert's
+// chunks (at most ceil(T / kChunk), every token picking distinct experts),
+// which bounds the table's slots.
 constexpr int kXcds = 8;
 constexpr int kXtabHead = 64;      // ints before the records
 inline int xcd_slots(const Dims& dm) {

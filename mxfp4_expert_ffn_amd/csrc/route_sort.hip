@@ -363,23 +363,58 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
     }
     if (tid == kSortThreads - 1) *nchunks = cbefore + nincl;
     __syncthreads();
-    // per-XCD chunk table: wave x (< kXcds) takes XCD x, lane j the rank that
-    // group j of kXcds ranks gives it in snake order; a scan of their chunk
-    // counts places each expert's chunks in the XCD's list
-    if (tid < kXcds * kWave) {
-        const int x = wave, j = lane;
-        const int r = kXcds * j + ((j & 1) ? kXcds - 1 - x : x);
-        const int e = r < na ? act[r] : 0;
-        const int n = r < na ? counts[e] : 0;
+    // per-XCD chunk table: the experts in rank order (chunk counts never
+    // increase with rank), each to the XCD with the fewest chunks so far,
+    // the lowest index on ties -- greedy list scheduling, whose largest list
+    // holds at most floor(nchunks / kXcds) plus one expert's chunks.  Equal
+    // counts come in runs, and greedy deals a run to the XCDs at the lowest
+    // load one each, in index order, before any load above it: so wave 0
+    // places up to kXcds experts per round (lane x < kXcds holds XCD x's
+    // load, lane i the count of rank r0 + i of the current block of ranks).
+    // keys[] (free after the ranking) receives each rank's
+    // (XCD << 24 | first slot).
+    int32_t* xasg = reinterpret_cast<int32_t*>(keys);
+    if (wave == 0) {
+        int load = 0;                                   // lane x < kXcds: XCD x's chunks so far
+        for (int r0 = 0; r0 < na; r0 += kWave) {
+            const int rr = r0 + lane;
+            const int mv = rr < na ? (counts[act[rr]] + chunk_rows - 1) / chunk_rows : 0;
+            const int nb = min(kWave, na - r0);
+            int pos = 0;                                // next rank of the block to place
+            while (pos < nb) {
+                const int m = __builtin_amdgcn_readlane(mv, pos);
+                // the run of ranks with this count, from pos to the block's end at most
+                const uint64_t run = __ballot(lane >= pos && lane < nb && mv == m);
+                const int nrun = (int)__builtin_popcountll(run);
+                // the XCDs at the lowest load (lane reads into scalar
+                // registers, not cross-lane shuffles through LDS)
+                int lo = __builtin_amdgcn_readlane(load, 0);
+#pragma unroll
+                for (int k = 1; k < kXcds; ++k) lo = min(lo, __builtin_amdgcn_readlane(load, k));
+                const uint64_t takers = __ballot(lane < kXcds && load == lo);
+                const int before = (int)__builtin_popcountll(takers & ((1ull << lane) - 1));   // lower-indexed takers
+                const int ntake = (int)__builtin_popcountll(takers);
+                const int cnt = ntake < nrun ? ntake : nrun;
+                if (lane < kXcds && load == lo && before < cnt) {
+                    xasg[r0 + pos + before] = (lane << 24) | load;
+                    load += m;
+                }
+                pos += cnt;
+            }
+        }
+        if (lane < kXcds) xtab[lane] = load;
+    }
+    __syncthreads();
+    if (tid < na) {
+        const int a = xasg[tid], x = a >> 24, slot = a & 0xFFFFFF;
+        const int e = act[tid], n = counts[e];
         const int m = (n + chunk_rows - 1) / chunk_rows;
-        const int incl = wave_inclusive_scan(m, lane);
-        if (lane == kWave - 1) xtab[x] = incl;
-        int32_t* rec = xtab + kXtabHead + kChunkRec * ((size_t)x * xstride + (incl - m));
+        int32_t* rec = xtab + kXtabHead + kChunkRec * ((size_t)x * xstride + slot);
         for (int q = 0; q < m; ++q) {
             rec[kChunkRec * q + 0] = e;
             rec[kChunkRec * q + 1] = exoff[e] + q * chunk_rows;
             rec[kChunkRec * q + 2] = min(chunk_rows, n - q * chunk_rows);
-            rec[kChunkRec * q + 3] = rnk[r] + q;      // the chunk's index in the global list
+            rec[kChunkRec * q + 3] = rnk[tid] + q;    // the chunk's index in the global list
         }
     }
     return tid < E ? excl : 0;
@@ -545,19 +580,15 @@ __device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, in
         rec[2] = c;
         rec[3] = 0;
         // per-XCD table (the layout of expert_lists): one chunk per expert,
-        // so rank r sits in slot r / kXcds of its XCD's list
-        const int j = r / kXcds, i = r % kXcds;
-        int32_t* xr = xtab + kXtabHead + kChunkRec * ((size_t)((j & 1) ? kXcds - 1 - i : i) * xstride + j);
+        // so the greedy assignment deals rank r to XCD r mod kXcds, slot
+        // r / kXcds
+        int32_t* xr = xtab + kXtabHead + kChunkRec * ((size_t)(r % kXcds) * xstride + r / kXcds);
         xr[0] = lane;
         xr[1] = excl;
         xr[2] = c;
         xr[3] = r;
     }
-    if (lane < kXcds) {
-        int n = 0;
-        for (int j = 0; kXcds * j < na; ++j) n += kXcds * j + ((j & 1) ? kXcds - 1 - lane : lane) < na;
-        xtab[lane] = n;
-    }
+    if (lane < kXcds) xtab[lane] = na / kXcds + (lane < na % kXcds);
     if (lane == 0) {
         offsets[E] = P;
         active[E] = na;
