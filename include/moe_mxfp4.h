@@ -267,16 +267,16 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
  *                       runtime keeps one engine kernel resident so that
  *                       microsecond operators pay no gap between them
  *                       (techllm.github.io "Xiaomi MiMo x TileRT", section
- *                       "3. TileRT").  Batches of more pairs than experts
- *                       take the ticketed form: the permutation launch also
- *                       lists each XCD's chunks, and every workgroup of the
- *                       one launch takes a ticket and runs that unit
+ *                       "3. TileRT").  Routing and the permutation are
+ *                       the per-phase launches (the permutation also lists
+ *                       each XCD's chunks).  Batches of more pairs than
+ *                       experts take the ticketed form: every workgroup of
+ *                       the one launch takes a ticket and runs that unit
  *                       (gate/up units first, then down units, each waiting
  *                       for its chunk).  Smaller batches take the
- *                       persistent form: per-expert pair lists (one launch),
- *                       then a kernel of as many workgroups as the GPU
- *                       holds, each looping over gate/up units and then
- *                       taking down units from a queue.  Batches up to
+ *                       persistent form: a kernel of as many workgroups as
+ *                       the GPU holds, each looping over gate/up units and
+ *                       then taking down units from a queue.  Batches up to
  *                       MOE_MXFP4_FUSED_MAX_PAIRS pairs; larger ones run
  *                       "stream".
  *   "stream"            one launch per phase: permutation, gate/up +

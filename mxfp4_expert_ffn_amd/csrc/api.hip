@@ -48,7 +48,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
     size_t logits, ids, w, offsets, sorted, active, chunks, nchunks, xtab, sort_part, xq, xs, h, hs, o, fctl,
-        fcounts, flists, total;
+        total;
 };
 
 Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
@@ -73,11 +73,9 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     L.h = at;       at += round256(P * (size_t)c.d_ff * (mx8 ? 1 : sizeof(uint16_t)));
     L.hs = at;      at += mx8 ? round256(P * (size_t)(c.d_ff / MOE_MXFP4_BLOCK)) : 0;
     L.o = at;       at += round256(P * (size_t)c.d_model * sizeof(float));
-    // the fused path's counters and per-expert pair lists (bf16 mode)
+    // the fused path's counters (bf16 mode)
     const bool fz = !mx8 && moe::fused_supported(dm);
     L.fctl = at;    at += fz ? round256((size_t)moe::fused_ctl_ints(dm) * sizeof(int32_t)) : 0;
-    L.fcounts = at; at += fz ? round256((size_t)c.num_experts * sizeof(int32_t)) : 0;
-    L.flists = at;  at += fz ? round256((size_t)c.num_experts * T * sizeof(int32_t)) : 0;
     L.total = at;
     return L;
 }
@@ -278,27 +276,18 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
     }
     const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
     if (!mx8 && ctx->fused && moe::fused_supported(dm)) {
-        // routing (which clears the fused kernel's counters), the per-expert
-        // pair lists and chunk list (timed as the permutation stage), the
-        // persistent kernel (gate/up and down: timed as the gate/up stage),
-        // the combine
+        // routing (which clears the fused kernel's counters) and the
+        // permutation, then one launch of gate/up and down units (timed as
+        // the gate/up stage), then the combine
         const bool chain = moe::fused_chain_form(dm);
-        if (chain && moe::route_sort_fused(dm)) {
-            if (fault_at("route") ||
-                moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s, ws.fctl, moe::fused_ctl_ints(dm)) !=
-                    hipSuccess ||
-                mark(1) != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess)
-                return MOE_ERR_HIP;
-        } else {
-            if (fault_at("route") ||
-                moe::launch_route(router_logits, dm, ws, s, ws.fctl, moe::fused_ctl_ints(dm)) != hipSuccess ||
-                mark(1) != hipSuccess)
-                return MOE_ERR_HIP;
-            if (fault_at("sort") ||
-                (chain ? moe::launch_sort(dm, ws, chunk_rows, s) : moe::launch_fused_lists(dm, ws, s)) != hipSuccess ||
-                mark(2) != hipSuccess || mark(3) != hipSuccess)
-                return MOE_ERR_HIP;
-        }
+        const bool rs = moe::route_sort_fused(dm);
+        if (fault_at("route") ||
+            (rs ? moe::launch_route_sort(router_logits, dm, ws, chunk_rows, s, ws.fctl, moe::fused_ctl_ints(dm))
+                : moe::launch_route(router_logits, dm, ws, s, ws.fctl, moe::fused_ctl_ints(dm))) != hipSuccess ||
+            mark(1) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (!rs && (fault_at("sort") || moe::launch_sort(dm, ws, chunk_rows, s) != hipSuccess)) return MOE_ERR_HIP;
+        if (mark(2) != hipSuccess || mark(3) != hipSuccess) return MOE_ERR_HIP;
         // one launch runs both projections: it is the gate/up and the down site
         if (fault_at("gateup") || fault_at("down") ||
             moe::launch_fused(x, ctx->w, dm, ws, spin_limit(), s) != hipSuccess ||
@@ -313,7 +302,7 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
                          dm.T, dm.P, dm.E, dm.d, dm.f, dm.k, w_router ? "router projection, " : "",
                          chain ? "routing, permutation + per-XCD chunk lists, one launch of ticketed gate/up and "
                                  "down units"
-                               : "routing, per-expert pair lists, persistent kernel (gate/up + SwiGLU, down)");
+                               : "routing, permutation, persistent kernel (gate/up + SwiGLU, down)");
         return copy_debug(c, dm, ws, debug_out, s);
     }
     const bool fused_rs = moe::route_sort_fused(dm);
@@ -393,8 +382,6 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
     ws.o = reinterpret_cast<float*>(base + L.o);
     ws.os = reinterpret_cast<uint8_t*>(base + L.o + (size_t)num_tokens * c.top_k * c.d_model * sizeof(uint16_t));
     ws.fctl = reinterpret_cast<int32_t*>(base + L.fctl);
-    ws.fcounts = reinterpret_cast<int32_t*>(base + L.fcounts);
-    ws.flists = reinterpret_cast<int32_t*>(base + L.flists);
 
     moe::Dims dm{num_tokens, c.d_model, c.d_ff, c.num_experts, c.top_k, num_tokens * c.top_k};
     hipStream_t s = static_cast<hipStream_t>(hip_stream);

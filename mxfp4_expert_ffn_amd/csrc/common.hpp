@@ -105,9 +105,7 @@ struct Workspace {
                               // mode: fp16 codes in the first half of that space
     uint8_t* os;              // MXFP8 mode: [P][d/128] scale exponents + 127 of o's fp16
                               // codes, placed after them inside o's space
-    int32_t* fctl;            // fused path: work-queue, error and completion counters
-    int32_t* fcounts;         // fused path: [E] pairs per expert
-    int32_t* flists;          // fused path: [E][T] pair ids of each expert, ascending
+    int32_t* fctl;            // fused path: work-queue, ticket, error and completion counters
 };
 
 // Problem description passed by value to kernels.
@@ -147,18 +145,16 @@ inline int xcd_slots(const Dims& dm) {
 }
 
 // The fused path (bf16 activations): the routing launch clears the
-// fused_ctl_ints(dm) counters; then, in the ticketed form
-// (fused_chain_form), the per-phase permutation launch (which also writes
-// the per-XCD chunk table), or else launch_fused_lists (stable per-expert
-// pair lists, expert offsets, chunk list); then launch_fused runs gate/up
-// and down as work units of one launch.  Up to kFusedMaxPairs pairs.
+// fused_ctl_ints(dm) counters, the permutation launch writes the chunk list
+// and the per-XCD chunk table, then launch_fused runs gate/up and down as
+// work units of one launch: ticketed (fused_chain_form) or persistent.  Up
+// to kFusedMaxPairs pairs.
 constexpr int kFusedMaxPairs = MOE_MXFP4_FUSED_MAX_PAIRS;
 bool fused_supported(const Dims& dm);
 int fused_ctl_ints(const Dims& dm);
 // Index of the error word in the counters: nonzero after a call in which a
 // device-side wait gave up.
 constexpr int kFusedErrorWord = 64;   // ints from the start of the counters
-hipError_t launch_fused_lists(const Dims& dm, const Workspace& ws, hipStream_t s);
 bool fused_chain_form(const Dims& dm);
 hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
                         int spin_limit, hipStream_t s);

@@ -3,12 +3,15 @@
 // overlap instead of each draining the GPU before the next launch ramps up.
 // Two forms (fused_chain_form picks one per batch):
 //
-//   - ticketed (k_chain; batches with more pairs than experts): the
-//     per-phase permutation launch, which also lists each XCD's chunks,
-//     then one workgroup per unit, each taking a ticket (see k_chain);
-//   - persistent (k_fused; at most one pair per expert on average): a small
-//     launch builds per-expert pair lists, then a grid of as many
-//     workgroups as the GPU holds loops over the units, as described below.
+//   - ticketed (k_chain; batches with more pairs than experts): one
+//     workgroup per unit, each taking a ticket (see k_chain);
+//   - persistent (k_fused; at most one pair per expert on average): a grid
+//     of as many workgroups as the GPU holds loops over the units, as
+//     described below.
+//
+// Both run after the per-phase routing and permutation launches (the
+// permutation also lists each XCD's chunks), whose first launch also clears
+// the counters here.
 //
 // The unit bodies compile to the per-phase kernels' schedule only where a
 // workgroup runs one unit: inside a loop over units the compiler keeps one
@@ -22,11 +25,6 @@
 // 런타임"; dothoosh.com article, section "TileRT: عصر فشار بر GPU").  On gfx950
 // the same idea takes this form:
 //
-//   - k_expert_lists (one workgroup per expert): the ids of expert e's pairs
-//     in ascending pair order -- a stable counting sort, each expert
-//     independent -- and their count; the last workgroup to finish (a
-//     counter) turns the counts into expert offsets and the chunk list
-//     (chunks of <= 64 pairs, expert by expert).
 //   - k_fused (as many workgroups as the GPU holds at once): workgroup b
 //     first runs the gate/up units (chunk, column tile) b, b + G, b + 2G, ...
 //     -- a fixed assignment, no queue atomics, and a gate/up unit never
@@ -69,21 +67,16 @@ using stream::kThreads;
 // polls of waiting workgroups and the atomics on other counters do not queue
 // behind each other at one memory channel.
 constexpr int kLine = 64;                       // ints per 256 bytes
-enum { kScanDone = 0, kError = kLine, kDownQueue = 2 * kLine, kTicket = 3 * kLine,
-       kChunkDone = kTicket + kXcds * kLine };
+// (line 0 is spare)
+enum { kError = kLine, kDownQueue = 2 * kLine, kTicket = 3 * kLine, kChunkDone = kTicket + kXcds * kLine };
 static_assert(kError == kFusedErrorWord, "the host reads the error word at this index");
 
 struct FusedArgs {
     GemmArgs gu, dn;
-    const int32_t* ids;        // [P] expert of each pair (routing output)
     int32_t* ctl;              // counters (cleared by the routing launch)
-    int32_t* counts;           // [E] pairs per expert
-    int32_t* lists;            // [E][T] pair ids of each expert, ascending
-    int32_t* offsets;          // [E+1] first sorted position of each expert
-    int32_t* sorted;           // [P] the permutation (written by the tile-0 gate/up units)
-    int32_t* chunks;           // chunk records (expert, first sorted position, pairs, rank of the first pair)
-    int32_t* nchunks;
-    int32_t E, T, P;
+    const int32_t* sorted;     // [P] the permutation (pair ids in expert order)
+    const int32_t* chunks;     // global chunk list (expert, first sorted position, pairs, 0)
+    const int32_t* nchunks;
     int32_t ntg, ntd;          // column tiles per chunk: gate/up, down
     int32_t spin_limit;        // poll rounds before a wait gives up; < 0: every wait gives up at once
     const int32_t* xtab;       // per-XCD chunk table (ticketed form)
@@ -130,87 +123,6 @@ __device__ __forceinline__ bool await(const FusedArgs& f, const int32_t* p, int3
     return __builtin_amdgcn_readfirstlane(*s_flag) != 0;
 }
 
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    return v;
-}
-
-// Exclusive scan of one value per thread over the 256-thread workgroup;
-// *total gets the sum.  s_tmp: 4 ints of LDS.
-__device__ __forceinline__ int block_excl_scan(int v, int* s_tmp, int* total) {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int incl = wave_incl_scan(v, lane);
-    if (lane == kWave - 1) s_tmp[wave] = incl;
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
-        const int t = s_tmp[w];
-        before += w < wave ? t : 0;
-        all += t;
-    }
-    __syncthreads();
-    *total = all;
-    return before + incl - v;
-}
-
-// The pairs of expert blockIdx.x in ascending order.  Thread i owns the
-// contiguous ids [i*Q, i*Q + Q): it counts its matches, an exclusive scan
-// over the threads gives its first rank, and it writes its matches in
-// order.  The last workgroup to finish (the counter) then builds the expert
-// offsets and the chunk list from all counts: thread i takes experts 2i and
-// 2i + 1 (E <= 512).
-__global__ __launch_bounds__(kThreads) void k_expert_lists(FusedArgs f) {
-    __shared__ int32_t s_tmp[4], s_last;
-    const int e = blockIdx.x;
-    const int Q = (f.P + kThreads - 1) / kThreads;
-    const int p0 = threadIdx.x * Q, p1 = min(p0 + Q, f.P);
-    int n = 0;
-    for (int p = p0; p < p1; ++p) n += f.ids[p] == e;
-    int total;
-    int at = block_excl_scan(n, s_tmp, &total);
-    int32_t* list = f.lists + (size_t)e * f.T;
-    for (int p = p0; p < p1; ++p)
-        if (f.ids[p] == e) list[at++] = p;
-    if (threadIdx.x == 0) f.counts[e] = total;
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));        // vmcnt(0): this wave's stores done
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const int done = __hip_atomic_fetch_add(f.ctl + kScanDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == f.E - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_last = done == f.E - 1;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
-    const int n0 = e0 < f.E ? f.counts[e0] : 0, n1 = e1 < f.E ? f.counts[e1] : 0;
-    const int c0 = (n0 + kChunk - 1) / kChunk, c1 = (n1 + kChunk - 1) / kChunk;
-    int npairs, nch;
-    const int off = block_excl_scan(n0 + n1, s_tmp, &npairs);
-    const int coff = block_excl_scan(c0 + c1, s_tmp, &nch);
-    auto emit = [&](int ex, int nx, int first_pos, int first_chunk) {
-        f.offsets[ex] = first_pos;
-        for (int c = 0; c * kChunk < nx; ++c) {
-            int32_t* rec = f.chunks + kChunkRec * (first_chunk + c);
-            rec[0] = ex;
-            rec[1] = first_pos + c * kChunk;
-            rec[2] = min(kChunk, nx - c * kChunk);
-            rec[3] = c * kChunk;
-        }
-    };
-    if (e0 < f.E) emit(e0, n0, off, coff);
-    if (e1 < f.E) emit(e1, n1, off + n0, coff + c0);
-    if (threadIdx.x == 0) {
-        f.offsets[f.E] = npairs;
-        *f.nchunks = nch;
-    }
-}
-
 template <int RT, int DG, int DD>
 __global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
     constexpr int kRing = DG > DD ? DG : DD;
@@ -233,10 +145,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
         const int e = __builtin_amdgcn_readfirstlane(rec[0]);
         const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
         const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
-        const int first = __builtin_amdgcn_readfirstlane(rec[3]);
-        const int32_t* pairs = f.lists + (size_t)e * f.T + first;
-        if (nt == 0 && (int)threadIdx.x < rows) f.sorted[m0 + threadIdx.x] = pairs[threadIdx.x];
-        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, pairs, m0, rows, [] {});
+        // the chunk's pairs sit at sorted positions m0 .. m0 + rows - 1
+        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, f.sorted + m0, m0, rows, [] {});
         publish(f.ctl + kChunkDone + kLine * chunk);
         __syncthreads();               // the LDS ring is free again
     }
@@ -255,10 +165,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
         const int e = __builtin_amdgcn_readfirstlane(rec[0]);
         const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
         const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
-        const int first = __builtin_amdgcn_readfirstlane(rec[3]);
-        const int32_t* pairs = f.lists + (size_t)e * f.T + first;
         if (!await(f, f.ctl + kChunkDone + kLine * chunk, f.ntg, &s_flag)) return;
-        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, pairs, m0, rows, take);
+        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, f.sorted + m0, m0, rows, take);
         if (threadIdx.x == 0) s_next = next;
         __syncthreads();               // s_next holds the next unit; the LDS ring is free again
         v = __builtin_amdgcn_readfirstlane(s_next);
@@ -342,7 +250,7 @@ hipError_t launch_variant(const FusedArgs& f, int items, hipStream_t s) {
 
 int fused_ctl_ints(const Dims& dm) { return fused::kChunkDone + fused::kLine * max_chunks(dm); }
 
-bool fused_supported(const Dims& dm) { return dm.P <= kFusedMaxPairs && dm.E <= 2 * stream::kThreads; }
+bool fused_supported(const Dims& dm) { return dm.P <= kFusedMaxPairs; }
 
 namespace fused {
 namespace {
@@ -361,10 +269,8 @@ FusedArgs make_args(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& d
     f.dn.w0 = w.w_down; f.dn.s0 = w.w_down_scale;
     f.dn.o_out = ws.o;
     f.dn.K = dm.f; f.dn.N = dm.d; f.dn.k_top = dm.k; f.dn.ldo = dm.d;
-    f.ids = ws.topk_ids;
-    f.ctl = ws.fctl; f.counts = ws.fcounts; f.lists = ws.flists;
-    f.offsets = ws.offsets; f.sorted = ws.sorted_pairs; f.chunks = ws.chunks; f.nchunks = ws.nchunks;
-    f.E = dm.E; f.T = dm.T; f.P = dm.P;
+    f.ctl = ws.fctl;
+    f.sorted = ws.sorted_pairs; f.chunks = ws.chunks; f.nchunks = ws.nchunks;
     f.ntg = RT == 2 ? col_tiles<kGateUp, 2>(dm.f) : col_tiles<kGateUp, 4>(dm.f);
     f.ntd = RT == 2 ? col_tiles<kDown, 2>(dm.d) : col_tiles<kDown, 4>(dm.d);
     f.gu.n_tiles = f.ntg;
@@ -378,12 +284,6 @@ FusedArgs make_args(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& d
 }  // namespace
 }  // namespace fused
 
-hipError_t launch_fused_lists(const Dims& dm, const Workspace& ws, hipStream_t s) {
-    const moe_mxfp4_weights none{};
-    const fused::FusedArgs f = fused::make_args(nullptr, none, dm, ws, 0);
-    hipLaunchKernelGGL(fused::k_expert_lists, dim3(dm.E), dim3(stream::kThreads), 0, s, f);
-    return hipGetLastError();
-}
 
 // The ticketed form wins where experts have several pairs (256 tokens:
 // 138 against 151 us for the persistent kernel, 145 for the per-phase
