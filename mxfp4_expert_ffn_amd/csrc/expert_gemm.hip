@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a
     const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
     if (slot >= __builtin_amdgcn_readfirstlane(*count)) return;     // uniform per workgroup
     // the chunk's pairs sit at sorted positions start .. start + rows - 1
-    run_unit<MODE, RT, D>(a, lds, e, nt, a.sorted + start, start, rows, [] {});
+    run_unit<MODE, RT, D>(a, lds, e, nt, a.sorted + start, start, rows, [] {}, [] {});
 }
 
 template <int MODE, int RT>

@@ -25,15 +25,15 @@
 // 런타임"; dothoosh.com article, section "TileRT: عصر فشار بر GPU").  On gfx950
 // the same idea takes this form:
 //
-//   - k_fused (as many workgroups as the GPU holds at once): workgroup b
-//     first runs the gate/up units (chunk, column tile) b, b + G, b + 2G, ...
-//     -- a fixed assignment, no queue atomics, and a gate/up unit never
-//     waits -- and then takes down units from a queue (one atomic per unit)
-//     in chunk order, so the workgroups that finish gate/up first take the
-//     down work of the chunks that finished first.  A down unit of chunk c
-//     waits only for the gate/up units of chunk c (a counter per chunk),
-//     which resident workgroups finish without waiting on anything.  Down
-//     work starts while gate/up still streams the weights of later chunks.
+//   - k_fused (as many workgroups as the GPU holds at once): every
+//     workgroup takes units from one queue (one atomic per unit, taken a
+//     unit ahead): first the gate/up units (chunk, column tile), then the
+//     down units in chunk order, so the workgroups that finish gate/up first
+//     take the down work of the chunks that finished first.  A down unit of
+//     chunk c waits only for the gate/up units of chunk c (a counter per
+//     chunk), which running workgroups hold and finish without waiting on
+//     anything.  Down work starts while gate/up still streams the weights of
+//     later chunks.
 //   - Every wait is bounded: past the limit the kernel raises an error word
 //     in the workspace and its workgroups exit normally (a grid larger than
 //     what the GPU holds, for example because another kernel occupies it,
@@ -135,40 +135,47 @@ __global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
     int32_t& s_next = *reinterpret_cast<int32_t*>(lds + kRing * kSlot + sizeof(int32_t));
     const int nc = __builtin_amdgcn_readfirstlane(*f.nchunks);
     const int nG = nc * f.ntg, nD = nc * f.ntd;
-    // Gate/up units u = b, b + G, ... (never waiting), then down units from
-    // the down queue in chunk order, so a workgroup that finishes its gate/up
-    // work early takes the down work whose chunks finished first.  Two loops
-    // keep the two pipelines' registers apart.
-    for (int u = blockIdx.x; u < nG; u += gridDim.x) {
-        const int chunk = u / f.ntg, nt = u % f.ntg;
+    // One queue hands out every unit: tickets 0 .. nG-1 are the gate/up
+    // units (chunk-major), then the down units in chunk order.  Each
+    // workgroup takes its next ticket once the current unit has issued its
+    // last weight loads (lane 0; handed over through LDS at the end), so
+    // the queue's latency runs under the unit's last steps.  A down unit waits only for gate/up units
+    // of its chunk, and a workgroup sees a ticket past the gate/up units
+    // only after every gate/up ticket went to a running workgroup: every
+    // wait ends, however many workgroups the GPU holds at once (another
+    // kernel may occupy part of it).  Two loops keep the two pipelines'
+    // registers apart.
+    if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(f.ctl + kDownQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int v = __builtin_amdgcn_readfirstlane(s_next);
+    int next = 0;
+    auto take = [&] {
+        if (threadIdx.x == 0) next = __hip_atomic_fetch_add(f.ctl + kDownQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    while (v < nG) {
+        const int chunk = v / f.ntg, nt = v % f.ntg;
         const int32_t* rec = f.chunks + kChunkRec * chunk;
         const int e = __builtin_amdgcn_readfirstlane(rec[0]);
         const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
         const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
         // the chunk's pairs sit at sorted positions m0 .. m0 + rows - 1
-        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, f.sorted + m0, m0, rows, [] {});
+        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, f.sorted + m0, m0, rows, [] {}, take);
         publish(f.ctl + kChunkDone + kLine * chunk);
-        __syncthreads();               // the LDS ring is free again
+        if (threadIdx.x == 0) s_next = next;
+        __syncthreads();               // s_next holds the next ticket; the LDS ring is free again
+        v = __builtin_amdgcn_readfirstlane(s_next);
     }
-    if (threadIdx.x == 0) s_next = __hip_atomic_fetch_add(f.ctl + kDownQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    int v = __builtin_amdgcn_readfirstlane(s_next);
-    int next = 0;
-    // the next down unit is taken right before this one's first loads, and
-    // its index handed over through LDS at the end
-    auto take = [&] {
-        if (threadIdx.x == 0) next = __hip_atomic_fetch_add(f.ctl + kDownQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    while (v < nD) {
-        const int chunk = v / f.ntd, nt = v % f.ntd;
+    while (v < nG + nD) {
+        const int w = v - nG;
+        const int chunk = w / f.ntd, nt = w % f.ntd;
         const int32_t* rec = f.chunks + kChunkRec * chunk;
         const int e = __builtin_amdgcn_readfirstlane(rec[0]);
         const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
         const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
         if (!await(f, f.ctl + kChunkDone + kLine * chunk, f.ntg, &s_flag)) return;
-        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, f.sorted + m0, m0, rows, take);
+        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, f.sorted + m0, m0, rows, [] {}, take);
         if (threadIdx.x == 0) s_next = next;
-        __syncthreads();               // s_next holds the next unit; the LDS ring is free again
+        __syncthreads();               // s_next holds the next ticket; the LDS ring is free again
         v = __builtin_amdgcn_readfirstlane(s_next);
     }
 }
@@ -208,11 +215,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain(FusedArgs f) {
     const int chunk = __builtin_amdgcn_readfirstlane(rec[3]);
     // the chunk's pairs sit at sorted positions start .. start + rows - 1
     if (gateup) {
-        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, f.sorted + start, start, rows, [] {});
+        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, f.sorted + start, start, rows, [] {}, [] {});
         publish(f.ctl + kChunkDone + kLine * chunk);
     } else {
         if (!await(f, f.ctl + kChunkDone + kLine * chunk, f.ntg, &s_flag)) return;
-        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, f.sorted + start, start, rows, [] {});
+        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, f.sorted + start, start, rows, [] {}, [] {});
     }
 }
 

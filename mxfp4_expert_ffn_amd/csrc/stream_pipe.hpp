@@ -247,10 +247,15 @@ struct Pipe {
     // t*k + j; m0 is the chunk's first row in expert-sorted order (the rows of
     // h).  Gate/up reads x rows pairs[i] / k and writes h rows m0 + i; down
     // reads h rows m0 + i and writes o rows pairs[i].
-    // pre() runs right before the first loads of the pipeline are issued.
-    template <typename Pre>
+    // pre() runs right before the first loads of the pipeline are issued,
+    // late() right after its last weight loads (before the last D steps,
+    // which issue no weights: a memory operation started there has those
+    // steps to complete before the unit ends; vector-memory operations
+    // complete in order, so one issued before the first loads would hold up
+    // the first step instead).
+    template <typename Pre, typename Late>
     __device__ static void run(const GemmArgs& a, uint8_t* lds, int e, int nt, const int32_t* pairs, int m0, int M,
-                               Pre&& pre) {
+                               Pre&& pre, Late&& late) {
         const int tid = threadIdx.x, lane = tid % kWave;
         const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
         const int li = lane % 16, g = lane / 16;
@@ -320,6 +325,8 @@ struct Pipe {
 
         int s = 0;
         for (; s < n - D; s += D) steps<0, false>(c, acc, w, sg, s, li, g);
+        late();
+        pin();
         steps<0, true>(c, acc, w, sg, s, li, g);
 
         // Epilogue.  Lane holds D[token 4g + r][column li] of every (ms, rt).
@@ -353,15 +360,16 @@ struct Pipe {
 };
 
 // One unit with the sub-tile count MS picked from the chunk's pair count;
-// pre() runs right before the pipeline's first loads.
-template <int MODE, int RT, int D, bool H_COHERENT = false, typename Pre>
+// pre() runs right before the pipeline's first loads, late() right after
+// its last weight loads.
+template <int MODE, int RT, int D, bool H_COHERENT = false, typename Pre, typename Late>
 __device__ __forceinline__ void run_unit(const GemmArgs& a, uint8_t* lds, int e, int nt, const int32_t* pairs,
-                                         int m0, int rows, Pre&& pre) {
+                                         int m0, int rows, Pre&& pre, Late&& late) {
     switch (min(kMaxMs, (rows + 15) / 16)) {
-        case 1: Pipe<MODE, RT, 1, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre); break;
-        case 2: Pipe<MODE, RT, 2, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre); break;
-        case 3: Pipe<MODE, RT, 3, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre); break;
-        default: Pipe<MODE, RT, 4, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre); break;
+        case 1: Pipe<MODE, RT, 1, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre, late); break;
+        case 2: Pipe<MODE, RT, 2, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre, late); break;
+        case 3: Pipe<MODE, RT, 3, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre, late); break;
+        default: Pipe<MODE, RT, 4, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre, late); break;
     }
 }
 

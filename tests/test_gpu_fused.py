@@ -199,3 +199,32 @@ def test_fused_repeated_calls_are_bit_identical(monkeypatch):
         torch.cuda.synchronize()
         assert torch.equal(y, y0), i
     assert fused_l.device_status(w.T) == 0
+
+
+@pytest.mark.parametrize("T,E,k", [(8, 64, 8), (96, 16, 4)])     # persistent form (P <= E), ticketed form
+def test_fused_calls_on_two_streams_at_once(monkeypatch, T, E, k):
+    # two calls in flight together on distinct workspaces: each kernel's
+    # units are handed out to running workgroups only, so neither waits on
+    # work that the other's workgroups keep from starting
+    w = synth.Workload("fzs", T, 512, 1024, E, k, "bf16", "normal", 915)
+    acts = synth.make_activations(w)
+    wts = problems.pack_experts(w)
+    stream_l, fused_l = _layers(monkeypatch, problems.to_device(wts), w, w.T, 1)
+    x = torch.from_numpy(acts["x_bf16"].view(np.int16)).cuda().view(torch.bfloat16)
+    lg = torch.from_numpy(acts["logits"]).cuda()
+    y_ref = stream_l(x, lg).clone()
+    nbytes = fused_l.workspace_bytes(w.T)
+    ws = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    outs = [torch.empty((w.T, w.d), dtype=torch.float32, device="cuda") for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    print(f"fused: two streams, T={T} E={E} k={k}", flush=True)
+    for _ in range(6):
+        for st, wsp, out in zip(streams, ws, outs):
+            with torch.cuda.stream(st):
+                fused_l(x, lg, out=out, workspace=wsp)
+    torch.cuda.synchronize()
+    for wsp, out in zip(ws, outs):
+        assert fused_l.device_status(w.T, workspace=wsp) == 0
+        assert torch.equal(out, y_ref)
