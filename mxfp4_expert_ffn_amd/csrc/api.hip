@@ -64,7 +64,7 @@ Layout make_layout(const moe_mxfp4_config& c, int64_t T) {
     moe::Dims dm{(int32_t)T, c.d_model, c.d_ff, c.num_experts, c.top_k, (int32_t)P};
     L.chunks = at;  at += round256((size_t)moe::max_chunks(dm) * moe::kChunkRec * sizeof(int32_t));
     L.nchunks = at; at += 256;
-    L.xtab = at;    at += round256(((size_t)moe::kXtabHead + (size_t)moe::kXcds * moe::xcd_slots(dm) * moe::kChunkRec) *
+    L.xtab = at;    at += round256(((size_t)moe::kXtabHead + (size_t)moe::kXcds * moe::xcd_slots(dm) * moe::kXtabRec) *
                                    sizeof(int32_t));
     L.sort_part = at; at += round256((size_t)moe::sort_tiles((int)P) * c.num_experts * sizeof(int32_t));
     const bool mx8 = c.act_mode == MOE_ACT_MXFP8_E4M3;

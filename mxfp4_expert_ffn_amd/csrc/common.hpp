@@ -95,7 +95,7 @@ struct Workspace {
                               //   sorted_pairs, pairs in the chunk, 0)
     int32_t* nchunks;         // [1] number of chunks
     int32_t* xtab;            // per-XCD chunk table: [kXtabHead] chunks per XCD (kXcds used),
-                              //   then [kXcds][xcd_slots(dm)] chunk records
+                              //   then [kXcds][xcd_slots(dm)] records of kXtabRec ints
     int32_t* sort_part;       // [sort_tiles(P)][E] per-tile expert histograms / first positions
     uint8_t* xq;              // MXFP8 mode: [T][d] E4M3 codes of x
     uint8_t* xs;              // MXFP8 mode: [T][d/32] E8M0 scales of x
@@ -139,9 +139,49 @@ inline int max_chunks(const Dims& dm) {
 // which bounds the table's slots.
 constexpr int kXcds = 8;
 constexpr int kXtabHead = 64;      // ints before the records
+// Table record: expert, position of the chunk's first pair in sorted_pairs,
+// pairs in the chunk, the chunk's index in the global list, the chunk's
+// index among its expert's chunks, the expert's chunk count, 2 unused.
+constexpr int kXtabRec = 8;
 inline int xcd_slots(const Dims& dm) {
     const int T = dm.T < dm.P ? dm.T : dm.P;
     return (max_chunks(dm) + kXcds - 1) / kXcds + (T + kChunk - 1) / kChunk;
+}
+
+// Work unit u of XCD x's list, with nt_per column tiles per chunk
+// (u < xstride * nt_per); false for a unit past the list's end.  An
+// expert's m chunks fill m consecutive slots, hence units [s * nt_per,
+// (s + m) * nt_per) of the list, which run column tile by column tile: the
+// m units of one weight tile are neighbours, start together on the XCD and
+// share that tile's fetch through its L2 (chunk by chunk instead, a hot
+// expert's later chunks fetch its weights again).  The list's length and
+// the slot's record are read together, so a single-chunk expert's unit
+// waits on one round trip.
+struct XcdUnit {
+    int e, start, rows, chunk, nt;
+};
+__device__ __forceinline__ bool xcd_unit(const int32_t* xtab, int xstride, int x, int u, int nt_per, XcdUnit& w) {
+    const int32_t* list = xtab + kXtabHead + (size_t)kXtabRec * x * xstride;
+    const int q = u / nt_per;
+    const int32_t* r = list + kXtabRec * q;
+    const int n = __builtin_amdgcn_readfirstlane(xtab[x]);
+    w.e = __builtin_amdgcn_readfirstlane(r[0]);
+    w.start = __builtin_amdgcn_readfirstlane(r[1]);
+    w.rows = __builtin_amdgcn_readfirstlane(r[2]);
+    w.chunk = __builtin_amdgcn_readfirstlane(r[3]);
+    const int pos = __builtin_amdgcn_readfirstlane(r[4]);
+    const int m = __builtin_amdgcn_readfirstlane(r[5]);
+    w.nt = u - q * nt_per;
+    if (q >= n) return false;                   // (the record is then stale and unused)
+    if (m > 1) {
+        const int v = u - (q - pos) * nt_per;   // unit within the expert's group
+        w.nt = v / m;
+        r = list + kXtabRec * (q - pos + (v - w.nt * m));
+        w.start = __builtin_amdgcn_readfirstlane(r[1]);
+        w.rows = __builtin_amdgcn_readfirstlane(r[2]);
+        w.chunk = __builtin_amdgcn_readfirstlane(r[3]);
+    }
+    return true;
 }
 
 // The fused path (bf16 activations): the routing launch clears the

@@ -14,31 +14,27 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a
     // Work unit = (chunk, column tile).  With a per-XCD table (batches of
     // more pairs than experts), workgroup g runs on XCD g mod kXcds (the
     // GPU's round-robin) and takes the units of that XCD's chunk list in
-    // order; otherwise unit g of the global list.  Both are chunk-major: the
-    // column tiles of a chunk (same activation rows) are adjacent, and so are
-    // the chunks of an expert, hottest expert first.  The record and the
-    // chunk count are read together, so the weight loads wait on one round
-    // trip; workgroup-uniform values are kept in scalar registers so that the
-    // buffer descriptors built from them are scalar too.
-    const int* rec;
-    const int* count;
-    int slot, nt;
+    // order (xcd_unit: a hot expert's chunks interleaved by column tile);
+    // otherwise unit g of the global list, chunk-major: the column tiles of
+    // a chunk (same activation rows) are adjacent, hottest expert first.
+    // The record and the chunk count are read together, so the weight loads
+    // wait on one round trip; workgroup-uniform values are kept in scalar
+    // registers so that the buffer descriptors built from them are scalar
+    // too.
+    int e, start, rows, nt;
     if (a.xtab) {
-        const int x = blockIdx.x % kXcds;
-        slot = blockIdx.x / kXcds / a.n_tiles;
-        nt = blockIdx.x / kXcds % a.n_tiles;
-        rec = a.xtab + kXtabHead + kChunkRec * (x * a.xstride + slot);
-        count = a.xtab + x;
+        XcdUnit w;
+        if (!xcd_unit(a.xtab, a.xstride, blockIdx.x % kXcds, blockIdx.x / kXcds, a.n_tiles, w)) return;
+        e = w.e; start = w.start; rows = w.rows; nt = w.nt;
     } else {
-        slot = blockIdx.x / a.n_tiles;
+        const int slot = blockIdx.x / a.n_tiles;
         nt = blockIdx.x % a.n_tiles;
-        rec = a.chunks + kChunkRec * slot;
-        count = a.nchunks;
+        const int* rec = a.chunks + kChunkRec * slot;
+        e = __builtin_amdgcn_readfirstlane(rec[0]);
+        start = __builtin_amdgcn_readfirstlane(rec[1]);
+        rows = __builtin_amdgcn_readfirstlane(rec[2]);
+        if (slot >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;     // uniform per workgroup
     }
-    const int e = __builtin_amdgcn_readfirstlane(rec[0]);
-    const int start = __builtin_amdgcn_readfirstlane(rec[1]);
-    const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
-    if (slot >= __builtin_amdgcn_readfirstlane(*count)) return;     // uniform per workgroup
     // the chunk's pairs sit at sorted positions start .. start + rows - 1
     run_unit<MODE, RT, D>(a, lds, e, nt, a.sorted + start, start, rows, [] {}, [] {});
 }

@@ -184,7 +184,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_fused(FusedArgs f) {
 // ticket of counter b mod kXcds (so each counter serves exactly its share of
 // the grid whatever the dispatch order) and runs unit `ticket` of that
 // XCD's list in the per-XCD chunk table: first the gate/up units of its
-// chunks (chunk-major), then their down units in the same order.  A down
+// chunks, then their down units in the same order (xcd_unit: expert by
+// expert, a hot expert's chunks interleaved by column tile).  A down
 // unit waits only for gate/up units of its chunk, which sit earlier in the
 // same list: their tickets were taken first, by workgroups that are running
 // or done and never wait, so every wait ends.  With the GPU's round-robin
@@ -205,21 +206,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain(FusedArgs f) {
     const int nG = nslots * f.ntg, nD = nslots * f.ntd;
     const bool gateup = t < nG;
     if (!gateup && t - nG >= nD) return;                 // past the list: nothing to do
-    const int u = gateup ? t : t - nG;
-    const int nt_per = gateup ? f.ntg : f.ntd;
-    const int32_t* rec = f.xtab + kXtabHead + kChunkRec * (x * f.xstride + u / nt_per);
-    const int nt = u % nt_per;
-    const int e = __builtin_amdgcn_readfirstlane(rec[0]);
-    const int start = __builtin_amdgcn_readfirstlane(rec[1]);
-    const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
-    const int chunk = __builtin_amdgcn_readfirstlane(rec[3]);
-    // the chunk's pairs sit at sorted positions start .. start + rows - 1
+    XcdUnit w;
+    xcd_unit(f.xtab, f.xstride, x, gateup ? t : t - nG, gateup ? f.ntg : f.ntd, w);   // t < nG + nD: in the list
+    // the chunk's pairs sit at sorted positions w.start .. w.start + w.rows - 1
     if (gateup) {
-        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, e, nt, f.sorted + start, start, rows, [] {}, [] {});
-        publish(f.ctl + kChunkDone + kLine * chunk);
+        stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, w.e, w.nt, f.sorted + w.start, w.start, w.rows, [] {},
+                                                [] {});
+        publish(f.ctl + kChunkDone + kLine * w.chunk);
     } else {
-        if (!await(f, f.ctl + kChunkDone + kLine * chunk, f.ntg, &s_flag)) return;
-        stream::run_unit<kDown, RT, DD>(f.dn, lds, e, nt, f.sorted + start, start, rows, [] {}, [] {});
+        if (!await(f, f.ctl + kChunkDone + kLine * w.chunk, f.ntg, &s_flag)) return;
+        stream::run_unit<kDown, RT, DD>(f.dn, lds, w.e, w.nt, f.sorted + w.start, w.start, w.rows, [] {}, [] {});
     }
 }
 

@@ -409,12 +409,14 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
         const int a = xasg[tid], x = a >> 24, slot = a & 0xFFFFFF;
         const int e = act[tid], n = counts[e];
         const int m = (n + chunk_rows - 1) / chunk_rows;
-        int32_t* rec = xtab + kXtabHead + kChunkRec * ((size_t)x * xstride + slot);
+        int32_t* rec = xtab + kXtabHead + kXtabRec * ((size_t)x * xstride + slot);
         for (int q = 0; q < m; ++q) {
-            rec[kChunkRec * q + 0] = e;
-            rec[kChunkRec * q + 1] = exoff[e] + q * chunk_rows;
-            rec[kChunkRec * q + 2] = min(chunk_rows, n - q * chunk_rows);
-            rec[kChunkRec * q + 3] = rnk[tid] + q;    // the chunk's index in the global list
+            rec[kXtabRec * q + 0] = e;
+            rec[kXtabRec * q + 1] = exoff[e] + q * chunk_rows;
+            rec[kXtabRec * q + 2] = min(chunk_rows, n - q * chunk_rows);
+            rec[kXtabRec * q + 3] = rnk[tid] + q;    // the chunk's index in the global list
+            rec[kXtabRec * q + 4] = q;
+            rec[kXtabRec * q + 5] = m;
         }
     }
     return tid < E ? excl : 0;
@@ -582,11 +584,13 @@ __device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, in
         // per-XCD table (the layout of expert_lists): one chunk per expert,
         // so the greedy assignment deals rank r to XCD r mod kXcds, slot
         // r / kXcds
-        int32_t* xr = xtab + kXtabHead + kChunkRec * ((size_t)(r % kXcds) * xstride + r / kXcds);
+        int32_t* xr = xtab + kXtabHead + kXtabRec * ((size_t)(r % kXcds) * xstride + r / kXcds);
         xr[0] = lane;
         xr[1] = excl;
         xr[2] = c;
         xr[3] = r;
+        xr[4] = 0;
+        xr[5] = 1;
     }
     if (lane < kXcds) xtab[lane] = na / kXcds + (lane < na % kXcds);
     if (lane == 0) {
