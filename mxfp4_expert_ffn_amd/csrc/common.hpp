@@ -158,7 +158,7 @@ inline int xcd_slots(const Dims& dm) {
 // the slot's record are read together, so a single-chunk expert's unit
 // waits on one round trip.
 struct XcdUnit {
-    int e, start, rows, chunk, nt;
+    int e, start, rows, chunk, nt, m;    // m: the expert's chunks
 };
 __device__ __forceinline__ bool xcd_unit(const int32_t* xtab, int xstride, int x, int u, int nt_per, XcdUnit& w) {
     const int32_t* list = xtab + kXtabHead + (size_t)kXtabRec * x * xstride;
@@ -171,6 +171,7 @@ __device__ __forceinline__ bool xcd_unit(const int32_t* xtab, int xstride, int x
     w.chunk = __builtin_amdgcn_readfirstlane(r[3]);
     const int pos = __builtin_amdgcn_readfirstlane(r[4]);
     const int m = __builtin_amdgcn_readfirstlane(r[5]);
+    w.m = m;
     w.nt = u - q * nt_per;
     if (q >= n) return false;                   // (the record is then stale and unused)
     if (m > 1) {

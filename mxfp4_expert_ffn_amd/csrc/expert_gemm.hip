@@ -22,10 +22,11 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a
     // registers so that the buffer descriptors built from them are scalar
     // too.
     int e, start, rows, nt;
+    bool shared = false;
     if (a.xtab) {
         XcdUnit w;
         if (!xcd_unit(a.xtab, a.xstride, blockIdx.x % kXcds, blockIdx.x / kXcds, a.n_tiles, w)) return;
-        e = w.e; start = w.start; rows = w.rows; nt = w.nt;
+        e = w.e; start = w.start; rows = w.rows; nt = w.nt; shared = w.m > 1;
     } else {
         const int slot = blockIdx.x / a.n_tiles;
         nt = blockIdx.x % a.n_tiles;
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 2 : 3) void k_expert(GemmArgs a
         if (slot >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;     // uniform per workgroup
     }
     // the chunk's pairs sit at sorted positions start .. start + rows - 1
-    run_unit<MODE, RT, D>(a, lds, e, nt, a.sorted + start, start, rows, [] {}, [] {});
+    run_unit<MODE, RT, D>(a, lds, e, nt, a.sorted + start, start, rows, [] {}, [] {}, shared);
 }
 
 template <int MODE, int RT>

@@ -211,11 +211,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain(FusedArgs f) {
     // the chunk's pairs sit at sorted positions w.start .. w.start + w.rows - 1
     if (gateup) {
         stream::run_unit<kGateUp, RT, DG, true>(f.gu, lds, w.e, w.nt, f.sorted + w.start, w.start, w.rows, [] {},
-                                                [] {});
+                                                [] {}, w.m > 1);
         publish(f.ctl + kChunkDone + kLine * w.chunk);
     } else {
         if (!await(f, f.ctl + kChunkDone + kLine * w.chunk, f.ntg, &s_flag)) return;
-        stream::run_unit<kDown, RT, DD>(f.dn, lds, w.e, w.nt, f.sorted + w.start, w.start, w.rows, [] {}, [] {});
+        stream::run_unit<kDown, RT, DD>(f.dn, lds, w.e, w.nt, f.sorted + w.start, w.start, w.rows, [] {}, [] {},
+                                        w.m > 1);
     }
 }
 

@@ -67,8 +67,12 @@ constexpr int kRsrcWord3 = 0x00020000;         // gfx9 raw buffer descriptor, dw
 // Cache policy of the weight loads: nt (non-temporal).  Each weight byte is
 // streamed once per chunk, so it should not displace the activation rows
 // the column tiles share; measured 3-14% faster than the default policy
-// (and setting it on the small scale loads as well was slower).
+// (and setting it on the small scale loads as well was slower).  The
+// chunks of an expert with several chunks load with the default policy
+// instead (kSharedWeightAux): their units of one weight tile run together
+// (xcd_unit), and nt lines leave the L2 before the later units read them.
 constexpr int kWeightAux = 2;
+constexpr int kSharedWeightAux = 0;
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -119,7 +123,7 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* src, uint8_t* lds) {
 // H_COHERENT: gate/up stores h with agent-scope (device-coherent) stores,
 // which another workgroup may read during the same launch once this one has
 // waited for them; otherwise plain stores (read by a later launch).
-template <int MODE, int RT, int MS, int D, bool H_COHERENT = false>
+template <int MODE, int RT, int MS, int D, bool H_COHERENT = false, int WAUX = kWeightAux>
 struct Pipe {
     static constexpr int kHalf = MODE == kGateUp ? RT / 2 : RT;
     static constexpr int kColsPerWave = kHalf * 16;
@@ -153,7 +157,7 @@ struct Pipe {
             const int mat = (MODE == kGateUp && rt >= kHalf) ? 1 : 0;
             const int tile = c.tile0 + rt % kHalf;
             w[rt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    c.rw[mat], c.lane16, (tile * c.ns + step) * 1024, kWeightAux));
+                                                    c.rw[mat], c.lane16, (tile * c.ns + step) * 1024, WAUX));
             sg[rt] = __builtin_amdgcn_raw_buffer_load_b32(c.rs[mat], c.lane4, (tile * c.ng + step / 4) * 256, 0);
         }
     }
@@ -361,10 +365,18 @@ struct Pipe {
 
 // One unit with the sub-tile count MS picked from the chunk's pair count;
 // pre() runs right before the pipeline's first loads, late() right after
-// its last weight loads.
+// its last weight loads.  shared: the expert has other chunks whose units
+// of the same weight tile run alongside; the unit then loads its weights
+// with kSharedWeightAux, in the full-chunk shape whatever its pair count
+// (one more body instead of four: rows past the chunk's last pair are
+// computed and never stored).
 template <int MODE, int RT, int D, bool H_COHERENT = false, typename Pre, typename Late>
 __device__ __forceinline__ void run_unit(const GemmArgs& a, uint8_t* lds, int e, int nt, const int32_t* pairs,
-                                         int m0, int rows, Pre&& pre, Late&& late) {
+                                         int m0, int rows, Pre&& pre, Late&& late, bool shared = false) {
+    if (shared) {
+        Pipe<MODE, RT, kMaxMs, D, H_COHERENT, kSharedWeightAux>::run(a, lds, e, nt, pairs, m0, rows, pre, late);
+        return;
+    }
     switch (min(kMaxMs, (rows + 15) / 16)) {
         case 1: Pipe<MODE, RT, 1, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre, late); break;
         case 2: Pipe<MODE, RT, 2, D, H_COHERENT>::run(a, lds, e, nt, pairs, m0, rows, pre, late); break;
