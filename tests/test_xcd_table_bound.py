@@ -5,7 +5,9 @@ chunks expert by expert.  The host
 sizes the table and the grid with ceil(max_chunks / 8) + ceil(T / 64) slots
 per XCD, max_chunks = min(E, P) + P // 64; this checks that no XCD's list
 ever needs more, over random routings and the extreme ones (every expert
-equally loaded, one expert taking every token, k = E)."""
+equally loaded, one expert taking every token, k = E), and that the order
+in which the kernels take a list's units (an expert's chunks interleaved
+column tile by column tile) runs every chunk's every tile exactly once."""
 import numpy as np
 import pytest
 
@@ -78,3 +80,37 @@ def test_extreme_routings_fit_the_slot_bound(T, E, k):
     for counts in (even, hot, tail):
         assert counts.sum() == T * k and counts.max() <= T
         assert slots_needed(counts, CHUNK).max() <= bound(T, E, k), (T, E, k)
+
+
+def unit_of(u, nt_per, group_pos, group_m):
+    """Work unit u of one XCD's list -> (slot, column tile), as the kernels
+    map it: slot q = u // nt_per carries its chunk's index among its
+    expert's chunks (pos) and their number (m); an expert's m chunks run
+    column tile by column tile."""
+    q = u // nt_per
+    pos, m = group_pos[q], group_m[q]
+    if m == 1:
+        return q, u - q * nt_per
+    v = u - (q - pos) * nt_per
+    nt = v // m
+    return q - pos + v % m, nt
+
+
+@pytest.mark.parametrize("nt_per", [1, 12, 16, 24])
+def test_unit_order_covers_every_chunk_and_tile_once(nt_per):
+    # every (slot, column tile) of a list is one unit, and the m chunks of an
+    # expert take adjacent units for each column tile
+    rng = np.random.default_rng(nt_per)
+    for _ in range(50):
+        ms = [int(x) for x in rng.choice([1, 1, 1, 2, 3, 5], size=int(rng.integers(1, 12)))]
+        pos = [p for m in ms for p in range(m)]
+        gm = [m for m in ms for _ in range(m)]
+        n = len(pos)
+        seen = [unit_of(u, nt_per, pos, gm) for u in range(n * nt_per)]
+        assert sorted(seen) == [(q, t) for q in range(n) for t in range(nt_per)]
+        first = 0
+        for m in ms:
+            units = seen[first * nt_per:(first + m) * nt_per]
+            for t in range(nt_per):
+                assert units[t * m:(t + 1) * m] == [(first + c, t) for c in range(m)]
+            first += m
