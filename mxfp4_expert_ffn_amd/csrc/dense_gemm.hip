@@ -66,6 +66,8 @@ struct DenseArgs {
     const int32_t* sorted;       // [P]
     const int32_t* chunks;       // chunk records
     const int32_t* nchunks;
+    const int32_t* xtab;         // per-XCD chunk table (xcd_unit)
+    int32_t xstride;
     uint8_t* h_out;              // gate/up: [P][f] E4M3
     uint8_t* h_scale_out;        // gate/up: [P][f/32]
     uint16_t* o_out;             // down: [P][d] fp16 codes, row = pair index
@@ -424,19 +426,16 @@ struct Dense {
 template <int MODE, int WN, int STAGES>
 __global__ __launch_bounds__((Shape<WN, STAGES>::kT), (Shape<WN, STAGES>::kPerCu)) void k_dense(DenseArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Shape<WN, STAGES>::kLds];
-    // Work unit = (chunk, column tile), chunk-major; chunks are listed
-    // expert by expert, hottest first.  Uniform values go to scalar
-    // registers so that the buffer descriptors built from them are scalar.
-    const int unit = blockIdx.x;
-    const int chunk = unit / a.n_tiles;
-    const int nt = unit % a.n_tiles;
-    // the record (inside the chunk list for every unit of the grid) is read
-    // together with the count, so the first loads wait on one round trip
-    const int* rec = a.chunks + kChunkRec * chunk;
-    const int e = __builtin_amdgcn_readfirstlane(rec[0]);
-    const int start = __builtin_amdgcn_readfirstlane(rec[1]);
-    const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
-    if (chunk >= __builtin_amdgcn_readfirstlane(*a.nchunks)) return;
+    // Work unit = (chunk, column tile) of the per-XCD chunk table: workgroup
+    // g runs on XCD g mod kXcds (the GPU's round-robin) and takes unit
+    // g / kXcds of that XCD's list, where each expert's 4-5 chunks run
+    // column tile by column tile (xcd_unit), so they share the weight tile,
+    // and its chunks their activation rows, through one L2.  Uniform values
+    // go to scalar registers so that the buffer descriptors built from them
+    // are scalar.
+    XcdUnit w;
+    if (!xcd_unit(a.xtab, a.xstride, blockIdx.x % kXcds, blockIdx.x / kXcds, a.n_tiles, w)) return;
+    const int e = w.e, start = w.start, rows = w.rows, nt = w.nt;
     // run() takes (first sorted position m0, chunk offset c0, pairs M) with
     // the chunk's pairs at m0 + c0 .. m0 + M - 1
     Dense<MODE, WN, STAGES>::run(a, smem, e, nt, start, 0, rows);
@@ -451,9 +450,14 @@ int max_dense_chunks(const Dims& dm) {
 // 2 x 2 wavefronts, two step buffers: the fastest shape measured (2 x 4
 // wavefronts and 3- or 4-deep rings leave one workgroup per CU).
 template <int MODE>
-hipError_t launch(const DenseArgs& a, int units, hipStream_t s) {
+hipError_t launch(DenseArgs a, const Dims& dm, hipStream_t s) {
     constexpr int WN = 2, ST = 2;
-    hipLaunchKernelGGL((k_dense<MODE, WN, ST>), dim3(units), dim3(Shape<WN, ST>::kT), 0, s, a);
+    a.xstride = xcd_slots(dm);
+    // slots an XCD's list can fill at kDenseChunk pairs per chunk (the
+    // greedy bound: an eighth of the chunks plus one expert's)
+    const int T = dm.T < dm.P ? dm.T : dm.P;
+    const int slots = (max_dense_chunks(dm) + kXcds - 1) / kXcds + (T + kDenseChunk - 1) / kDenseChunk;
+    hipLaunchKernelGGL((k_dense<MODE, WN, ST>), dim3(kXcds * slots * a.n_tiles), dim3(Shape<WN, ST>::kT), 0, s, a);
     return hipGetLastError();
 }
 
@@ -464,10 +468,10 @@ hipError_t launch_gateup_dense(const moe_mxfp4_weights& w, const Dims& dm, const
     a.act = ws.xq; a.act_scale = ws.xs; a.act_rows = (uint32_t)dm.T;
     a.w0 = w.w_gate; a.s0 = w.w_gate_scale;
     a.w1 = w.w_up;   a.s1 = w.w_up_scale;
-    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks; a.xtab = ws.xtab;
     a.h_out = ws.h; a.h_scale_out = ws.hs; a.o_out = nullptr;
     a.K = dm.d; a.N = dm.f; a.n_tiles = dm.f / 128; a.k_top = dm.k; a.ldo = dm.f;
-    return launch<kGateUp>(a, max_dense_chunks(dm) * a.n_tiles, s);
+    return launch<kGateUp>(a, dm, s);
 }
 
 hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws, hipStream_t s) {
@@ -475,11 +479,11 @@ hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const W
     a.act = ws.h; a.act_scale = ws.hs; a.act_rows = (uint32_t)dm.P;
     a.w0 = w.w_down; a.s0 = w.w_down_scale;
     a.w1 = nullptr;  a.s1 = nullptr;
-    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.sorted = ws.sorted_pairs; a.chunks = ws.chunks; a.nchunks = ws.nchunks; a.xtab = ws.xtab;
     a.h_out = nullptr; a.h_scale_out = nullptr;
     a.o_out = reinterpret_cast<uint16_t*>(ws.o); a.o_scale_out = ws.os;
     a.K = dm.f; a.N = dm.d; a.n_tiles = dm.d / 256; a.k_top = dm.k; a.ldo = dm.d;
-    return launch<kDown>(a, max_dense_chunks(dm) * a.n_tiles, s);
+    return launch<kDown>(a, dm, s);
 }
 
 }  // namespace moe
