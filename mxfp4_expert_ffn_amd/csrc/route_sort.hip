@@ -369,10 +369,11 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
     // holds at most floor(nchunks / kXcds) plus one expert's chunks.  Equal
     // counts come in runs, and greedy deals a run to the XCDs at the lowest
     // load one each, in index order, before any load above it: so wave 0
-    // places up to kXcds experts per round (lane x < kXcds holds XCD x's
-    // load, lane i the count of rank r0 + i of the current block of ranks).
-    // keys[] (free after the ranking) receives each rank's
-    // (XCD << 24 | first slot).
+    // places the experts in rounds, one expert per XCD at the lowest load,
+    // or whole levels of a run when every XCD is at the lowest load (lane
+    // x < kXcds holds XCD x's load, lane i the count of rank r0 + i of the
+    // current block of ranks).  keys[] (free after the ranking) receives
+    // each rank's (XCD << 24 | first slot).
     int32_t* xasg = reinterpret_cast<int32_t*>(keys);
     if (wave == 0) {
         int load = 0;                                   // lane x < kXcds: XCD x's chunks so far
@@ -392,8 +393,18 @@ __device__ int expert_lists(const int32_t* counts, uint64_t* keys, int32_t* act,
 #pragma unroll
                 for (int k = 1; k < kXcds; ++k) lo = min(lo, __builtin_amdgcn_readlane(load, k));
                 const uint64_t takers = __ballot(lane < kXcds && load == lo);
-                const int before = (int)__builtin_popcountll(takers & ((1ull << lane) - 1));   // lower-indexed takers
                 const int ntake = (int)__builtin_popcountll(takers);
+                if (ntake == kXcds && nrun >= kXcds) {
+                    // every XCD at the lowest load: greedy deals whole levels
+                    // of the run, item p to XCD p mod kXcds at load lo +
+                    // (p / kXcds) m, so place them in one round
+                    const int lv = nrun / kXcds, p = lane - pos;
+                    if (p >= 0 && p < lv * kXcds) xasg[r0 + lane] = ((p % kXcds) << 24) | (lo + (p / kXcds) * m);
+                    if (lane < kXcds) load += lv * m;
+                    pos += lv * kXcds;
+                    continue;
+                }
+                const int before = (int)__builtin_popcountll(takers & ((1ull << lane) - 1));   // lower-indexed takers
                 const int cnt = ntake < nrun ? ntake : nrun;
                 if (lane < kXcds && load == lo && before < cnt) {
                     xasg[r0 + pos + before] = (lane << 24) | load;

@@ -114,3 +114,48 @@ def test_unit_order_covers_every_chunk_and_tile_once(nt_per):
             for t in range(nt_per):
                 assert units[t * m:(t + 1) * m] == [(first + c, t) for c in range(m)]
             first += m
+
+
+def rounds_placement(mv):
+    """The sort's placement of ranked experts (chunk counts mv, non-increasing)
+    by one 64-lane wave: per round, the XCDs at the lowest load take one
+    expert each from the current run of equal counts, in index order, or,
+    when all eight are at the lowest load, whole levels of the run at once.
+    Returns (XCD, first slot) per rank."""
+    load, asg = [0] * XCDS, [None] * len(mv)
+    for r0 in range(0, len(mv), 64):
+        blk = mv[r0:r0 + 64]
+        pos = 0
+        while pos < len(blk):
+            m = blk[pos]
+            nrun = sum(1 for v in blk[pos:] if v == m)
+            lo = min(load)
+            takers = [x for x in range(XCDS) if load[x] == lo]
+            if len(takers) == XCDS and nrun >= XCDS:
+                lv = nrun // XCDS
+                for p in range(lv * XCDS):
+                    asg[r0 + pos + p] = (p % XCDS, lo + (p // XCDS) * m)
+                load = [v + lv * m for v in load]
+                pos += lv * XCDS
+                continue
+            cnt = min(len(takers), nrun)
+            for b, x in enumerate(takers[:cnt]):
+                asg[r0 + pos + b] = (x, load[x])
+                load[x] += m
+            pos += cnt
+    return asg
+
+
+def test_round_placement_is_sequential_greedy():
+    # each expert, in rank order, to the XCD with the fewest chunks so far
+    # (lowest index on ties), at that XCD's current load as its first slot
+    rng = np.random.default_rng(21)
+    for _ in range(2000):
+        n = int(rng.integers(1, 400))
+        mv = sorted((int(v) for v in rng.choice([1, 1, 1, 1, 2, 2, 3, 5, 8, 17], size=n)), reverse=True)
+        load, want = [0] * XCDS, []
+        for m in mv:
+            x = int(np.argmin(load))
+            want.append((x, load[x]))
+            load[x] += m
+        assert rounds_placement(mv) == want
