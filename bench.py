@@ -216,8 +216,14 @@ def kernel_path(moe, w, mx8):
     persistent form, up to FUSED_MAX_PAIRS pairs."""
     if mx8:
         return "dense"
-    if os.environ.get("MOE_MXFP4_PATH") == "stream" or w.P > moe.FUSED_MAX_PAIRS:
+    path = os.environ.get("MOE_MXFP4_PATH") or "fused"
+    if path == "stream" or w.P > moe.FUSED_MAX_PAIRS:
         return "stream"
+    # one verify block (at most 64 pairs over at most 64 experts, no more
+    # pairs than experts, at most 1024 logits): routing, permutation and both
+    # projections in one launch, then the combine
+    if path == "fused" and w.E <= 64 and w.P <= 64 and w.P <= w.E and w.T * w.E <= 1024:
+        return "fused (routing in the expert launch)"
     return "fused (ticketed)" if w.P > w.E else "fused (persistent)"
 
 
@@ -319,9 +325,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="verify_32seq")
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated across steps")
-    ap.add_argument("--path", choices=("stream", "fused"), default=None,
-                    help="kernel path of the bf16 workloads (MOE_MXFP4_PATH): one launch per phase, or the "
-                         "persistent fused kernel; default: the library's")
+    ap.add_argument("--path", choices=("stream", "fused_launches", "fused"), default=None,
+                    help="kernel path of the bf16 workloads (MOE_MXFP4_PATH): one launch per phase; routing, "
+                         "one launch of both projections and the combine; or that with the whole layer in one "
+                         "launch for a single verify block; default: the library's (fused)")
     ap.add_argument("--cpu-tokens", type=int, default=128)       # about 10 s of oracle time on 16 cores
     ap.add_argument("--cpu-tokens-1thread", type=int, default=8,
                     help="tokens of the single-threaded oracle leg (8-, 256-token verify and tiny workloads)")
@@ -454,6 +461,15 @@ def main():
         roofline = {"bound": "hbm", "kernel": "k_expert<gate/up>", "achieved": achieved,
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                     "traffic": traffic, "traffic_counter": traffic_note, "algorithmic_bytes": gateup_bytes,
+                    **duration}
+    elif "routing in" in kpath:
+        # one kernel routes, permutes and runs both projections: all expert
+        # bytes, x, the logits and the float32 per-pair outputs it writes
+        nbytes = fused_bytes + w.T * w.E * 4
+        achieved = nbytes / gateup_s / 1e9
+        roofline = {"bound": "hbm", "kernel": "k_layer (routing, permutation, gate/up and down units, one launch)",
+                    "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": traffic, "traffic_counter": traffic_note, "algorithmic_bytes": nbytes,
                     **duration}
     else:
         # one kernel runs gate/up and down (the down stage launches nothing)

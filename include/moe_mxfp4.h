@@ -246,7 +246,10 @@ moe_status moe_mxfp4_forward(moe_mxfp4_ctx* ctx, const void* hidden,
  * it, so calls on one GPU whose executions overlap in time (concurrent
  * streams, or concurrent host threads) race and give undefined results;
  * serialise them (one stream, or events).  Nothing in it needs clearing:
- * every value a call reads from it was written earlier in the same call.
+ * every value a call reads from it was written earlier in the same call
+ * (the counters of the expert launch that routes in every workgroup are
+ * in the stream's state block, which the library also holds without
+ * allocating per call: see MOE_MXFP4_PATH).
  * Errors: as moe_mxfp4_forward; WORKSPACE when the call would need more
  * scratch than MOE_MXFP4_NOALLOC_SCRATCH_BYTES (moe_mxfp4_workspace_bytes
  * gives the figure; 256 tokens at d_model 4096, d_ff 1536, top-8 need about
@@ -279,19 +282,41 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
  *                       then taking down units from a queue.  Batches up to
  *                       MOE_MXFP4_FUSED_MAX_PAIRS pairs; larger ones run
  *                       "stream".
+ *                       For a single verify block (at most 64 pairs over
+ *                       at most 64 experts, no more pairs than experts, at
+ *                       most 1024 router logits) the routing and the
+ *                       permutation run inside that one launch instead:
+ *                       every workgroup routes the block's tokens and
+ *                       permutes its pairs itself (the same code as the
+ *                       routing launches), so the call is two launches,
+ *                       that one and the combine.  The launch's counters
+ *                       live in a state block that the library keeps per
+ *                       (GPU, stream) in device memory of its own (16 per
+ *                       GPU, held until the process ends); the combine
+ *                       launch clears it for the stream's next call, and the
+ *                       first call on a stream (or one after a call whose
+ *                       combine launch failed) clears it with one small
+ *                       extra launch.  Streams beyond the 16th on a GPU
+ *                       route in launches of their own.
+ *   "fused_launches"    "fused" with the routing and permutation always in
+ *                       launches of their own.
  *   "stream"            one launch per phase: permutation, gate/up +
  *                       SwiGLU, down, combine.
- * Both give bit-identical outputs.  Any other value makes create fail with
+ * All give bit-identical outputs.  Any other value makes create fail with
  * MOE_ERR_INVALID_ARG.  MXFP8 mode has one path (the dense kernels).
  *
- * The fused kernel's waits for other workgroups are bounded; past the
+ * The fused kernels' waits for other workgroups are bounded; past the
  * bound (or with MOE_MXFP4_SPIN_LIMIT set to a negative value, read on every
- * call, for tests of this path) it raises an error word in the workspace,
- * its workgroups exit normally and the call's outputs are undefined.
- * moe_mxfp4_device_status waits for hip_stream and writes that word of the
- * most recent call with `num_tokens` tokens on `workspace` (device) to
- * *status (host): 0 = no wait gave up; always 0 on paths without such
- * waits.  Errors: INVALID_ARG, CAPACITY, HIP.
+ * call, for tests of this path) they raise an error word, the workgroups
+ * exit normally and the call's outputs are undefined.
+ * moe_mxfp4_device_status waits for hip_stream and writes to *status (host)
+ * the error word of the most recent call with `num_tokens` tokens: where the
+ * routing runs inside the expert launch (see "fused"), of the most recent
+ * such call on hip_stream on the current GPU (the word sits in the stream's
+ * state block; workspace is not read); otherwise of the most recent such call
+ * on `workspace` (device).
+ * 0 = no wait gave up; always 0 on paths without such waits.  Errors:
+ * INVALID_ARG, CAPACITY, HIP.
  */
 #define MOE_MXFP4_FUSED_MAX_PAIRS 8192
 

@@ -291,8 +291,9 @@ class MoeMxfp4:
         return out
 
     def device_status(self, num_tokens: int, workspace=None, stream=None) -> int:
-        """The fused kernel's error word of the last call with ``num_tokens``
-        tokens on ``workspace`` (default: this object's cached workspace for
+        """The fused kernels' error word of the last call with ``num_tokens``
+        tokens: on ``stream`` where the expert launch routes a verify block itself,
+        else on ``workspace`` (default: this object's cached workspace for
         ``stream``); waits for the stream.  0 = no device-side wait gave up."""
         ws = self.workspace(num_tokens, stream) if workspace is None else workspace
         st = ctypes.c_int32()

@@ -33,9 +33,14 @@ struct moe_mxfp4_ctx {
     // it differs from the previous call's
     bool log = false;
     std::atomic<int32_t> logged_tokens{-1};
-    // bf16 activations: the persistent fused kernel ("fused") or one launch
-    // per phase ("stream", the default), from MOE_MXFP4_PATH at create
+    // bf16 activations, from MOE_MXFP4_PATH at create: one launch of both
+    // projections ("fused", the default: for a single verify block the
+    // routing and permutation run inside that launch, else in launches of
+    // their own; then the combine), the same with the routing always in
+    // launches of its own ("fused_launches"), or one launch per phase
+    // ("stream")
     bool fused = false;
+    bool layer = false;
 };
 
 namespace {
@@ -159,13 +164,15 @@ moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg, const moe_mxfp4_weights
     for (const void* p : ptrs)
         if (!aligned16(p)) return MOE_ERR_ALIGNMENT;
     const char* path = std::getenv("MOE_MXFP4_PATH");
-    if (path && *path && std::strcmp(path, "fused") != 0 && std::strcmp(path, "stream") != 0)
+    if (path && *path && std::strcmp(path, "fused") != 0 && std::strcmp(path, "fused_launches") != 0 &&
+        std::strcmp(path, "stream") != 0)
         return MOE_ERR_INVALID_ARG;
     moe_mxfp4_ctx* ctx = new (std::nothrow) moe_mxfp4_ctx;
     if (!ctx) return MOE_ERR_INTERNAL;
     ctx->cfg = *cfg;
     ctx->w = *weights;
     ctx->fused = !(path && std::strcmp(path, "stream") == 0);      // "fused" is the default
+    ctx->layer = !(path && *path) || std::strcmp(path, "fused") == 0;
     const char* lg = std::getenv("MOE_MXFP4_LOG");
     ctx->log = lg && *lg && std::strcmp(lg, "0") != 0;
     if (ctx->log)
@@ -173,7 +180,10 @@ moe_status moe_mxfp4_create(const moe_mxfp4_config* cfg, const moe_mxfp4_weights
                      cfg->num_experts, cfg->d_model, cfg->d_ff, cfg->top_k, cfg->max_tokens,
                      cfg->act_mode == MOE_ACT_MXFP8_E4M3 ? "mxfp8" : "bf16",
                      cfg->out_dtype == MOE_OUT_F32 ? "f32" : "bf16",
-                     cfg->act_mode == MOE_ACT_MXFP8_E4M3 ? "dense" : ctx->fused ? "fused" : "stream");
+                     cfg->act_mode == MOE_ACT_MXFP8_E4M3 ? "dense"
+                     : ctx->layer                         ? "fused"
+                     : ctx->fused                         ? "fused_launches"
+                                                          : "stream");
     *out = ctx;
     return MOE_OK;
 }
@@ -258,6 +268,65 @@ moe_status copy_debug(const moe_mxfp4_config& c, const moe::Dims& dm, const moe:
     return MOE_OK;
 }
 
+// State blocks of the layer kernel that routes in every workgroup:
+// kLayerPool per device, in a device array (each block cleared by a small
+// launch the first time a stream takes it, or after a call whose combine
+// launch, which clears the block for the next call, could not be made).  A
+// stream keeps its block for the life of the process, so calls on one stream
+// find the block their predecessor left clear; calls that may overlap run on
+// different streams and so on different blocks.  Blocks are shared by every
+// context on the device.  With every block taken, further streams use the
+// other launches.  In host code the array's name is a host-side stand-in:
+// only the device address found with hipGetSymbolAddress is handed to
+// kernels.
+constexpr int kLayerPool = 16;
+__device__ __align__(256) int32_t layer_pool[kLayerPool * moe::kLayerStateInts];
+
+constexpr int kMaxDevices = 64;
+struct LayerPool {
+    int32_t* base = nullptr;                 // device address of layer_pool
+    hipStream_t stream[kLayerPool] = {};
+    bool taken[kLayerPool] = {};
+    bool clear[kLayerPool] = {};             // the last call on it made its combine launch
+};
+std::mutex layer_mu;
+LayerPool layer_dev[kMaxDevices];
+
+// The block of stream s on the current device (taken now if `take`), with
+// *fresh = true when it must be cleared before use; *clear: its flag, which
+// the caller lowers before its launches and raises once the combine launch
+// is made.  nullptr if the stream has none and none is left (or on a HIP
+// error).
+int32_t* layer_state(hipStream_t s, bool take, bool* fresh, bool** clear = nullptr) {
+    *fresh = false;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(layer_mu);
+    LayerPool& lp = layer_dev[dev];
+    if (!lp.base) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(layer_pool)) != hipSuccess || !p) return nullptr;
+        lp.base = static_cast<int32_t*>(p);
+    }
+    for (int i = 0; i < kLayerPool; ++i)
+        if (lp.taken[i] && lp.stream[i] == s) {
+            *fresh = !lp.clear[i];
+            if (clear) *clear = &lp.clear[i];
+            return lp.base + (size_t)i * moe::kLayerStateInts;
+        }
+    if (!take) return nullptr;
+    for (int i = 0; i < kLayerPool; ++i)
+        if (!lp.taken[i]) {
+            lp.taken[i] = true;
+            lp.stream[i] = s;
+            lp.clear[i] = false;
+            *fresh = true;
+            if (clear) *clear = &lp.clear[i];
+            return lp.base + (size_t)i * moe::kLayerStateInts;
+        }
+    return nullptr;
+}
+
 // The launches of one forward call on stream s, the workspace already
 // carved; mark(i) records stage-timing event i (a no-op when timing is off).
 template <typename Mark>
@@ -275,6 +344,33 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
         router_logits = ws_logits;
     }
     const int chunk_rows = mx8 ? moe::kDenseChunk : moe::kChunk;
+    bool fresh = false, *lclear = nullptr;
+    int32_t* lstate =
+        !mx8 && ctx->layer && moe::layer_supported(dm) ? layer_state(s, true, &fresh, &lclear) : nullptr;
+    if (lstate) {
+        // routing, permutation and both projections in one launch (timed as
+        // the gate/up stage), then the combine, which clears the stream's
+        // state block for its next call; a block not known to be clear is
+        // cleared first
+        if (fault_at("route") || fault_at("sort") || fault_at("gateup") || fault_at("down")) return MOE_ERR_HIP;
+        if (mark(1) != hipSuccess || mark(2) != hipSuccess) return MOE_ERR_HIP;
+        *lclear = false;
+        if (fresh && moe::launch_layer_clear(lstate, s) != hipSuccess) return MOE_ERR_HIP;
+        if (mark(3) != hipSuccess ||
+            moe::launch_layer(x, router_logits, ctx->w, dm, ws, lstate, spin_limit(), s) != hipSuccess ||
+            mark(4) != hipSuccess || mark(5) != hipSuccess)
+            return MOE_ERR_HIP;
+        if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, false, s, lstate) != hipSuccess)
+            return MOE_ERR_HIP;
+        *lclear = true;
+        if (mark(6) != hipSuccess) return MOE_ERR_HIP;
+        if (ctx->log && ctx->logged_tokens.exchange(dm.T) != dm.T)
+            std::fprintf(stderr, "moe_mxfp4: T=%d P=%d E=%d d=%d f=%d k=%d: %sone launch of routing and "
+                         "permutation in every workgroup, gate/up + SwiGLU and down; combine (float32 per-pair "
+                         "outputs)\n",
+                         dm.T, dm.P, dm.E, dm.d, dm.f, dm.k, w_router ? "router projection, " : "");
+        return copy_debug(c, dm, ws, debug_out, s);
+    }
     if (!mx8 && ctx->fused && moe::fused_supported(dm)) {
         // routing (which clears the fused kernel's counters) and the
         // permutation, then one launch of gate/up and down units (timed as
@@ -410,7 +506,6 @@ moe_status forward_impl(moe_mxfp4_ctx* ctx, const void* hidden, const float* rou
 // with hipGetSymbolAddress and only that address is ever handed to kernels.
 __device__ __align__(256) uint8_t scratch[MOE_MXFP4_NOALLOC_SCRATCH_BYTES];
 
-constexpr int kMaxDevices = 64;
 std::mutex scratch_mu;
 void* scratch_ptr[kMaxDevices];
 
@@ -472,9 +567,23 @@ moe_status moe_mxfp4_device_status(const moe_mxfp4_ctx* ctx, const void* workspa
                        num_tokens * ctx->cfg.top_k};
     if (num_tokens == 0 || ctx->cfg.act_mode != MOE_ACT_BF16 || !ctx->fused || !moe::fused_supported(dm))
         return MOE_OK;                                // no device-side waits on this path
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    if (ctx->layer && moe::layer_supported(dm)) {
+        // routing in the expert kernel: the stream's state block (none yet:
+        // no call)
+        bool fresh = false;
+        const int32_t* st = layer_state(s, false, &fresh);
+        if (!st) return MOE_OK;
+        int32_t ep = 0, err = 0;
+        if (hipMemcpyAsync(&ep, st + moe::kLayerEpoch, sizeof(ep), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipMemcpyAsync(&err, st + moe::kLayerError, sizeof(err), hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return MOE_ERR_HIP;
+        *status = ep != 0 && err == ep;            // raised by the call that advanced the epoch last
+        return MOE_OK;
+    }
     if (!workspace) return MOE_ERR_INVALID_ARG;
     const Layout L = make_layout(ctx->cfg, num_tokens);
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
     int32_t word = 0;
     const char* src = static_cast<const char*>(workspace) + L.fctl + moe::kFusedErrorWord * sizeof(int32_t);
     if (hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||

@@ -36,13 +36,25 @@ __device__ __forceinline__ f32x4_t load_o4(const OT* p, const uint8_t* sc) {
 // KK and the k row loads are all issued before the sum (the rows are read
 // once, so they bypass the caches' retention).  o holds float32 values
 // (streaming path) or fp16 codes with a scale byte per 128 columns in os
-// (dense path).
+// (dense path).  layer_st: the state block of the routing expert kernel
+// that ran before (nullptr: none), whose queue and chunk counters workgroup
+// 0 clears for the stream's next call and whose epoch it advances.
 template <int KK, typename OT>
 __global__ __launch_bounds__(kThreads) void k_finalize(Dims dm, const OT* __restrict__ o,
                                                        const uint8_t* __restrict__ os,
                                                        const float* __restrict__ topk_w,
-                                                       void* __restrict__ out, int out_dtype) {
+                                                       void* __restrict__ out, int out_dtype,
+                                                       int32_t* __restrict__ layer_st) {
 #pragma clang fp contract(off)
+    if (layer_st && blockIdx.x == 0) {
+        static_assert(kChunk < kThreads, "one thread per counter");
+        if (threadIdx.x == 0) {
+            layer_st[kLayerQueue] = 0;
+            layer_st[kLayerEpoch] = layer_st[kLayerEpoch] + 1;
+        } else if (threadIdx.x <= kChunk) {
+            layer_st[kLayerChunkDone + kLayerLine * (threadIdx.x - 1)] = 0;
+        }
+    }
     const int q = dm.d / 4;
     const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
     if (gid >= (size_t)dm.T * q) return;
@@ -184,18 +196,19 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 }  // namespace
 
 hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, bool o_f16,
-                           hipStream_t s) {
+                           hipStream_t s, int32_t* layer_state) {
     const size_t n = (size_t)dm.T * (dm.d / 4);
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads)), block(kThreads);
     const uint16_t* o16 = reinterpret_cast<const uint16_t*>(ws.o);
+    int32_t* st = layer_state;
     if (dm.k == 8 && o_f16)
-        hipLaunchKernelGGL((k_finalize<8, uint16_t>), grid, block, 0, s, dm, o16, ws.os, ws.topk_w, out, out_dtype);
+        hipLaunchKernelGGL((k_finalize<8, uint16_t>), grid, block, 0, s, dm, o16, ws.os, ws.topk_w, out, out_dtype, st);
     else if (dm.k == 8)
-        hipLaunchKernelGGL((k_finalize<8, float>), grid, block, 0, s, dm, ws.o, ws.os, ws.topk_w, out, out_dtype);
+        hipLaunchKernelGGL((k_finalize<8, float>), grid, block, 0, s, dm, ws.o, ws.os, ws.topk_w, out, out_dtype, st);
     else if (o_f16)
-        hipLaunchKernelGGL((k_finalize<0, uint16_t>), grid, block, 0, s, dm, o16, ws.os, ws.topk_w, out, out_dtype);
+        hipLaunchKernelGGL((k_finalize<0, uint16_t>), grid, block, 0, s, dm, o16, ws.os, ws.topk_w, out, out_dtype, st);
     else
-        hipLaunchKernelGGL((k_finalize<0, float>), grid, block, 0, s, dm, ws.o, ws.os, ws.topk_w, out, out_dtype);
+        hipLaunchKernelGGL((k_finalize<0, float>), grid, block, 0, s, dm, ws.o, ws.os, ws.topk_w, out, out_dtype, st);
     return hipGetLastError();
 }
 

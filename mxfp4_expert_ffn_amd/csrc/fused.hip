@@ -51,6 +51,7 @@
 //
 // The unit bodies are the per-phase kernels' own pipeline (stream_pipe.hpp),
 // so every h and o value is bit-identical to the multi-launch path.
+#include "route_core.hpp"
 #include "stream_pipe.hpp"
 
 namespace moe {
@@ -62,6 +63,7 @@ using stream::kDown;
 using stream::kGateUp;
 using stream::kSlot;
 using stream::kThreads;
+using stream::kWaves;
 
 // ctl[] words.  Each counter sits on a 256-byte line of its own, so the
 // polls of waiting workgroups and the atomics on other counters do not queue
@@ -220,6 +222,215 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain(FusedArgs f) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The layer of one verify block (at most 64 pairs over at most 64 experts)
+// in two launches: this persistent kernel, with no launch in front of it,
+// and the combine after it.
+//
+//   - Every workgroup routes all T tokens and permutes the P pairs itself,
+//     in LDS (route_core.hpp: the same code, so the same bits, as the
+//     routing launches), from the block's logits staged in LDS by one
+//     coalesced pass.  That costs a workgroup about what reading the chunk
+//     count and record did, and no workgroup waits for another to publish
+//     the permutation.  Workgroup 0 also writes the routing to the workspace
+//     (the routing outputs of the call, and the weights the combine reads).
+//   - Units come from one queue as in k_fused: gate/up units first, then
+//     down units in chunk order, each waiting for its chunk's gate/up tiles;
+//     the per-pair outputs go to the workspace for the combine launch.
+//   - Counters: the stream's state block (the queue, a counter per chunk,
+//     the error word and the epoch).  The combine launch clears them for the
+//     stream's next call, so that call needs no clearing launch in front of
+//     it; a wait that gives up stores epoch + 1 in the error word.
+//
+// Also measured, and slower: the combine inside this kernel as well, either
+// by the down unit that completes a column tile (a store drain and an atomic
+// with return after every down unit: 81 us against 71 us for k_fused at 8
+// tokens) or by every workgroup once a counter of finished down units is
+// full (hundreds of workgroups polling one line: 116 us).
+struct LayerArgs {
+    GemmArgs gu, dn;
+    const float* logits;       // [T][E]
+    Dims dm;
+    int32_t* st;               // the stream's state block
+    // the call's routing outputs in the workspace (written by workgroup 0)
+    int32_t *ids, *offsets, *sorted, *active, *chunks, *nchunks;
+    float* wts;
+    int32_t ntg, ntd;
+    int32_t spin_limit;
+};
+
+// LDS beside the unit ring: routing and permutation of the block.
+constexpr int kLyWords = 0;                                        // flag, next ticket, epoch
+constexpr int kLySc = 16;                                          // RankScratch<1>[kWaves]
+constexpr int kLyIds = kLySc + kWaves * (int)sizeof(route::RankScratch<1>);
+constexpr int kLyWts = kLyIds + kChunk * 4;
+constexpr int kLyCnt = kLyWts + kChunk * 4;
+constexpr int kLyExo = kLyCnt + kWave * 4;
+constexpr int kLyKeys = kLyExo + kWave * 4;                        // uint64 [64]
+constexpr int kLyOff = kLyKeys + kWave * 8;                        // [E + 1]
+constexpr int kLyAct = kLyOff + (kWave + 4) * 4;                   // [E + 1]
+constexpr int kLySorted = kLyAct + (kWave + 4) * 4;                // [P]
+constexpr int kLyChunks = kLySorted + kChunk * 4;                  // [64][kChunkRec]
+constexpr int kLyNch = kLyChunks + kChunk * kChunkRec * 4;
+constexpr int kLyLogits = kLyNch + 16;                             // [T][E] router logits
+constexpr int kLyBytes = kLyLogits + kLayerMaxLogits * 4;
+static_assert(kLayerMaxLogits % kThreads == 0, "whole logit loads per thread");
+static_assert(kLySc % 16 == 0 && kLyKeys % 8 == 0 && sizeof(route::RankScratch<1>) % 16 == 0, "LDS alignment");
+
+// Workgroup barrier ordering LDS accesses only (no wait for outstanding
+// global memory operations).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wait (one lane) until *p >= target; false once a wait of this call gave
+// up (its error word holds `tag`), or when the poll limit runs out (then
+// this one raises it).
+__device__ bool layer_wait(const LayerArgs& a, const int32_t* p, int32_t target, int32_t tag) {
+    for (int i = 0;; ++i) {
+        if (a.spin_limit >= 0 && load_agent(p) >= target) return true;
+        if (i % 32 == 31 && load_agent(a.st + kLayerError) == tag) return false;
+        if (i >= a.spin_limit) {
+            __hip_atomic_store(a.st + kLayerError, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+template <int RT, int DG, int DD>
+__global__ __launch_bounds__(kThreads, 2) void k_layer(LayerArgs a) {
+    constexpr int kRing = DG > DD ? DG : DD;
+    // one LDS object (see k_fused): the unit ring, then the block's routing
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kSlot + kLyBytes];
+    uint8_t* ly = lds + kRing * kSlot;
+    int32_t* s_words = reinterpret_cast<int32_t*>(ly + kLyWords);
+    route::RankScratch<1>* sc = reinterpret_cast<route::RankScratch<1>*>(ly + kLySc);
+    int32_t* s_ids = reinterpret_cast<int32_t*>(ly + kLyIds);
+    float* s_wts = reinterpret_cast<float*>(ly + kLyWts);
+    int32_t* s_off = reinterpret_cast<int32_t*>(ly + kLyOff);
+    int32_t* s_act = reinterpret_cast<int32_t*>(ly + kLyAct);
+    int32_t* s_sorted = reinterpret_cast<int32_t*>(ly + kLySorted);
+    int32_t* s_chunks = reinterpret_cast<int32_t*>(ly + kLyChunks);
+    int32_t* s_nch = reinterpret_cast<int32_t*>(ly + kLyNch);
+    float* s_lg = reinterpret_cast<float*>(ly + kLyLogits);
+    const Dims dm = a.dm;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+
+    // The block's logits (up to kLayerMaxLogits / kThreads per thread) into
+    // LDS; then lane 0 takes the first ticket and reads the epoch, whose
+    // results are used only after the routing and the permutation.  Until
+    // then the workgroup meets at barriers that order LDS only: a barrier
+    // that also ordered global memory would wait for the atomic, which every
+    // workgroup issues at once.
+    constexpr int kLg = kLayerMaxLogits / kThreads;
+    float lgv[kLg];
+#pragma unroll
+    for (int q = 0; q < kLg; ++q) {
+        const int i = tid + q * kThreads;
+        lgv[q] = i < dm.T * dm.E ? a.logits[i] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < kLg; ++q) s_lg[tid + q * kThreads] = lgv[q];
+    int first = 0, epoch = 0;
+    if (tid == 0) {
+        first = __hip_atomic_fetch_add(a.st + kLayerQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        epoch = load_agent(a.st + kLayerEpoch);
+    }
+    lds_barrier();
+    // one wave per token ranks its logits, then wave 0 permutes the pairs
+    for (int t = wave; t < dm.T; t += kWaves) route::route_token_rank<1>(s_lg, dm, t, lane, sc[wave], s_ids, s_wts, nullptr);
+    lds_barrier();
+    if (wave == 0)
+        route::sort_wave(dm, s_ids, reinterpret_cast<int32_t*>(ly + kLyCnt), reinterpret_cast<int32_t*>(ly + kLyExo),
+                         reinterpret_cast<uint64_t*>(ly + kLyKeys), lane, s_off, s_sorted, s_act, s_chunks, s_nch,
+                         nullptr, 0);
+    if (tid == 0) {
+        s_words[1] = first;
+        s_words[2] = epoch;
+    }
+    lds_barrier();
+    const int nc = __builtin_amdgcn_readfirstlane(*s_nch);
+    const int32_t tag = __builtin_amdgcn_readfirstlane(s_words[2]) + 1;
+    if (blockIdx.x == 0) {
+        for (int i = tid; i < dm.P; i += kThreads) {
+            a.ids[i] = s_ids[i];
+            a.wts[i] = s_wts[i];
+            a.sorted[i] = s_sorted[i];
+        }
+        for (int i = tid; i < dm.E; i += kThreads) a.offsets[i] = s_off[i];
+        for (int i = tid; i < nc; i += kThreads) a.active[i] = s_act[i];
+        for (int i = tid; i < nc * kChunkRec; i += kThreads) a.chunks[i] = s_chunks[i];
+        if (tid == 0) {
+            a.offsets[dm.E] = dm.P;
+            a.active[dm.E] = nc;
+            *a.nchunks = nc;
+        }
+    }
+
+    const int nG = nc * a.ntg, nD = nc * a.ntd;
+    int v = __builtin_amdgcn_readfirstlane(s_words[1]);
+    int next = 0;
+    auto take = [&] {
+        if (tid == 0) next = __hip_atomic_fetch_add(a.st + kLayerQueue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    while (v < nG) {
+        const int chunk = v / a.ntg, nt = v % a.ntg;
+        const int32_t* rec = s_chunks + kChunkRec * chunk;
+        const int e = __builtin_amdgcn_readfirstlane(rec[0]);
+        const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
+        const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
+        stream::run_unit<kGateUp, RT, DG, true>(a.gu, lds, e, nt, s_sorted + m0, m0, rows, [] {}, take);
+        publish(a.st + kLayerChunkDone + kLayerLine * chunk);
+        if (tid == 0) s_words[1] = next;
+        __syncthreads();
+        v = __builtin_amdgcn_readfirstlane(s_words[1]);
+    }
+    while (v < nG + nD) {
+        const int w = v - nG;
+        const int chunk = w / a.ntd, nt = w % a.ntd;
+        const int32_t* rec = s_chunks + kChunkRec * chunk;
+        const int e = __builtin_amdgcn_readfirstlane(rec[0]);
+        const int m0 = __builtin_amdgcn_readfirstlane(rec[1]);
+        const int rows = __builtin_amdgcn_readfirstlane(rec[2]);
+        if (tid == 0) {
+            const bool ok = layer_wait(a, a.st + kLayerChunkDone + kLayerLine * chunk, a.ntg, tag);
+            if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_words[0] = ok;
+        }
+        __syncthreads();
+        if (!__builtin_amdgcn_readfirstlane(s_words[0])) return;
+        stream::run_unit<kDown, RT, DD>(a.dn, lds, e, nt, s_sorted + m0, m0, rows, [] {}, take);
+        if (tid == 0) s_words[1] = next;
+        __syncthreads();               // s_words[1] holds the next ticket; the LDS ring is free again
+        v = __builtin_amdgcn_readfirstlane(s_words[1]);
+    }
+}
+
+__global__ void k_layer_clear(int32_t* st) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < kLayerStateInts; i += gridDim.x * blockDim.x) st[i] = 0;
+}
+
+template <int DG, int DD>
+hipError_t launch_layer_variant(const LayerArgs& a, int items, hipStream_t s) {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_layer<2, DG, DD>),
+                                                         kThreads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidValue;
+        cached[dev] = per_cu * cus > 0 ? per_cu * cus : 1;
+    }
+    const int grid = items < cached[dev] ? items : cached[dev];
+    hipLaunchKernelGGL((k_layer<2, DG, DD>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
 template <int RT, int DG, int DD>
 hipError_t launch_chain(const FusedArgs& f, const Dims& dm, hipStream_t s) {
     // every counter gets xstride * (ntg + ntd) workgroups: at least the
@@ -326,6 +537,40 @@ hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dim
     if (g4) return fused::launch_variant<4, 4, 2>(f, items, s);
     if (d4) return fused::launch_variant<4, 2, 4>(f, items, s);
     return fused::launch_variant<4, 2, 2>(f, items, s);
+}
+
+bool layer_supported(const Dims& dm) {
+    return dm.E <= kWave && dm.P <= kChunk && dm.P <= dm.E && stream::tiles_per_wave(dm) == 2 &&
+           dm.T * dm.E <= kLayerMaxLogits;
+}
+
+hipError_t launch_layer(const uint16_t* x, const float* logits, const moe_mxfp4_weights& w, const Dims& dm,
+                        const Workspace& ws, int32_t* state, int spin_limit, hipStream_t s) {
+    if (!layer_supported(dm)) return hipErrorInvalidValue;
+    const fused::FusedArgs f = fused::make_args(x, w, dm, ws, spin_limit);
+    fused::LayerArgs a{};
+    a.gu = f.gu;
+    a.dn = f.dn;
+    a.logits = logits;
+    a.dm = dm;
+    a.st = state;
+    a.ids = ws.topk_ids; a.wts = ws.topk_w; a.offsets = ws.offsets; a.sorted = ws.sorted_pairs;
+    a.active = ws.active; a.chunks = ws.chunks; a.nchunks = ws.nchunks;
+    a.ntg = f.ntg;
+    a.ntd = f.ntd;
+    a.spin_limit = spin_limit;
+    // every active expert is one chunk
+    const int items = (dm.P < dm.E ? dm.P : dm.E) * (a.ntg + a.ntd);
+    const bool g4 = (dm.d / kKStep) % 4 == 0, d4 = (dm.f / kKStep) % 4 == 0;
+    if (g4 && d4) return fused::launch_layer_variant<4, 4>(a, items, s);
+    if (g4) return fused::launch_layer_variant<4, 2>(a, items, s);
+    if (d4) return fused::launch_layer_variant<2, 4>(a, items, s);
+    return fused::launch_layer_variant<2, 2>(a, items, s);
+}
+
+hipError_t launch_layer_clear(int32_t* state, hipStream_t s) {
+    hipLaunchKernelGGL(fused::k_layer_clear, dim3(16), dim3(256), 0, s, state);
+    return hipGetLastError();
 }
 
 }  // namespace moe

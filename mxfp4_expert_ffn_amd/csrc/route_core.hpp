@@ -1,0 +1,207 @@
+// Routing of one token by one wavefront and the permutation of a batch of
+// at most 64 pairs by one wavefront: shared by the routing launches
+// (route_sort.hip) and the expert kernel that routes a verify block itself
+// (fused.hip k_layer), which runs them inside every workgroup.
+//
+// Routing: techllm.github.io "Xiaomi MiMo x TileRT", section "3. TileRT",
+// names the expert-routing step; the pages give no rule, so: the k largest
+// logits (ties to the lower expert index), weights = softmax over the k
+// selected logits.  Permutation: a stable counting sort of the pairs
+// p = t*k + j by expert (ballots on the expert-id bits, no atomics), the
+// active experts ranked by descending count (ties to the lower index).
+#pragma once
+
+#include "common.hpp"
+
+#include <float.h>
+
+namespace moe {
+namespace route {
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Per-wave LDS scratch of the ranking router.
+template <int NV>
+struct alignas(16) RankScratch {                 // sv is read as float4
+    float sv[NV * kWave];
+    int32_t sid[kMaxTopK];
+    float sval[kMaxTopK];
+    float sex[kMaxTopK];
+};
+
+// Routing of token t by one wavefront, E <= 64 * NV.  Lane l holds logits l
+// and l + 64.  The rank of logit e is the number of logits that come before
+// it in the order (value descending, expert index ascending); the experts of
+// ranks 0..k-1 are the selection, already in order.  Writes ids/weights of
+// the token's k slots (and the ids to ids_lds when given).
+template <int NV>
+__device__ __forceinline__ void route_token_rank(const float* __restrict__ logits, const Dims& dm, int t, int lane,
+                                 RankScratch<NV>& sc, int32_t* __restrict__ ids, float* __restrict__ wts,
+                                 int32_t* ids_lds) {
+    const float* l = logits + (size_t)t * dm.E;
+    float v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        // padding sorts after every logit: it never beats one (-inf included)
+        v[i] = e < dm.E ? l[e] : -INFINITY;
+        sc.sv[e] = v[i];
+    }
+    wave_sync_lds();
+    int rank[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) rank[i] = 0;
+    const float4* row = reinterpret_cast<const float4*>(sc.sv);
+#pragma unroll 4
+    for (int q = 0; q < NV * kWave / 4; ++q) {
+        const float4 u4 = row[q];
+        const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e2 = 4 * q + j;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                rank[i] += (u[j] > v[i]) || (u[j] == v[i] && e2 < lane + kWave * i);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        if (e < dm.E && rank[i] < dm.k) {
+            sc.sid[rank[i]] = e;
+            sc.sval[rank[i]] = v[i];
+        }
+    }
+    wave_sync_lds();
+    float ex = 0.0f;
+    if (lane < dm.k) {
+        ex = expf(sc.sval[lane] - sc.sval[0]);
+        sc.sex[lane] = ex;
+    }
+    wave_sync_lds();
+    if (lane < dm.k) {
+        // the k terms added in slot order, read four at a time
+        float sum = 0.0f;
+        const float4* sx = reinterpret_cast<const float4*>(sc.sex);
+        for (int j = 0; j < dm.k; j += 4) {
+            const float4 s4 = sx[j / 4];
+            sum += s4.x;
+            if (j + 1 < dm.k) sum += s4.y;
+            if (j + 2 < dm.k) sum += s4.z;
+            if (j + 3 < dm.k) sum += s4.w;
+        }
+        const int id = sc.sid[lane];
+        ids[(size_t)t * dm.k + lane] = id;
+        wts[(size_t)t * dm.k + lane] = ex / sum;
+        if (ids_lds) ids_lds[t * dm.k + lane] = id;
+    }
+    wave_sync_lds();                             // the scratch may be reused for the next token
+}
+
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(v, off);
+        if (lane >= off) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int id_bits(int E) {
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    return nbits;
+}
+
+// The permutation of at most 64 pairs over at most 64 experts by one
+// wavefront, with no workgroup barrier: lane p holds pair p, lane e expert e.
+// Same outputs as sort_single (a stable counting sort; experts ranked by
+// descending count, ties to the lower index).  A chunk never splits, since
+// the caller guarantees P <= chunk_rows, so active expert r is chunk record r.
+// ids: P expert ids (LDS); scratch: 64 counts, 64 offsets, 64 keys (used as
+// 64 ints).  The
+// outputs may be global or LDS memory; xtab == nullptr skips the per-XCD table.
+__device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, int32_t* cnt, int32_t* exo,
+                                          uint64_t* keys, int lane, int32_t* __restrict__ offsets,
+                                          int32_t* __restrict__ sorted, int32_t* __restrict__ active,
+                                          int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks,
+                                          int32_t* __restrict__ xtab, int xstride) {
+    const int E = dm.E, P = dm.P;
+    const bool valid = lane < P;
+    const int ep = valid ? ids[lane] : 0;
+    // lanes holding the same expert: one ballot per id bit
+    uint64_t peers = __ballot(valid);
+    for (int b = 0, nb = id_bits(E); b < nb; ++b) {
+        const bool bit = (ep >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    const int rank = __popcll(peers & below);          // earlier pairs of the same expert
+    cnt[lane] = 0;
+    wave_sync_lds();
+    if (valid && rank == 0) cnt[ep] = __popcll(peers);
+    wave_sync_lds();
+    const int c = lane < E ? cnt[lane] : 0;
+    const int excl = wave_inclusive_scan(c, lane) - c;
+    exo[lane] = excl;
+    if (lane < E) offsets[lane] = excl;
+    // rank of an active expert in the order (count descending, index
+    // ascending) = active experts with a larger count + those with the same
+    // count and a lower index.  Lanes of equal count find each other with one
+    // ballot per count bit (counts <= 64); a suffix sum over the histogram of
+    // counts gives the larger ones.
+    uint64_t same = __ballot(c > 0);
+    for (int b = 0; b < 7; ++b) {
+        const bool bit = (c >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+    }
+    const int eq_below = __popcll(same & below);
+    int32_t* hist = reinterpret_cast<int32_t*>(keys);      // [64]: active experts of count lane + 1
+    hist[lane] = 0;
+    wave_sync_lds();
+    if (c > 0 && eq_below == 0) hist[c - 1] = __popcll(same);
+    wave_sync_lds();
+    const int h = hist[lane];
+    const int hin = wave_inclusive_scan(h, lane);
+    const int ge = __builtin_amdgcn_readlane(hin, kWave - 1) - hin + h;   // active experts of count >= lane + 1
+    const int gt = __shfl(ge, c < kWave ? c : 0);                          // ... of count > c (c < 64)
+    const int r = (c < kWave ? gt : 0) + eq_below;
+    const int na = __popcll(__ballot(lane < E && c > 0));
+    if (lane < E && c > 0) {
+        active[r] = lane;
+        int32_t* rec = chunks + kChunkRec * r;
+        rec[0] = lane;
+        rec[1] = excl;
+        rec[2] = c;
+        rec[3] = 0;
+        // per-XCD table (the layout of expert_lists): one chunk per expert,
+        // so the greedy assignment deals rank r to XCD r mod kXcds, slot
+        // r / kXcds
+        if (xtab) {
+            int32_t* xr = xtab + kXtabHead + kXtabRec * ((size_t)(r % kXcds) * xstride + r / kXcds);
+            xr[0] = lane;
+            xr[1] = excl;
+            xr[2] = c;
+            xr[3] = r;
+            xr[4] = 0;
+            xr[5] = 1;
+        }
+    }
+    if (xtab && lane < kXcds) xtab[lane] = na / kXcds + (lane < na % kXcds);
+    if (lane == 0) {
+        offsets[E] = P;
+        active[E] = na;
+        *nchunks = na;
+    }
+    if (valid) sorted[exo[ep] + rank] = lane;
+}
+
+}  // namespace route
+}  // namespace moe

@@ -15,7 +15,7 @@
 // depend on their order.  Sizes: up to 64 pairs, one wave after the routing
 // in the same launch; up to 8192, one workgroup (fused with the routing for
 // up to 64 tokens); beyond, tiles of 2048 pairs in three launches.
-#include "common.hpp"
+#include "route_core.hpp"
 
 #include <float.h>
 #include <limits.h>
@@ -23,86 +23,12 @@
 namespace moe {
 namespace {
 
+using namespace route;
+
 constexpr int kRouteWaves = 4;          // tokens per routing workgroup
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kPrefetch = 8;            // rounds of pair ids loaded ahead per wave
-
-__device__ __forceinline__ void wave_sync_lds() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Per-wave LDS scratch of the ranking router.
-template <int NV>
-struct alignas(16) RankScratch {                 // sv is read as float4
-    float sv[NV * kWave];
-    int32_t sid[kMaxTopK];
-    float sval[kMaxTopK];
-    float sex[kMaxTopK];
-};
-
-// Routing of token t by one wavefront, E <= 64 * NV.  Lane l holds logits l
-// and l + 64.  The rank of logit e is the number of logits that come before
-// it in the order (value descending, expert index ascending); the experts of
-// ranks 0..k-1 are the selection, already in order.  Writes ids/weights of
-// the token's k slots (and the ids to ids_lds when given).
-template <int NV>
-__device__ __forceinline__ void route_token_rank(const float* __restrict__ logits, const Dims& dm, int t, int lane,
-                                 RankScratch<NV>& sc, int32_t* __restrict__ ids, float* __restrict__ wts,
-                                 int32_t* ids_lds) {
-    const float* l = logits + (size_t)t * dm.E;
-    float v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + kWave * i;
-        // padding sorts after every logit: it never beats one (-inf included)
-        v[i] = e < dm.E ? l[e] : -INFINITY;
-        sc.sv[e] = v[i];
-    }
-    wave_sync_lds();
-    int rank[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) rank[i] = 0;
-    const float4* row = reinterpret_cast<const float4*>(sc.sv);
-#pragma unroll 4
-    for (int q = 0; q < NV * kWave / 4; ++q) {
-        const float4 u4 = row[q];
-        const float u[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e2 = 4 * q + j;
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                rank[i] += (u[j] > v[i]) || (u[j] == v[i] && e2 < lane + kWave * i);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = lane + kWave * i;
-        if (e < dm.E && rank[i] < dm.k) {
-            sc.sid[rank[i]] = e;
-            sc.sval[rank[i]] = v[i];
-        }
-    }
-    wave_sync_lds();
-    float ex = 0.0f;
-    if (lane < dm.k) {
-        ex = expf(sc.sval[lane] - sc.sval[0]);
-        sc.sex[lane] = ex;
-    }
-    wave_sync_lds();
-    if (lane < dm.k) {
-        float sum = 0.0f;
-        for (int j = 0; j < dm.k; ++j) sum += sc.sex[j];
-        const int id = sc.sid[lane];
-        ids[(size_t)t * dm.k + lane] = id;
-        wts[(size_t)t * dm.k + lane] = ex / sum;
-        if (ids_lds) ids_lds[t * dm.k + lane] = id;
-    }
-    wave_sync_lds();                             // the scratch may be reused for the next token
-}
 
 // One wavefront per token, E <= 64 * NV.
 // Clear zero[0 .. nzero) with every thread of the grid (the persistent
@@ -222,14 +148,6 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void k_route(const float* __re
     }
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(v, off);
-        if (lane >= off) v += o;
-    }
-    return v;
-}
 
 // Bitmask of the lanes of this wave whose `key` equals mine (valid lanes only).
 __device__ __forceinline__ uint64_t match_peers(int key, bool valid, int nbits) {
@@ -270,11 +188,6 @@ __device__ __forceinline__ void wave_pairs(const int32_t* __restrict__ ids, int 
     }
 }
 
-__device__ __forceinline__ int id_bits(int E) {
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    return nbits;
-}
 
 // From the per-expert pair counts (LDS counts[E4], zero past E) of all P
 // pairs, with every thread of a kSortThreads workgroup: expert offsets
@@ -546,71 +459,6 @@ __global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __rest
     sort_single(dm, ids_lds, sm64, offsets, sorted, active, chunks, nchunks, chunk_rows, xtab, xstride);
 }
 
-// The permutation of at most 64 pairs over at most 64 experts by one
-// wavefront, with no workgroup barrier: lane p holds pair p, lane e expert e.
-// Same outputs as sort_single (a stable counting sort; experts ranked by
-// descending count, ties to the lower index).  A chunk never splits, since
-// the caller guarantees P <= chunk_rows, so active expert r is chunk record r.
-// ids: P expert ids (LDS); scratch: 64 counts, 64 offsets, 64 keys.
-__device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, int32_t* cnt, int32_t* exo,
-                                          uint64_t* keys, int lane, int32_t* __restrict__ offsets,
-                                          int32_t* __restrict__ sorted, int32_t* __restrict__ active,
-                                          int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks,
-                                          int32_t* __restrict__ xtab, int xstride) {
-    const int E = dm.E, P = dm.P;
-    const bool valid = lane < P;
-    const int ep = valid ? ids[lane] : 0;
-    // lanes holding the same expert: one ballot per id bit
-    uint64_t peers = __ballot(valid);
-    for (int b = 0, nb = id_bits(E); b < nb; ++b) {
-        const bool bit = (ep >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
-    }
-    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
-    const int rank = __popcll(peers & below);          // earlier pairs of the same expert
-    cnt[lane] = 0;
-    wave_sync_lds();
-    if (valid && rank == 0) cnt[ep] = __popcll(peers);
-    wave_sync_lds();
-    const int c = lane < E ? cnt[lane] : 0;
-    const int excl = wave_inclusive_scan(c, lane) - c;
-    exo[lane] = excl;
-    keys[lane] = ((uint64_t)(uint32_t)c << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)lane);
-    if (lane < E) offsets[lane] = excl;
-    wave_sync_lds();
-    // rank of an active expert = number of experts with a larger key (experts
-    // past E have count 0 and never outrank an active one)
-    int r = 0;
-    const uint64_t mine = keys[lane];
-    for (int e2 = 0; e2 < E; ++e2) r += keys[e2] > mine;
-    const int na = __popcll(__ballot(lane < E && c > 0));
-    if (lane < E && c > 0) {
-        active[r] = lane;
-        int32_t* rec = chunks + kChunkRec * r;
-        rec[0] = lane;
-        rec[1] = excl;
-        rec[2] = c;
-        rec[3] = 0;
-        // per-XCD table (the layout of expert_lists): one chunk per expert,
-        // so the greedy assignment deals rank r to XCD r mod kXcds, slot
-        // r / kXcds
-        int32_t* xr = xtab + kXtabHead + kXtabRec * ((size_t)(r % kXcds) * xstride + r / kXcds);
-        xr[0] = lane;
-        xr[1] = excl;
-        xr[2] = c;
-        xr[3] = r;
-        xr[4] = 0;
-        xr[5] = 1;
-    }
-    if (lane < kXcds) xtab[lane] = na / kXcds + (lane < na % kXcds);
-    if (lane == 0) {
-        offsets[E] = P;
-        active[E] = na;
-        *nchunks = na;
-    }
-    if (valid) sorted[exo[ep] + rank] = lane;
-}
 
 // Batches of at most 64 pairs over at most 64 experts: routing (one wave per
 // token) and then sort_wave on wave 0 -- one barrier in all, against the

@@ -161,7 +161,7 @@ def test_noalloc_forward_validates_before_touching_the_device():
 
 def test_path_selection_and_device_status_validation(monkeypatch):
     L = moe.lib()
-    for path, ok in (("stream", True), ("fused", True), ("", True), ("bogus", False)):
+    for path, ok in (("stream", True), ("fused", True), ("fused_launches", True), ("", True), ("bogus", False)):
         monkeypatch.setenv("MOE_MXFP4_PATH", path)
         st, h = _create()
         assert (st == 0) == ok, (path, st)
@@ -188,6 +188,17 @@ def test_path_selection_and_device_status_validation(monkeypatch):
         out.value = 7
         assert ds(h, None, 0, ctypes.byref(out), None) == 0 and out.value == 0     # no tokens
         assert ds(h, None, 8, ctypes.byref(out), None) == 1                        # no workspace
+    finally:
+        L.moe_mxfp4_destroy(h)
+    # a single verify block whose expert launch routes it itself keeps its
+    # error word in the stream's state block: no workspace is read, and a
+    # stream with no such call yet reports 0
+    monkeypatch.setenv("MOE_MXFP4_PATH", "fused")
+    st, h = _create(num_experts=16, max_tokens=8)
+    monkeypatch.delenv("MOE_MXFP4_PATH")
+    try:
+        out.value = 7
+        assert ds(h, None, 1, ctypes.byref(out), None) == 0 and out.value == 0
     finally:
         L.moe_mxfp4_destroy(h)
 

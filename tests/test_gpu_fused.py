@@ -225,6 +225,6 @@ def test_fused_calls_on_two_streams_at_once(monkeypatch, T, E, k):
             with torch.cuda.stream(st):
                 fused_l(x, lg, out=out, workspace=wsp)
     torch.cuda.synchronize()
-    for wsp, out in zip(ws, outs):
-        assert fused_l.device_status(w.T, workspace=wsp) == 0
+    for st, wsp, out in zip(streams, ws, outs):
+        assert fused_l.device_status(w.T, workspace=wsp, stream=st) == 0
         assert torch.equal(out, y_ref)
