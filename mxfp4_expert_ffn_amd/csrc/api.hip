@@ -18,7 +18,7 @@
 #include <new>
 #include <vector>
 
-#include "common.hpp"
+#include "layer.hpp"
 
 struct moe_mxfp4_ctx {
     moe_mxfp4_config cfg;
@@ -360,7 +360,7 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
             moe::launch_layer(x, router_logits, ctx->w, dm, ws, lstate, spin_limit(), s) != hipSuccess ||
             mark(4) != hipSuccess || mark(5) != hipSuccess)
             return MOE_ERR_HIP;
-        if (fault_at("combine") || moe::launch_finalize(dm, ws, out, c.out_dtype, false, s, lstate) != hipSuccess)
+        if (fault_at("combine") || moe::launch_finalize_layer(dm, ws, out, c.out_dtype, lstate, s) != hipSuccess)
             return MOE_ERR_HIP;
         *lclear = true;
         if (mark(6) != hipSuccess) return MOE_ERR_HIP;

@@ -9,7 +9,7 @@
 // exactly.  Each product is rounded to float32 on its own (no fused
 // multiply-add), the k products are added in slot order j = 0..k-1 (fixed
 // order: deterministic), and the sum is rounded once to the output type.
-#include "common.hpp"
+#include "layer.hpp"
 
 namespace moe {
 namespace {
@@ -195,12 +195,13 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, bool o_f16,
-                           hipStream_t s, int32_t* layer_state) {
+namespace {
+
+hipError_t finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, bool o_f16, hipStream_t s,
+                    int32_t* st) {
     const size_t n = (size_t)dm.T * (dm.d / 4);
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads)), block(kThreads);
     const uint16_t* o16 = reinterpret_cast<const uint16_t*>(ws.o);
-    int32_t* st = layer_state;
     if (dm.k == 8 && o_f16)
         hipLaunchKernelGGL((k_finalize<8, uint16_t>), grid, block, 0, s, dm, o16, ws.os, ws.topk_w, out, out_dtype, st);
     else if (dm.k == 8)
@@ -210,6 +211,18 @@ hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int o
     else
         hipLaunchKernelGGL((k_finalize<0, float>), grid, block, 0, s, dm, ws.o, ws.os, ws.topk_w, out, out_dtype, st);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, bool o_f16,
+                           hipStream_t s) {
+    return finalize(dm, ws, out, out_dtype, o_f16, s, nullptr);
+}
+
+hipError_t launch_finalize_layer(const Dims& dm, const Workspace& ws, void* out, int out_dtype, int32_t* state,
+                                 hipStream_t s) {
+    return finalize(dm, ws, out, out_dtype, false, s, state);
 }
 
 hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t row0,

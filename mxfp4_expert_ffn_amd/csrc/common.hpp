@@ -197,35 +197,6 @@ int fused_ctl_ints(const Dims& dm);
 // device-side wait gave up.
 constexpr int kFusedErrorWord = 64;   // ints from the start of the counters
 bool fused_chain_form(const Dims& dm);
-
-// Layer in two launches (bf16 activations, one verify block: at most 64
-// pairs over at most 64 experts, no more pairs than experts, at most
-// kLayerMaxLogits router logits): one persistent launch routes the tokens and
-// permutes the pairs inside every workgroup and runs the gate/up and down
-// units; the combine follows.  The first launch's counters live in a state
-// block of kLayerStateInts ints that a stream keeps across calls: the
-// combine launch clears them for the stream's next call (a launch after the
-// kernel that uses them, so no launch runs in front of it) and advances the
-// epoch (calls completed on the block); the error word holds epoch + 1 of
-// the last call in which a wait gave up.
-constexpr int kLayerMaxLogits = 1024;               // T * E, staged in LDS
-constexpr int kLayerLine = 64;                      // ints per 256-byte line
-enum {
-    kLayerEpoch = 0,
-    kLayerError = kLayerLine,
-    kLayerQueue = 2 * kLayerLine,
-    kLayerChunkDone = 3 * kLayerLine,
-    kLayerStateInts = kLayerChunkDone + kChunk * kLayerLine
-};
-bool layer_supported(const Dims& dm);
-// The routing, permutation and both projections; the per-pair outputs go to
-// ws.o for launch_finalize(..., state).  state: the stream's block.
-hipError_t launch_layer(const uint16_t* x, const float* logits, const moe_mxfp4_weights& w, const Dims& dm,
-                        const Workspace& ws, int32_t* state, int spin_limit, hipStream_t s);
-// Zero a state block (its first use on a device, or after a call whose
-// combine launch failed).
-hipError_t launch_layer_clear(int32_t* state, hipStream_t s);
-
 hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
                         int spin_limit, hipStream_t s);
 
@@ -265,10 +236,9 @@ hipError_t launch_gateup_dense(const moe_mxfp4_weights& w, const Dims& dm, const
 hipError_t launch_down_dense(const moe_mxfp4_weights& w, const Dims& dm, const Workspace& ws,
                              hipStream_t s);
 // o_f16: the per-pair outputs are fp16 codes in ws.o with scales in ws.os
-// (dense path), else float32 in ws.o.  layer_state: the state block of the
-// launch_layer call before it, whose counters it clears (nullptr: none).
+// (dense path), else float32 in ws.o
 hipError_t launch_finalize(const Dims& dm, const Workspace& ws, void* out, int out_dtype, bool o_f16,
-                           hipStream_t s, int32_t* layer_state = nullptr);
+                           hipStream_t s);
 hipError_t launch_debug_dequant(const uint8_t* packed, const uint8_t* scales, int64_t K, int32_t row0,
                                 int32_t nrows, float* out, hipStream_t s);
 hipError_t launch_tile(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K,

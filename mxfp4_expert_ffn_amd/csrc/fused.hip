@@ -51,6 +51,7 @@
 //
 // The unit bodies are the per-phase kernels' own pipeline (stream_pipe.hpp),
 // so every h and o value is bit-identical to the multi-launch path.
+#include "layer.hpp"
 #include "route_core.hpp"
 #include "stream_pipe.hpp"
 
