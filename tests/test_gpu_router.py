@@ -128,7 +128,10 @@ def _check_routing(ids_gpu, w_gpu, exact, bound, k):
     return clear
 
 
-@pytest.mark.parametrize("T,d,f,E,k", [(40, 512, 512, 8, 2), (33, 1024, 256, 64, 8), (70, 512, 256, 128, 8)])
+@pytest.mark.parametrize("T,d,f,E,k", [(40, 512, 512, 8, 2), (33, 1024, 256, 64, 8), (70, 512, 256, 128, 8),
+                                       # one verify block, and one token: the expert launch routes the
+                                       # projected logits itself
+                                       (8, 512, 256, 64, 8), (1, 1024, 512, 16, 4)])
 def test_forward_hidden_small(T, d, f, E, k):
     moe = _moe()
     w = synth.Workload("router", T, d, f, E, k, "bf16", "none", 700 + T)
