@@ -295,9 +295,13 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
  *                       GPU, held until the process ends); the combine
  *                       launch clears it for the stream's next call, and the
  *                       first call on a stream (or one after a call whose
- *                       combine launch failed) clears it with one small
- *                       extra launch.  Streams beyond the 16th on a GPU
- *                       route in launches of their own.
+ *                       combine launch failed, or after a capture) clears
+ *                       it with one small extra launch.  Streams beyond the
+ *                       16th on a GPU route in launches of their own.  A
+ *                       call captured into a graph keeps the block of the
+ *                       stream it was captured on: replays of that graph
+ *                       must not overlap other calls that use the same
+ *                       block (as calls sharing a workspace must not).
  *   "fused_launches"    "fused" with the routing and permutation always in
  *                       launches of their own.
  *   "stream"            one launch per phase: permutation, gate/up +

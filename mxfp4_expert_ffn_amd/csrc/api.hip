@@ -362,7 +362,12 @@ moe_status launch_all(moe_mxfp4_ctx* ctx, const uint16_t* x, const float* router
             return MOE_ERR_HIP;
         if (fault_at("combine") || moe::launch_finalize_layer(dm, ws, out, c.out_dtype, lstate, s) != hipSuccess)
             return MOE_ERR_HIP;
-        *lclear = true;
+        // Under stream capture nothing ran: the launches (a clear among them)
+        // only enter the graph, so the block is not known to be clear until
+        // an eager call has cleared it.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cap) != hipSuccess) return MOE_ERR_HIP;
+        *lclear = cap == hipStreamCaptureStatusNone;
         if (mark(6) != hipSuccess) return MOE_ERR_HIP;
         if (ctx->log && ctx->logged_tokens.exchange(dm.T) != dm.T)
             std::fprintf(stderr, "moe_mxfp4: T=%d P=%d E=%d d=%d f=%d k=%d: %sone launch of routing and "

@@ -211,3 +211,40 @@ def test_layer_on_more_streams_than_state_blocks(monkeypatch):
             assert torch.equal(out, y_ref)
     for st in streams:
         assert made["fused"].device_status(w.T, stream=st) == 0
+
+
+def test_layer_capture_on_a_stream_then_eager_calls_on_it(monkeypatch):
+    # calls captured on a stream and eager calls on the same stream share
+    # that stream's state block: replays and eager calls alternate on it,
+    # each exact
+    w = synth.Workload("lyc", 8, 512, 1024, 64, 8, "bf16", "normal", 1305)
+    acts = synth.make_activations(w)
+    wts = problems.pack_experts(w)
+    made = _layers(monkeypatch, problems.to_device(wts), w, 1)
+    layer = made["fused"]
+    x, lg = _inputs(acts)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    y_graph = torch.empty((w.T, w.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(layer.workspace_bytes(w.T), dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    print("layer: capture on a side stream", flush=True)
+    with torch.cuda.graph(g, stream=st):
+        layer(x, lg, out=y_graph, workspace=ws, stream=st)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(35)
+    for i in range(4):
+        xi = synth.bf16_bits_from_f32(rng.standard_normal((w.T, w.d)).astype(np.float32))
+        x.copy_(torch.from_numpy(xi.view(np.int16)).cuda().view(torch.bfloat16))
+        lg.copy_(torch.from_numpy(rng.standard_normal((w.T, w.E)).astype(np.float32)).cuda())
+        torch.cuda.synchronize()
+        y_ref = made["stream"](x, lg).clone()
+        torch.cuda.synchronize()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            y_eager = layer(x, lg, stream=st)            # eager, on the capture stream, before the replay
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_eager, y_ref), i
+        assert torch.equal(y_graph, y_ref), i
+        assert layer.device_status(w.T, stream=st) == 0
