@@ -25,6 +25,7 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -324,6 +325,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="verify_32seq")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="batch of this many tokens with the workload's model and routing recipe (a batch-size "
+                         "sweep; the named workload's own size by default)")
     ap.add_argument("--copies", type=int, default=3, help="weight copies rotated across steps")
     ap.add_argument("--path", choices=("stream", "fused_launches", "fused"), default=None,
                     help="kernel path of the bf16 workloads (MOE_MXFP4_PATH): one launch per phase; routing, "
@@ -366,6 +370,10 @@ def main():
     if args.path:
         os.environ["MOE_MXFP4_PATH"] = args.path
     w = synth.workload(args.workload)
+    if args.tokens is not None:
+        if args.tokens < 1:
+            ap.error("--tokens must be positive")
+        w = dataclasses.replace(w, name=f"{w.name}@{args.tokens}", T=args.tokens)
     mx8 = w.act == "mxfp8"
     torch.cuda.set_device(0)
     log(f"workload {w}")

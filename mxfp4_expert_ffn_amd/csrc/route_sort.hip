@@ -433,11 +433,15 @@ __global__ __launch_bounds__(kSortThreads) void k_sort(Dims dm, const int32_t* _
 }
 
 // Small batches (T <= kFusedMaxTokens, E <= 64): routing and the permutation
-// in one workgroup.  Wave w routes tokens w, w + 16, ... and keeps their ids
-// in LDS, where the sort then reads them: one launch instead of two, and no
-// round trip of the ids through memory between them.  LDS after the sort's:
-// ids[P] (rounded to 16 bytes), then one ranking scratch per wave.
-constexpr int kFusedMaxTokens = 4 * kSortWaves;
+// in one workgroup.  Wave w routes token w and keeps its ids in LDS, where
+// the sort then reads them: one launch instead of two, and no round trip of
+// the ids through memory between them.  One token per wave: ranking a
+// token's logits is 64 x 64 compares, and the 16 waves share one CU's four
+// SIMDs, so every further token per wave costs about 4 us (22 against 13 us
+// for the two launches at 64 tokens), while the routing launch spreads the
+// tokens over many CUs.  LDS after the sort's: ids[P] (rounded to 16 bytes),
+// then one ranking scratch per wave.
+constexpr int kFusedMaxTokens = kSortWaves;
 
 __global__ __launch_bounds__(kSortThreads) void k_route_sort(const float* __restrict__ logits, Dims dm,
                                                              int32_t* __restrict__ ids, float* __restrict__ wts,
