@@ -241,7 +241,9 @@ def test_k_extents(d, f):
 @pytest.mark.parametrize("T,E,k,coarse", [
     (20, 100, 6, False),      # E not a multiple of 64
     (24, 128, 8, True),       # many exact ties
-    (33, 64, 8, True),
+    (33, 64, 8, True),        # routing launch + single-workgroup permutation
+    (16, 64, 8, True),        # routing and permutation in one workgroup (one token per wave)
+    (12, 20, 6, False),
     (17, 200, 8, False),      # wave-wide argmax rounds (E > 128)
     (9, 512, 32, True),       # largest E and k the library accepts
 ])
