@@ -14,7 +14,7 @@
 // deterministic; the only atomic adds sum integer ranks, whose total does not
 // depend on their order.  Sizes: up to 64 pairs, one wave after the routing
 // in the same launch; up to 8192, one workgroup (fused with the routing for
-// up to 64 tokens); beyond, tiles of 2048 pairs in three launches.
+// up to 16 tokens); beyond, tiles of 2048 pairs in three launches.
 #include "route_core.hpp"
 
 #include <float.h>
