@@ -220,10 +220,10 @@ def kernel_path(moe, w, mx8):
     path = os.environ.get("MOE_MXFP4_PATH") or "fused"
     if path == "stream" or w.P > moe.FUSED_MAX_PAIRS:
         return "stream"
-    # one verify block (at most 64 pairs over at most 64 experts, no more
+    # one verify block (at most 64 pairs over at most 128 experts, no more
     # pairs than experts, at most 1024 logits): routing, permutation and both
     # projections in one launch, then the combine
-    if path == "fused" and w.E <= 64 and w.P <= 64 and w.P <= w.E and w.T * w.E <= 1024:
+    if path == "fused" and w.E <= 128 and w.P <= 64 and w.P <= w.E and w.T * w.E <= 1024:
         return "fused (routing in the expert launch)"
     return "fused (ticketed)" if w.P > w.E else "fused (persistent)"
 

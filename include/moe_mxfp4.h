@@ -283,7 +283,7 @@ moe_status moe_mxfp4_forward_noalloc(moe_mxfp4_ctx* ctx, const void* hidden, con
  *                       MOE_MXFP4_FUSED_MAX_PAIRS pairs; larger ones run
  *                       "stream".
  *                       For a single verify block (at most 64 pairs over
- *                       at most 64 experts, no more pairs than experts, at
+ *                       at most 128 experts, no more pairs than experts, at
  *                       most 1024 router logits) the routing and the
  *                       permutation run inside that one launch instead:
  *                       every workgroup routes the block's tokens and

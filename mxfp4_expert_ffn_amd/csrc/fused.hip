@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chain(FusedArgs f) {
 }
 
 // ---------------------------------------------------------------------------
-// The layer of one verify block (at most 64 pairs over at most 64 experts)
+// The layer of one verify block (at most 64 pairs over at most 128 experts)
 // in two launches: this persistent kernel, with no launch in front of it,
 // and the combine after it.
 //
@@ -265,12 +265,12 @@ constexpr int kLyWords = 0;                                        // flag, next
 constexpr int kLySc = 16;                                          // RankScratch<1>[kWaves]
 constexpr int kLyIds = kLySc + kWaves * (int)sizeof(route::RankScratch<1>);
 constexpr int kLyWts = kLyIds + kChunk * 4;
-constexpr int kLyCnt = kLyWts + kChunk * 4;
-constexpr int kLyExo = kLyCnt + kWave * 4;
-constexpr int kLyKeys = kLyExo + kWave * 4;                        // uint64 [64]
+constexpr int kLyCnt = kLyWts + kChunk * 4;                       // [128]
+constexpr int kLyExo = kLyCnt + 2 * kWave * 4;                     // [128]
+constexpr int kLyKeys = kLyExo + 2 * kWave * 4;                    // uint64 [64] or int [128]
 constexpr int kLyOff = kLyKeys + kWave * 8;                        // [E + 1]
-constexpr int kLyAct = kLyOff + (kWave + 4) * 4;                   // [E + 1]
-constexpr int kLySorted = kLyAct + (kWave + 4) * 4;                // [P]
+constexpr int kLyAct = kLyOff + (2 * kWave + 4) * 4;               // [E + 1]
+constexpr int kLySorted = kLyAct + (2 * kWave + 4) * 4;            // [P]
 constexpr int kLyChunks = kLySorted + kChunk * 4;                  // [64][kChunkRec]
 constexpr int kLyNch = kLyChunks + kChunk * kChunkRec * 4;
 constexpr int kLyLogits = kLyNch + 16;                             // [T][E] router logits
@@ -301,8 +301,12 @@ __device__ bool layer_wait(const LayerArgs& a, const int32_t* p, int32_t target,
     }
 }
 
-template <int RT, int DG, int DD>
+// NV: logits per lane of a routing wave (E <= 64 * NV): ranking for one, as
+// the routing launches do up to 64 experts; k argmax rounds for two, as they
+// do up to 128.
+template <int RT, int DG, int DD, int NV>
 __global__ __launch_bounds__(kThreads, 2) void k_layer(LayerArgs a) {
+    static_assert(NV == 1 || NV == 2, "up to 128 experts");
     constexpr int kRing = DG > DD ? DG : DD;
     // one LDS object (see k_fused): the unit ring, then the block's routing
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kSlot + kLyBytes];
@@ -342,12 +346,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_layer(LayerArgs a) {
     }
     lds_barrier();
     // one wave per token ranks its logits, then wave 0 permutes the pairs
-    for (int t = wave; t < dm.T; t += kWaves) route::route_token_rank<1>(s_lg, dm, t, lane, sc[wave], s_ids, s_wts, nullptr);
+    for (int t = wave; t < dm.T; t += kWaves) {
+        if constexpr (NV == 1)
+            route::route_token_rank<1>(s_lg, dm, t, lane, sc[wave], s_ids, s_wts, nullptr);
+        else
+            route::route_token_argmax<NV>(s_lg, dm, t, lane, s_ids, s_wts);
+    }
     lds_barrier();
-    if (wave == 0)
-        route::sort_wave(dm, s_ids, reinterpret_cast<int32_t*>(ly + kLyCnt), reinterpret_cast<int32_t*>(ly + kLyExo),
-                         reinterpret_cast<uint64_t*>(ly + kLyKeys), lane, s_off, s_sorted, s_act, s_chunks, s_nch,
-                         nullptr, 0);
+    if (wave == 0) {
+        int32_t* cnt = reinterpret_cast<int32_t*>(ly + kLyCnt);
+        int32_t* exo = reinterpret_cast<int32_t*>(ly + kLyExo);
+        if constexpr (NV == 1)
+            route::sort_wave(dm, s_ids, cnt, exo, reinterpret_cast<uint64_t*>(ly + kLyKeys), lane, s_off, s_sorted,
+                             s_act, s_chunks, s_nch, nullptr, 0);
+        else
+            route::sort_wave2(dm, s_ids, cnt, exo, reinterpret_cast<int32_t*>(ly + kLyKeys), lane, s_off, s_sorted,
+                              s_act, s_chunks, s_nch);
+    }
     if (tid == 0) {
         s_words[1] = first;
         s_words[2] = epoch;
@@ -414,21 +429,21 @@ __global__ void k_layer_clear(int32_t* st) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < kLayerStateInts; i += gridDim.x * blockDim.x) st[i] = 0;
 }
 
-template <int DG, int DD>
+template <int NV, int DG, int DD>
 hipError_t launch_layer_variant(const LayerArgs& a, int items, hipStream_t s) {
     static int cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (cached[dev] == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_layer<2, DG, DD>),
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_layer<2, DG, DD, NV>),
                                                          kThreads, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidValue;
         cached[dev] = per_cu * cus > 0 ? per_cu * cus : 1;
     }
     const int grid = items < cached[dev] ? items : cached[dev];
-    hipLaunchKernelGGL((k_layer<2, DG, DD>), dim3(grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_layer<2, DG, DD, NV>), dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -541,7 +556,7 @@ hipError_t launch_fused(const uint16_t* x, const moe_mxfp4_weights& w, const Dim
 }
 
 bool layer_supported(const Dims& dm) {
-    return dm.E <= kWave && dm.P <= kChunk && dm.P <= dm.E && stream::tiles_per_wave(dm) == 2 &&
+    return dm.E <= 2 * kWave && dm.P <= kChunk && dm.P <= dm.E && stream::tiles_per_wave(dm) == 2 &&
            dm.T * dm.E <= kLayerMaxLogits;
 }
 
@@ -563,10 +578,16 @@ hipError_t launch_layer(const uint16_t* x, const float* logits, const moe_mxfp4_
     // every active expert is one chunk
     const int items = (dm.P < dm.E ? dm.P : dm.E) * (a.ntg + a.ntd);
     const bool g4 = (dm.d / kKStep) % 4 == 0, d4 = (dm.f / kKStep) % 4 == 0;
-    if (g4 && d4) return fused::launch_layer_variant<4, 4>(a, items, s);
-    if (g4) return fused::launch_layer_variant<4, 2>(a, items, s);
-    if (d4) return fused::launch_layer_variant<2, 4>(a, items, s);
-    return fused::launch_layer_variant<2, 2>(a, items, s);
+    if (dm.E > kWave) {
+        if (g4 && d4) return fused::launch_layer_variant<2, 4, 4>(a, items, s);
+        if (g4) return fused::launch_layer_variant<2, 4, 2>(a, items, s);
+        if (d4) return fused::launch_layer_variant<2, 2, 4>(a, items, s);
+        return fused::launch_layer_variant<2, 2, 2>(a, items, s);
+    }
+    if (g4 && d4) return fused::launch_layer_variant<1, 4, 4>(a, items, s);
+    if (g4) return fused::launch_layer_variant<1, 4, 2>(a, items, s);
+    if (d4) return fused::launch_layer_variant<1, 2, 4>(a, items, s);
+    return fused::launch_layer_variant<1, 2, 2>(a, items, s);
 }
 
 hipError_t launch_layer_clear(int32_t* state, hipStream_t s) {

@@ -7,7 +7,7 @@
 namespace moe {
 
 // Layer in two launches (bf16 activations, one verify block: at most 64
-// pairs over at most 64 experts, no more pairs than experts, at most
+// pairs over at most 128 experts, no more pairs than experts, at most
 // kLayerMaxLogits router logits): one persistent launch routes the tokens and
 // permutes the pairs inside every workgroup and runs the gate/up and down
 // units; the combine follows.  The first launch's counters live in a state

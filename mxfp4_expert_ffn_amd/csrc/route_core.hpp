@@ -14,6 +14,7 @@
 #include "common.hpp"
 
 #include <float.h>
+#include <limits.h>
 
 namespace moe {
 namespace route {
@@ -102,6 +103,102 @@ __device__ __forceinline__ void route_token_rank(const float* __restrict__ logit
     wave_sync_lds();                             // the scratch may be reused for the next token
 }
 
+
+// (value, expert) order of the routing: larger value first, then the lower
+// expert index; INT_MAX marks an empty candidate, which comes last.
+__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
+    if (oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+    }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(float& bv, int& bi) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
+    take_better(bv, bi, ov, oi);
+}
+
+// Every lane ends with the wave-wide best candidate.  Within each row of 16
+// lanes, DPP moves pair lanes 1 apart, then 2 apart (quad permutes), then
+// the two halves of each 8 (half-mirror) and of the row (mirror): after each
+// step both partners hold the better of two groups.  The four row results
+// are then read from lanes 0, 16, 32, 48 and folded in that order.
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+    dpp_step<0xB1>(bv, bi);      // quad_perm [1, 0, 3, 2]
+    dpp_step<0x4E>(bv, bi);      // quad_perm [2, 3, 0, 1]
+    dpp_step<0x141>(bv, bi);     // row_half_mirror
+    dpp_step<0x140>(bv, bi);     // row_mirror
+    float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+    int ri = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+        take_better(rv, ri, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r)),
+                    __builtin_amdgcn_readlane(bi, 16 * r));
+    bv = rv;
+    bi = ri;
+}
+
+// Wave-wide sum with the same pairing (every lane gets the same bits: each
+// step adds the partner's value, and a + b == b + a).
+__device__ __forceinline__ float wave_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Routing of token t by one wavefront by k rounds of a wave-wide argmax, E <=
+// 64 * NV (lane l holds logits l, l + 64, ...): the same selection as
+// route_token_rank, cheaper than ranking once a lane holds two or more
+// logits; weights = softmax over the k selected, the k terms summed with
+// wave_sum.  Writes ids/weights of the token's k slots (global or LDS).
+template <int NV>
+__device__ __forceinline__ void route_token_argmax(const float* __restrict__ logits, const Dims& dm, int t, int lane,
+                                                   int32_t* __restrict__ ids, float* __restrict__ wts) {
+    const float* l = logits + (size_t)t * dm.E;
+    float v[NV];
+    uint32_t taken = 0;                          // slots already selected, or past E
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int e = lane + kWave * i;
+        v[i] = e < dm.E ? l[e] : 0.0f;
+        if (e >= dm.E) taken |= 1u << i;
+    }
+    int my_id = 0;
+    float my_val = 0.0f, top_val = 0.0f;
+    for (int j = 0; j < dm.k; ++j) {
+        // best untaken logit of this lane (lowest index on ties: i ascends)
+        float bv = -FLT_MAX;
+        int bi = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            if (!((taken >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
+                bv = v[i];
+                bi = lane + kWave * i;
+            }
+        }
+        wave_best(bv, bi);
+        if (bi % kWave == lane) taken |= 1u << (bi / kWave);
+        if (lane == j) {
+            my_id = bi;
+            my_val = bv;
+        }
+        if (j == 0) top_val = bv;
+    }
+    const float ex = lane < dm.k ? expf(my_val - top_val) : 0.0f;
+    const float sum = wave_sum(ex);
+    if (lane < dm.k) {
+        ids[(size_t)t * dm.k + lane] = my_id;
+        wts[(size_t)t * dm.k + lane] = ex / sum;
+    }
+}
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
@@ -195,6 +292,93 @@ __device__ __forceinline__ void sort_wave(const Dims& dm, const int32_t* ids, in
         }
     }
     if (xtab && lane < kXcds) xtab[lane] = na / kXcds + (lane < na % kXcds);
+    if (lane == 0) {
+        offsets[E] = P;
+        active[E] = na;
+        *nchunks = na;
+    }
+    if (valid) sorted[exo[ep] + rank] = lane;
+}
+
+}  // namespace route
+}  // namespace moe
+
+namespace moe {
+namespace route {
+
+// sort_wave for up to 128 experts: lane e holds experts e and e + 64 (the
+// same outputs: a stable counting sort, experts ranked by descending count,
+// ties to the lower index, each active expert one chunk).  P <= 64, so
+// counts fit 7 bits and the ranks come from the same ballots and count
+// histogram as sort_wave, per half: an expert of the high half also has
+// every low-half expert of its count before it.  ids: P expert ids (LDS);
+// scratch: cnt[128], exo[128], hist[128].
+__device__ __forceinline__ void sort_wave2(const Dims& dm, const int32_t* ids, int32_t* cnt, int32_t* exo,
+                                           int32_t* hist, int lane, int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ sorted, int32_t* __restrict__ active,
+                                           int32_t* __restrict__ chunks, int32_t* __restrict__ nchunks) {
+    const int E = dm.E, P = dm.P;
+    const bool valid = lane < P;
+    const int ep = valid ? ids[lane] : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0, nb = id_bits(E); b < nb; ++b) {
+        const bool bit = (ep >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    const uint64_t below = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    const int rank = __popcll(peers & below);          // earlier pairs of the same expert
+    cnt[lane] = 0;
+    cnt[lane + kWave] = 0;
+    wave_sync_lds();
+    if (valid && rank == 0) cnt[ep] = __popcll(peers);
+    wave_sync_lds();
+    const int c0 = lane < E ? cnt[lane] : 0;
+    const int c1 = lane + kWave < E ? cnt[lane + kWave] : 0;
+    const int i0 = wave_inclusive_scan(c0, lane), i1 = wave_inclusive_scan(c1, lane);
+    const int excl0 = i0 - c0, excl1 = __builtin_amdgcn_readlane(i0, kWave - 1) + i1 - c1;
+    exo[lane] = excl0;
+    exo[lane + kWave] = excl1;
+    if (lane < E) offsets[lane] = excl0;
+    if (lane + kWave < E) offsets[lane + kWave] = excl1;
+    uint64_t same0 = __ballot(c0 > 0), same1 = __ballot(c1 > 0);
+    for (int b = 0; b < 7; ++b) {
+        const bool b0 = (c0 >> b) & 1, b1 = (c1 >> b) & 1;
+        const uint64_t m0 = __ballot(b0), m1 = __ballot(b1);
+        same0 &= b0 ? m0 : ~m0;
+        same1 &= b1 ? m1 : ~m1;
+    }
+    const int eq0 = __popcll(same0 & below), eq1 = __popcll(same1 & below);
+    hist[lane] = 0;                                    // [c - 1]: low-half experts of count c
+    hist[lane + kWave] = 0;                            // [64 + c - 1]: high-half ones
+    wave_sync_lds();
+    if (c0 > 0 && eq0 == 0) hist[c0 - 1] = __popcll(same0);
+    if (c1 > 0 && eq1 == 0) hist[kWave + c1 - 1] = __popcll(same1);
+    wave_sync_lds();
+    const int hl = hist[lane], h = hl + hist[lane + kWave];
+    const int hin = wave_inclusive_scan(h, lane);
+    const int ge = __builtin_amdgcn_readlane(hin, kWave - 1) - hin + h;   // experts of count >= lane + 1
+    const int gt0 = __shfl(ge, c0 < kWave ? c0 : 0), gt1 = __shfl(ge, c1 < kWave ? c1 : 0);
+    const int lo1 = __shfl(hl, c1 > 0 ? c1 - 1 : 0);                    // low-half experts of count c1
+    const int r0 = (c0 < kWave ? gt0 : 0) + eq0;
+    const int r1 = (c1 < kWave ? gt1 : 0) + lo1 + eq1;
+    const int na = __popcll(__ballot(c0 > 0)) + __popcll(__ballot(c1 > 0));
+    if (c0 > 0) {
+        active[r0] = lane;
+        int32_t* rec = chunks + kChunkRec * r0;
+        rec[0] = lane;
+        rec[1] = excl0;
+        rec[2] = c0;
+        rec[3] = 0;
+    }
+    if (c1 > 0) {
+        active[r1] = lane + kWave;
+        int32_t* rec = chunks + kChunkRec * r1;
+        rec[0] = lane + kWave;
+        rec[1] = excl1;
+        rec[2] = c1;
+        rec[3] = 0;
+    }
     if (lane == 0) {
         offsets[E] = P;
         active[E] = na;

@@ -57,7 +57,7 @@ def _inputs(acts):
 
 
 def _eligible(w):
-    return w.E <= 64 and w.T * w.k <= 64 and w.T * w.k <= w.E and w.T * w.E <= 1024
+    return w.E <= 128 and w.T * w.k <= 64 and w.T * w.k <= w.E and w.T * w.E <= 1024
 
 
 @pytest.mark.parametrize("T,E,k,d,f,out_dtype", [
@@ -68,6 +68,9 @@ def _eligible(w):
     (1, 1, 1, 512, 256, 1),       # E = 1, K = 256 steps for down
     (16, 64, 4, 256, 512, 0),     # 16 tokens: 4 routed per wave, 1024 logits
     (5, 40, 8, 1024, 512, 1),     # E not a power of two
+    (8, 128, 8, 512, 1024, 0),    # 128 experts: two logits per lane, argmax rounds, two experts per lane
+    (4, 100, 6, 512, 512, 1),     # 65..128 experts, E not a power of two
+    (1, 96, 8, 256, 512, 1),
 ])
 def test_layer_equals_multi_launch_paths(monkeypatch, T, E, k, d, f, out_dtype):
     w = synth.Workload("ly", T, d, f, E, k, "bf16", "normal", 1200 + T + E + d)
@@ -91,13 +94,16 @@ def test_layer_equals_multi_launch_paths(monkeypatch, T, E, k, d, f, out_dtype):
     assert problems.rel_max_err(ys["fused"].float().cpu().numpy(), ref) <= TOL
 
 
-def test_layer_full_size_verify_block_equals_launches(monkeypatch):
-    w = synth.workload("verify_1seq")
+@pytest.mark.parametrize("name,T", [("verify_1seq", None), ("share_64seq", 8)])
+def test_layer_full_size_verify_block_equals_launches(monkeypatch, name, T):
+    w = synth.workload(name)
+    if T is not None:                                  # one verify block of that model
+        w = synth.Workload(w.name, T, w.d, w.f, w.E, w.k, w.act, w.bias, w.seed)
     assert _eligible(w)
     acts, wts = problems.problem(w)
     made = _layers(monkeypatch, problems.to_device(wts), w, 0)
     x, lg = _inputs(acts)
-    print("layer vs launches: verify_1seq", flush=True)
+    print(f"layer vs launches: {name} T={w.T}", flush=True)
     ys = {p: made[p](x, lg).clone() for p in PATHS}
     torch.cuda.synchronize()
     assert torch.equal(ys["fused"], ys["stream"])
