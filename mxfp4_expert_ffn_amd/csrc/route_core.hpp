@@ -27,47 +27,59 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 // Per-wave LDS scratch of the ranking router.
 template <int NV>
-struct alignas(16) RankScratch {                 // sv is read as float4
-    float sv[NV * kWave];
+struct alignas(16) RankScratch {                 // sk is read two keys at a time
+    uint64_t sk[NV * kWave];
     int32_t sid[kMaxTopK];
     float sval[kMaxTopK];
     float sex[kMaxTopK];
 };
 
+// The routing order of a logit as one unsigned 64-bit key, larger first:
+// the float's bits mapped to an unsigned integer that orders as the floats
+// do (the sign bit flipped for positive values, every bit for negative
+// ones; -0 taken as +0, which compares equal to it), then the expert index
+// inverted, so that of two equal values the lower index comes first.  For
+// finite and infinite logits, key order is the order (value descending,
+// index ascending) that float compares give; NaN logits are not supported.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0u;
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+
 // Routing of token t by one wavefront, E <= 64 * NV.  Lane l holds logits l
 // and l + 64.  The rank of logit e is the number of logits that come before
-// it in the order (value descending, expert index ascending); the experts of
-// ranks 0..k-1 are the selection, already in order.  Writes ids/weights of
-// the token's k slots (and the ids to ids_lds when given).
+// it in the order (value descending, expert index ascending), counted with
+// one 64-bit key compare per logit (route_key); the experts of ranks
+// 0..k-1 are the selection, already in order.  Writes ids/weights of the
+// token's k slots (and the ids to ids_lds when given).
 template <int NV>
 __device__ __forceinline__ void route_token_rank(const float* __restrict__ logits, const Dims& dm, int t, int lane,
                                  RankScratch<NV>& sc, int32_t* __restrict__ ids, float* __restrict__ wts,
                                  int32_t* ids_lds) {
     const float* l = logits + (size_t)t * dm.E;
     float v[NV];
+    uint64_t key[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = lane + kWave * i;
         // padding sorts after every logit: it never beats one (-inf included)
         v[i] = e < dm.E ? l[e] : -INFINITY;
-        sc.sv[e] = v[i];
+        key[i] = route_key(v[i], e);
+        sc.sk[e] = key[i];
     }
     wave_sync_lds();
     int rank[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) rank[i] = 0;
-    const float4* row = reinterpret_cast<const float4*>(sc.sv);
-#pragma unroll 4
-    for (int q = 0; q < NV * kWave / 4; ++q) {
-        const float4 u4 = row[q];
-        const float u[4] = {u4.x, u4.y, u4.z, u4.w};
+    typedef __attribute__((ext_vector_type(2))) uint64_t u64x2_t;
+    const u64x2_t* row = reinterpret_cast<const u64x2_t*>(sc.sk);
+#pragma unroll 8
+    for (int q = 0; q < NV * kWave / 2; ++q) {
+        const u64x2_t u2 = row[q];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e2 = 4 * q + j;
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-                rank[i] += (u[j] > v[i]) || (u[j] == v[i] && e2 < lane + kWave * i);
-        }
+        for (int i = 0; i < NV; ++i) rank[i] += (u2.x > key[i]) + (u2.y > key[i]);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
