@@ -217,7 +217,8 @@ size_t moe_mxfp4_workspace_bytes(const moe_mxfp4_ctx* ctx, int32_t num_tokens);
  * Run the expert layer for `num_tokens` tokens (0 is a no-op returning
  * MOE_OK).  All buffers are device memory:
  *   hidden         bf16  [T][d_model] (uint16 bit patterns)
- *   router_logits  float [T][E]
+ *   router_logits  float [T][E], finite or infinite (NaN logits give an
+ *                  unspecified selection)
  *   out            [T][d_model], bf16 (round to nearest even) or float per
  *                  cfg.out_dtype; fully overwritten
  *   workspace      at least moe_mxfp4_workspace_bytes(ctx, T) bytes
