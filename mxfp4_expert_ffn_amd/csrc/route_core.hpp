@@ -116,44 +116,11 @@ __device__ __forceinline__ void route_token_rank(const float* __restrict__ logit
 }
 
 
-// (value, expert) order of the routing: larger value first, then the lower
-// expert index; INT_MAX marks an empty candidate, which comes last.
-__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
-    if (oi != INT_MAX && (bi == INT_MAX || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-    }
-}
-
-template <int CTRL>
-__device__ __forceinline__ void dpp_step(float& bv, int& bi) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
-    const int oi = __builtin_amdgcn_update_dpp(0, bi, CTRL, 0xF, 0xF, false);
-    take_better(bv, bi, ov, oi);
-}
-
-// Every lane ends with the wave-wide best candidate.  Within each row of 16
-// lanes, DPP moves pair lanes 1 apart, then 2 apart (quad permutes), then
-// the two halves of each 8 (half-mirror) and of the row (mirror): after each
-// step both partners hold the better of two groups.  The four row results
-// are then read from lanes 0, 16, 32, 48 and folded in that order.
-__device__ __forceinline__ void wave_best(float& bv, int& bi) {
-    dpp_step<0xB1>(bv, bi);      // quad_perm [1, 0, 3, 2]
-    dpp_step<0x4E>(bv, bi);      // quad_perm [2, 3, 0, 1]
-    dpp_step<0x141>(bv, bi);     // row_half_mirror
-    dpp_step<0x140>(bv, bi);     // row_mirror
-    float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-    int ri = __builtin_amdgcn_readlane(bi, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r)
-        take_better(rv, ri, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * r)),
-                    __builtin_amdgcn_readlane(bi, 16 * r));
-    bv = rv;
-    bi = ri;
-}
-
-// Wave-wide sum with the same pairing (every lane gets the same bits: each
-// step adds the partner's value, and a + b == b + a).
+// Wave-wide sum.  Within each row of 16 lanes, DPP moves pair lanes 1 apart,
+// then 2 apart (quad permutes), then the two halves of each 8 (half-mirror)
+// and of the row (mirror); the four row sums are then read from lanes 0, 16,
+// 32, 48.  Every lane gets the same bits: each step adds the partner's
+// value, and a + b == b + a.
 __device__ __forceinline__ float wave_sum(float v) {
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
     v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
@@ -166,40 +133,70 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Routing of token t by one wavefront by k rounds of a wave-wide argmax, E <=
-// 64 * NV (lane l holds logits l, l + 64, ...): the same selection as
-// route_token_rank, cheaper than ranking once a lane holds two or more
-// logits; weights = softmax over the k selected, the k terms summed with
-// wave_sum.  Writes ids/weights of the token's k slots (global or LDS).
+// The logit a route_key came from (-0 comes back as +0, which changes no
+// difference to another logit but the sign of a zero one, and exp(+-0) = 1).
+__device__ __forceinline__ float route_key_value(uint64_t key) {
+    const uint32_t ord = (uint32_t)(key >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+// The larger of a lane's key and the key of the lane DPP control CTRL names.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_key(uint64_t k) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xF, 0xF, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > k ? o : k;
+}
+
+// The largest key of the wave, in every lane: the pairings of wave_sum within
+// each row of 16, then the four row results folded.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    k = dpp_max_key<0xB1>(k);       // quad_perm [1, 0, 3, 2]
+    k = dpp_max_key<0x4E>(k);       // quad_perm [2, 3, 0, 1]
+    k = dpp_max_key<0x141>(k);      // row_half_mirror
+    k = dpp_max_key<0x140>(k);      // row_mirror
+    uint64_t r = 0;
+#pragma unroll
+    for (int row = 0; row < 4; ++row) {
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * row) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * row);
+        r = o > r ? o : r;
+    }
+    return r;
+}
+
+// Routing of token t by one wavefront by k rounds of a wave-wide maximum of
+// route_keys, E <= 64 * NV (lane l holds logits l, l + 64, ...): the same
+// selection as route_token_rank (value descending, index ascending), with
+// one 64-bit compare per pairing and no branches, cheaper than ranking once
+// a lane holds two or more logits; weights = softmax over the k selected,
+// the k terms summed with wave_sum.  Writes ids/weights of the token's k
+// slots (global or LDS).  Every key of a logit is above 0, the key of
+// padding and of logits already taken.
 template <int NV>
 __device__ __forceinline__ void route_token_argmax(const float* __restrict__ logits, const Dims& dm, int t, int lane,
                                                    int32_t* __restrict__ ids, float* __restrict__ wts) {
     const float* l = logits + (size_t)t * dm.E;
-    float v[NV];
-    uint32_t taken = 0;                          // slots already selected, or past E
+    uint64_t key[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
         const int e = lane + kWave * i;
-        v[i] = e < dm.E ? l[e] : 0.0f;
-        if (e >= dm.E) taken |= 1u << i;
+        key[i] = e < dm.E ? route_key(l[e], e) : 0;
     }
     int my_id = 0;
     float my_val = 0.0f, top_val = 0.0f;
     for (int j = 0; j < dm.k; ++j) {
-        // best untaken logit of this lane (lowest index on ties: i ascends)
-        float bv = -FLT_MAX;
-        int bi = INT_MAX;
+        uint64_t b = key[0];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            if (!((taken >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
-                bv = v[i];
-                bi = lane + kWave * i;
-            }
-        }
-        wave_best(bv, bi);
-        if (bi % kWave == lane) taken |= 1u << (bi / kWave);
+        for (int i = 1; i < NV; ++i) b = key[i] > b ? key[i] : b;
+        b = wave_max_key(b);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            if (key[i] == b) key[i] = 0;             // taken
+        const float bv = route_key_value(b);
         if (lane == j) {
-            my_id = bi;
+            my_id = (int)(0xFFFFFFFFu - (uint32_t)b);
             my_val = bv;
         }
         if (j == 0) top_val = bv;
