@@ -319,7 +319,8 @@ def time_accept(w, args, moe, torch, np, synth):
             "whole_block_accepted": float((n == G).mean())}, inp
 
 
-def main():
+def parse_args(argv=None):
+    """The command line (argv: a list of arguments, default sys.argv[1:])."""
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
@@ -360,7 +361,11 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the measurements, run a plain device copy (torch.neg, float32) of this many "
                          "MiB: the reference dispatch for scaling HBM byte counters")
-    args = ap.parse_args()
+    return ap.parse_args(argv)
+
+
+def main():
+    args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(no collectives, no sharding); run with --gpus 1", file=sys.stderr)

@@ -71,3 +71,26 @@ def test_traffic_is_dropped_once_a_header_of_the_kernel_changes(tmp_path):
 
 def test_cpu_model_is_a_string():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_every_bench_command_in_the_profiles_parses():
+    # each summary under profiles/ names the command that produced it; the
+    # bench arguments of every such command must still be accepted as written
+    import glob
+    import shlex
+    n = 0
+    for p in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(p):
+            if "bench.py" not in line or not line.startswith("    "):
+                continue
+            words = shlex.split(line.strip())
+            i = next(j for j, w in enumerate(words) if w.endswith("bench.py"))
+            rest = []
+            for w in words[i + 1:]:
+                if w in (">", "2>", "&&", "|") or w.startswith(">"):
+                    break
+                rest.append(w)
+            args = bench.parse_args(rest)
+            assert args.gpus == 1, (p, line)
+            n += 1
+    assert n >= 20
