@@ -287,6 +287,46 @@ def test_exact_logit_ties_pick_lowest_experts():
     assert np.array_equal(ids[1], [0, 1, 2]) and np.array_equal(ids[0], [7, 0, 1])
 
 
+def _edge_logits(T, E, seed):
+    """Rows in turn: small integers (many exact ties), signed zeros with a
+    few -1s (+0 and -0 compare equal, so the lower index wins), -inf but for
+    three finite logits (fewer than k: the rest of the selection is -inf,
+    lowest indices first, each with weight 0), and normal values."""
+    rng = np.random.default_rng(seed)
+    L = np.empty((T, E), np.float32)
+    for t in range(T):
+        kind = t % 4
+        if kind == 0:
+            L[t] = rng.integers(-2, 3, E)
+        elif kind == 1:
+            L[t] = np.where(rng.random(E) < 0.5, 0.0, -0.0)
+            L[t, rng.choice(E, 3, replace=False)] = -1.0
+        elif kind == 2:
+            L[t] = -np.inf
+            L[t, rng.choice(E, 3, replace=False)] = rng.standard_normal(3)
+        else:
+            L[t] = rng.standard_normal(E)
+    assert np.signbit(L[1]).any() and (L[1] == 0).sum() > 3
+    return L
+
+
+@pytest.mark.parametrize("T,E,k", [(8, 64, 8), (8, 100, 8), (8, 128, 8),      # routed inside the expert launch
+                                   (40, 64, 8), (40, 100, 6), (40, 200, 8), (24, 512, 8)])
+def test_routing_edge_values_on_every_routing_path(T, E, k):
+    """Exact ties, -0 against +0 and -inf logits, through the ranking (up to
+    64 experts) and the argmax rounds (65-512), both in the routing launches
+    and inside the expert launch of one verify block: the oracle's strict
+    comparison (value descending, then the lower index) gives the ids, and
+    a -inf slot weight 0."""
+    w, acts, wts = _custom(T, 256, 256, E, k, seed=70 + E + T, logits=_edge_logits(T, E, 170 + E + T))
+    got, _ = _run(w, acts, problems.to_device(wts))
+    _check_routing(w, acts, got)
+    ids = got["topk_ids"].reshape(T, k)
+    assert np.array_equal(ids[2][3:], np.sort(ids[2][3:]))      # the -inf part: ascending indices
+    ref = oracle.moe_forward(acts["x_bf16"], acts["logits"], wts, k)["y"]
+    assert np.isfinite(got["y"]).all() and problems.rel_max_err(got["y"], ref) <= TOL
+
+
 def test_zero_weights_give_zero_output():
     w, acts, wts = _custom(8, 256, 256, 4, 2, seed=62)
     for n in ("w_gate", "w_up", "w_down"):
